@@ -1,0 +1,26 @@
+"""Build the fp64 CPU oracle (test infrastructure) into oracle/libmac_oracle.so.
+
+Plain gcc, -O2, OpenMP, no fast-math.  Run as ``python -m oracle.build``.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "mac_oracle.c")
+LIB = os.path.join(HERE, "libmac_oracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp",
+           "-fno-fast-math", "-Wall", "-Wextra", "-Wno-unused-parameter",
+           SRC, "-o", LIB + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))
