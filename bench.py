@@ -1,0 +1,244 @@
+"""Benchmark of the MAC-Attention decode step on one MI355X.
+
+Workload (default): batch 16 x 131072-token context, 32 query / 8 KV heads,
+d = 128, paged bf16 KV (16-token pages, permuted table), ring 32, r = 256,
+tau = 0.3, per-request AR(1) rho ~ U[0.8, 0.99] -- synthetic inputs of that
+shape (no dataset, no model weights).
+
+A step is one pass of the whole hot path over the batch: append this token's
+K/V rows, match, complete, reduce/merge (the attention phase) and amend on its
+own stream.  The timed region runs K steps after W warm-up steps; inputs are
+resident in HBM before it starts.  Kernel durations come from the library's
+HIP events on the stream each kernel runs on (MAC_F_TIMING); the attention
+phase is match -> reduce, amend excluded, as the pages split it (Table 5).
+
+Prints one JSON line.  `value` is the attention-phase microseconds per decode
+step (lower is better); the line also carries achieved HBM GB/s, tokens/s, the
+roofline of the dominant kernel (complete), the in-house full-attention kernel
+on the same cache and the fp64 oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=48)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", default="b16_128k")
+    ap.add_argument("--r", type=int, default=0, help="override the band width")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-baseline-kernel", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 2 GiB device copy (reference for HBM counters)")
+    return ap.parse_args()
+
+
+class Bench:
+    def __init__(self, w, flags, K, V, paged, table):
+        import torch
+        import kv_reuse_amd as mac
+        self.w = w
+        self.torch = torch
+        self.mac = mac
+        dev = "cuda"
+        self.kc, self.vc, self.table = K, V, table
+        self.seq = torch.zeros(w.B, dtype=torch.int32, device=dev)
+        self.pos = torch.zeros(w.B, dtype=torch.int32, device=dev)
+        self.cfg = mac.make_config(
+            batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, ring_size=w.W, band=w.r, tau=w.tau,
+            rope_theta=w.theta, layout=mac.MAC_KV_PAGED if paged else mac.MAC_KV_CONTIGUOUS,
+            kv_dtype=mac.MAC_FP32 if w.kv == "fp32" else mac.MAC_BF16, max_seq_len=w.n_cap,
+            flags=flags | mac.MAC_F_TIMING)
+        self.stream = torch.cuda.current_stream()
+        self.layer = mac.MacLayer(self.cfg, main_stream=self.stream)
+        self.view = mac.make_kv_view(self.kc, self.vc, self.seq, self.table,
+                                     num_pages=self.kc.shape[0] if paged else 0)
+        self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+
+    def step(self, t, q, k_new, v_new):
+        w = self.w
+        self.pos.fill_(w.C + t)
+        self.seq.fill_(w.C + t + 1)
+        self.layer.append_kv(self.view, k_new, v_new, self.pos, self.stream)
+        self.layer.decode_step(self.view, q, self.out, None, self.stream)
+        return self.layer.stats()          # synchronises; last step's kernel times
+
+
+def oracle_baseline(w, K, V, qs, n_req, n_steps):
+    """fp64 oracle, as it stands, on the first n_req requests for n_steps steps."""
+    import oracle
+    from workloads import bf16_bits
+    Kg, Vg = [], []
+    for b in range(n_req):
+        for g in range(w.Hkv):
+            Kg.append(bf16_bits(K[b, g, :w.C + n_steps]))
+            Vg.append(bf16_bits(V[b, g, :w.C + n_steps]))
+    orc = oracle.Oracle(n_req, w.Hq, w.Hkv, w.d, w.W, w.r, w.tau, w.theta,
+                        kv_fp32=(w.kv == "fp32"))
+    t0 = time.perf_counter()
+    for t in range(n_steps):
+        orc.step(Kg, Vg, np.full(n_req, w.C + t + 1, np.int32), qs[t, :n_req])
+    dt = time.perf_counter() - t0
+    return dt / n_steps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the decode step runs on a single MI355X here and "
+              "--gpus %d is not supported (the sharding design is described in DESIGN.md)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import kv_reuse_amd as mac
+    from workloads import get_config, kv_logical, page_table, queries, scaled, to_paged
+    mac.load()
+    torch.cuda.set_device(0)
+    w = get_config(args.config)
+    if args.r:
+        w = scaled(w, r=args.r)
+    total = args.warmup + args.steps
+    assert total <= w.steps, "at most %d steps for this workload" % w.steps
+    paged = w.layout == "paged"
+
+    t_setup = time.perf_counter()
+    K, V = kv_logical(w, "cuda")
+    steps_idx = torch.arange(w.C, w.C + total, device="cuda")
+    k_rows = K[:, :, steps_idx].permute(2, 0, 1, 3).contiguous()     # [steps, B, Hkv, d]
+    v_rows = V[:, :, steps_idx].permute(2, 0, 1, 3).contiguous()
+    qs = queries(w, steps=total)
+    q_dev = torch.as_tensor(qs, device="cuda")
+    if paged:
+        tab_np = page_table(w)
+        kc, vc = to_paged(K, tab_np), to_paged(V, tab_np)
+        table = torch.as_tensor(tab_np, device="cuda")
+    else:
+        kc, vc, table = K, V, None
+    host_sample = None
+    if not args.no_cpu_baseline:
+        n_req = min(2, w.B)
+        host_sample = (K[:n_req, :, :w.C + 8].clone(), V[:n_req, :, :w.C + 8].clone())
+    if paged:
+        del K, V
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    bench = Bench(w, 0, kc, vc, paged, table)
+    for t in range(args.warmup):
+        bench.step(t, q_dev[t], k_rows[t], v_rows[t])
+    st0 = bench.layer.stats()
+    torch.cuda.synchronize()
+    att, comp, match, red, amend, hits, toks = [], [], [], [], [], [], []
+    prev = st0
+    wall0 = time.perf_counter()
+    for t in range(args.warmup, total):
+        st = bench.step(t, q_dev[t], k_rows[t], v_rows[t])
+        att.append(st["last_us_attention"])
+        comp.append(st["last_us_complete"])
+        match.append(st["last_us_match"])
+        red.append(st["last_us_reduce"])
+        amend.append(st["last_us_amend"])
+        hits.append(st["hits"] - prev["hits"])
+        toks.append(st["kv_tokens_critical"] - prev["kv_tokens_critical"])
+        prev = st
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    st1 = bench.layer.stats()
+    bench.layer.close()
+
+    row_bytes = 2 * w.d * w.kv_elem_bytes                   # one key row + one value row
+    kv_bytes = np.array(toks, np.float64) * row_bytes       # per step, per complete launch
+    q_bytes = w.B * w.Hq * w.d * 4
+    comp_bytes = kv_bytes + q_bytes
+    att_us = float(np.mean(att))
+    comp_us = float(np.mean(comp))
+    achieved = float(np.mean(comp_bytes)) / (comp_us * 1e-6) / 1e9
+    att_bytes = float(np.mean(kv_bytes)) + (w.B * w.Hq * (w.W * w.d * 4 + 3 * w.d * 4))
+    heads = w.B * w.Hq
+
+    # in-house full-attention kernel (every head misses) on the same cache
+    base = None
+    if not args.no_baseline_kernel:
+        fb = Bench(w, mac.MAC_F_DISABLE_REUSE, kc, vc, paged, table)
+        fa, fc = [], []
+        for t in range(min(total, 4 + 16)):
+            st = fb.step(t, q_dev[t], k_rows[t], v_rows[t])
+            if t >= 4:
+                fa.append(st["last_us_attention"])
+                fc.append(st["last_us_complete"])
+        full_tok = (w.C + total) * w.B * w.Hkv
+        base = {"attention_us": float(np.mean(fa)), "complete_us": float(np.mean(fc)),
+                "hbm_gbps": full_tok * row_bytes / (float(np.mean(fc)) * 1e-6) / 1e9,
+                "speedup_vs_full": float(np.mean(fa)) / att_us}
+        fb.layer.close()
+
+    cpu = None
+    if host_sample is not None:
+        n_req = host_sample[0].shape[0]
+        n_steps = 4
+        torch.set_num_threads(1)
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        sec = oracle_baseline(w, host_sample[0], host_sample[1], qs, n_req, n_steps)
+        cpu = {"value": sec * 1e6 * (w.B / n_req), "unit": "us/step", "cores": cores,
+               "kind": "oracle",
+               "sample": "%d of %d requests (all %d heads each), first %d decode steps from an "
+                         "empty ring, scaled by %d/%d to the batch" % (n_req, w.B, w.Hq, n_steps,
+                                                                       w.B, n_req)}
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.int16, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    line = {
+        "metric": "attention-phase µs/decode step + HBM GB/s at 128K ctx, batch 16, GQA 32q/8kv",
+        "value": att_us,
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "context": w.C, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.d, "kv_layout": w.layout,
+                   "ring": w.W, "band": w.r, "tau": w.tau, "rho": list(w.rho)},
+        "hbm_gbps": float(np.mean(kv_bytes)) / (att_us * 1e-6) / 1e9,
+        "tokens_per_s": w.B / (att_us * 1e-6),
+        "kv_bytes_per_step": float(np.mean(kv_bytes)),
+        "head_hit_rate": float(np.sum(hits)) / (heads * len(hits)),
+        "kernel_us": {"match": float(np.mean(match)), "complete": comp_us,
+                      "reduce": float(np.mean(red)), "amend": float(np.mean(amend))},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "complete_kernel", "bytes_per_launch": float(np.mean(comp_bytes))},
+        "attention_phase_bytes_per_step": att_bytes,
+        "full_attention_kernel": base,
+        "cpu_baseline": cpu,
+        "setup_s": t_setup,
+        "bad_input": int(st1["bad_input"]),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * mac.h -- C ABI of the MAC-Attention decode library for MI355X (gfx950).
+ *
+ * The operation is the decode step of MAC-Attention (arXiv 2604.00235; paper
+ * card at thelatestinai.com, abstract and Figure 2): for every (request,
+ * query head) the pre-RoPE query is matched by L2 distance against a short
+ * ring of recent pre-RoPE queries (match, Figure 2 (a)); on a hit only the
+ * band+tail of the KV cache is attended and merged in the log domain with the
+ * matched entry's cached prefix summary (complete, Figure 2 (b)); off the
+ * critical path the last r keys are removed from the new summary and the pair
+ * (pre-RoPE query, summary) enters the ring (amend, Figure 2 (c)).  A miss is
+ * full attention over the whole context.
+ *
+ * Conventions for every call:
+ *  - Pointers are device pointers unless marked "host".
+ *  - Positions are 0-based.  For request b the query position is
+ *    m = seq_lens[b] - 1; its own K/V row must already be in the cache.
+ *  - A summary (o, M, l) is the normalised attention output o[d], a reference
+ *    max M of the scaled logits and the normaliser l = sum exp(logit - M).
+ *  - Calls are asynchronous on the stream they receive (NULL: the handle's main
+ *    stream) unless stated.  A handle is one attention layer and is not
+ *    thread-safe.
+ *  - No C++ exception crosses this boundary.  Every call returns mac_status;
+ *    mac_last_error() gives the handle's last message.  Shape and pointer
+ *    errors are caught on the host before any launch.  Device faults surface
+ *    as MAC_EHIP at the next synchronising call.  Data values are not
+ *    validated (NaN propagates); indices read from device memory (sequence
+ *    lengths, page ids, positions) are bounds-checked on the device, and an
+ *    out-of-range entry idles that request or row and is counted in
+ *    mac_stats_t.bad_input instead of being dereferenced.
+ */
+#ifndef MAC_H
+#define MAC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mac_ctx *mac_handle;
+
+typedef enum {
+    MAC_OK = 0,
+    MAC_EINVAL = 1,          /* bad argument or configuration */
+    MAC_ENOMEM = 2,          /* device allocation failed */
+    MAC_EHIP = 3,            /* a HIP runtime call failed */
+    MAC_ESTATE = 4,          /* call not valid in the handle's state */
+    MAC_EUNSUPPORTED = 5     /* valid request this build does not implement */
+} mac_status;
+
+typedef enum { MAC_KV_CONTIGUOUS = 0, MAC_KV_PAGED = 1 } mac_kv_layout;
+typedef enum { MAC_BF16 = 0, MAC_FP32 = 1 } mac_dtype;
+
+enum {
+    MAC_F_DISABLE_REUSE = 1u,  /* every head misses: plain full attention, no ring upkeep */
+    MAC_F_SYNC_AMEND = 2u,     /* run amend on the decode stream instead of the amend stream */
+    MAC_F_TIMING = 4u,         /* time each kernel with HIP events (read via mac_stats) */
+    MAC_F_RECORD_DEBUG = 8u    /* keep per-head decisions for mac_debug_last */
+};
+
+/* Layer configuration (host struct).  head_dim must be 128; Hq % Hkv == 0;
+ * 1 <= ring_size <= 64; band >= 1; page_size must be 16.  tau < 0 disables
+ * every hit.  sm_scale == 0 selects 1/sqrt(head_dim). */
+typedef struct {
+    int32_t batch;          /* B: requests decoded together */
+    int32_t num_q_heads;    /* Hq */
+    int32_t num_kv_heads;   /* Hkv; query head h reads KV head h / (Hq/Hkv) */
+    int32_t head_dim;       /* d */
+    int32_t ring_size;      /* W: recent queries kept per (request, query head) */
+    int32_t band;           /* r: band width removed by amend */
+    float tau;              /* relative-L2 threshold: hit iff ||q~ - q~_p|| <= tau ||q~|| */
+    float rope_theta;       /* RoPE base (rotate-half), e.g. 500000 */
+    float sm_scale;         /* softmax scale on <q, k>; 0 -> 1/sqrt(d) */
+    int32_t layout;         /* mac_kv_layout */
+    int32_t kv_dtype;       /* mac_dtype of the cache */
+    int32_t page_size;      /* tokens per page (16) */
+    int32_t max_seq_len;    /* token capacity per request (multiple of page_size) */
+    uint32_t flags;         /* MAC_F_* */
+} mac_config;
+
+/* Borrowed view of one layer's KV cache (host struct; pointed-to memory is
+ * device memory owned by the caller).
+ *  contiguous: k, v are [B][Hkv][max_seq_len][d]
+ *  paged:      k, v are [num_pages][Hkv][page_size][d]; request b's token t
+ *              lives in page page_table[b*max_pages_per_req + t/page_size],
+ *              row t%page_size.  Keys are stored post-RoPE. */
+typedef struct {
+    void *k;
+    void *v;
+    const int32_t *page_table;   /* paged only: [B][max_pages_per_req] */
+    int32_t max_pages_per_req;   /* paged only */
+    int32_t num_pages;           /* paged only */
+    const int32_t *seq_lens;     /* [B]; <= 0 marks an idle request */
+} mac_kv_view;
+
+/* Counters since mac_init / mac_reset.  Byte counts are the algorithmic bytes
+ * of key/value rows streamed (each key row and value row counted once). */
+typedef struct {
+    uint64_t steps;              /* mac_decode_step calls */
+    uint64_t decisions;          /* (request, head) decisions taken by match */
+    uint64_t hits;
+    uint64_t misses;
+    uint64_t near_tau;           /* decisions whose relative distance lies within 1e-4 of tau */
+    uint64_t override_invalid;   /* forced hits naming no stored position (taken as misses) */
+    uint64_t kv_tokens_critical; /* keys streamed by complete, summed over KV groups */
+    uint64_t kv_tokens_amend;    /* keys re-read by amend */
+    uint64_t kv_bytes_critical;
+    uint64_t kv_bytes_amend;
+    uint64_t aux_bytes;          /* device memory owned by the handle */
+    uint64_t bad_input;          /* device-side index checks that idled a request or row */
+    float last_us_match;         /* MAC_F_TIMING: last step, microseconds */
+    float last_us_complete;
+    float last_us_reduce;
+    float last_us_amend;
+    float last_us_attention;     /* match + complete + reduce, one event pair */
+} mac_stats_t;
+
+/* Check a configuration without touching the GPU (host only). */
+mac_status mac_config_validate(const mac_config *cfg /* host */);
+
+/* Device bytes mac_init would allocate for cfg on a device with num_cu
+ * compute units (host only). */
+size_t mac_aux_bytes(const mac_config *cfg /* host */, int32_t num_cu);
+
+/* Create a handle: validate cfg, allocate the rings, summaries and work
+ * buffers on the current device, and take main_stream as the default stream.
+ * amend_stream NULL creates a stream of default priority owned by the handle.
+ * Rings start empty (the first decode call misses everywhere). */
+mac_status mac_init(const mac_config *cfg /* host */, void *main_stream, void *amend_stream,
+                    mac_handle *out /* host */);
+
+/* Free everything mac_init allocated; synchronises the handle's streams. */
+mac_status mac_destroy(mac_handle h);
+
+/* Empty every ring and zero the counters (asynchronous on the main stream,
+ * ordered after pending amend work). */
+mac_status mac_reset(mac_handle h);
+
+/* Write this step's post-RoPE key and value rows into the cache: k_new and
+ * v_new are [B][Hkv][d] in the cache dtype; request b's rows go to position
+ * positions[b] (< 0: skipped).  The KV manager's job; the pages say the method
+ * composes with paged KV managers (abstract). */
+mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv /* host */, const void *k_new,
+                         const void *v_new, const int32_t *positions, void *stream);
+
+/* One MAC decode step (Figure 2): q_pre_rope is [B][Hq][d] fp32 pre-RoPE
+ * queries, out receives [B][Hq][d] fp32 attention outputs.  override_pos is
+ * NULL or [B][Hq] int32: -2 no override, -1 force a miss, p >= 0 force a hit
+ * on the ring entry stored at position p (a counted miss when absent).
+ * Waits on the previous step's amend; enqueues match, complete and the
+ * reduce/merge on `stream`, then amend on the amend stream (or on `stream`
+ * with MAC_F_SYNC_AMEND).  The library copies what amend needs, so the caller
+ * may reuse q_pre_rope, out and seq_lens as soon as the step's work on
+ * `stream` has run. */
+mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv /* host */,
+                           const float *q_pre_rope, float *out, const int32_t *override_pos,
+                           void *stream);
+
+/* Synchronise the handle's streams and copy the counters (host). */
+mac_status mac_stats(mac_handle h, mac_stats_t *out /* host */);
+
+/* MAC_F_RECORD_DEBUG only: synchronise and copy the last step's per-head
+ * matched position (-1 on a miss), hit flag and relative distance of the
+ * nearest entry (NaN when the ring held none); each [B][Hq] host arrays, any
+ * may be NULL. */
+mac_status mac_debug_last(mac_handle h, int32_t *p /* host */, uint8_t *hit /* host */,
+                          float *rel /* host */);
+
+/* Message for the handle's last failed call ("" if none); h NULL gives the
+ * message of the last failed mac_init or validation on this thread. */
+const char *mac_last_error(mac_handle h);
+
+const char *mac_status_string(mac_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAC_H */

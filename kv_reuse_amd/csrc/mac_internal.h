@@ -1,0 +1,84 @@
+// mac_internal.h -- state layout and kernel launch interface shared by the
+// host runtime (mac_runtime.cpp) and the gfx950 kernels (mac_kernels.hip).
+//
+// Device memory owned by a handle (fp32 unless noted):
+//   ring_q     [B][Hq][W][D]        pre-RoPE queries of recent steps
+//   ring_s     [B][Hq][W][SUMM]     summaries AS_{1:pos-r}: o[D], M, l, pad
+//   ring_pos   [B][W]  int32        position stored in each slot (-1 empty)
+//   q_copy     [B][Hq][D]           this step's pre-RoPE queries (for amend)
+//   q_rot      [B][Hq][D]           this step's post-RoPE queries
+//   m_buf      [B]     int32        this step's query position (-1 idle)
+//   dec_slot   [B][Hq] int32        matched slot (-1 miss)
+//   dec_p      [B][Hq] int32        matched position (-1 miss)
+//   dec_start  [B][Hq] int32        first key of the head's span
+//   dec_rel    [B][Hq]              relative distance of the nearest entry
+//   grp_start  [B][Hkv] int32       first key of the group's union span (-1 idle)
+//   partials   [NW + B*Hkv][G][SUMM] per-(worker, group) unnormalised summaries
+//   as_full    [B][Hq][SUMM]        AS_{1:m} of this step, input of amend
+//   stats      [MAC_NSTAT] uint64
+// M values inside the library are in log2 units of the scaled logit
+// (s * log2 e); every summary the library stores uses the same units.
+#pragma once
+#include <cstdint>
+#include <hip/hip_runtime.h>
+
+namespace mac {
+
+constexpr int D = 128;          // head_dim supported by the kernels
+constexpr int SUMM = D + 4;     // o[D], M, l, 2 pad floats (16-byte rows)
+constexpr int PAGE = 16;        // tokens per page
+constexpr int BLOCK = 256;      // threads per workgroup (4 waves of 64)
+constexpr int WAVES = BLOCK / 64;
+constexpr int MAX_W = 64;       // ring slots per (request, head)
+constexpr int MAX_GROUPS = 4096;  // B * Hkv
+constexpr int MIN_PAGES_PER_WORKER = 2;
+
+enum Stat {
+    ST_DECISIONS = 0, ST_HITS, ST_MISSES, ST_NEAR_TAU, ST_OVR_INVALID, ST_TOK_CRIT, ST_TOK_AMEND,
+    ST_BAD_INPUT, MAC_NSTAT = 16
+};
+
+struct KvView {
+    void *k;
+    void *v;
+    const int32_t *page_table;
+    int32_t max_pages;      // pages per request (paged) -- bound of page_table rows
+    int32_t num_pages;      // paged: pages in the pool
+    int32_t max_seq_len;    // contiguous: row stride in tokens; both: token bound
+    int32_t paged;
+};
+
+struct Shape {
+    int32_t B, Hq, Hkv, G, W, r;
+    float tau, scale_log2;  // scale_log2 = sm_scale * log2(e)
+    int32_t reuse;          // 0: every head misses
+};
+
+struct State {
+    float *ring_q, *ring_s, *q_copy, *q_rot, *partials, *as_full, *dec_rel;
+    int32_t *ring_pos, *m_buf, *dec_slot, *dec_p, *dec_start, *grp_start;
+    unsigned long long *stats;
+    const double *inv_freq;   // [D/2] theta^(-2i/D), fp64
+    int32_t n_workers;        // waves in the complete grid
+};
+
+// Launchers (enqueue only; return the launch status).
+hipError_t launch_match(const Shape &s, const State &st, const KvView &kv, const int32_t *seq_lens,
+                        const float *q_pre, const int32_t *override_pos, int waves,
+                        hipStream_t stream);
+// Waves per match block whose ring tiles fit in max_lds bytes of LDS.
+int match_waves(const Shape &s, size_t max_lds);
+hipError_t launch_complete(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
+                           int n_blocks, hipStream_t stream);
+hipError_t launch_reduce(const Shape &s, const State &st, float *out, hipStream_t stream);
+hipError_t launch_amend(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
+                        int slot_new, hipStream_t stream);
+hipError_t launch_append(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
+                         const void *k_new, const void *v_new, const int32_t *positions,
+                         hipStream_t stream);
+hipError_t launch_reset(const Shape &s, const State &st, hipStream_t stream);
+// Workgroups of the complete kernel resident per CU (occupancy query).
+int complete_blocks_per_cu(bool kv_fp32, int G, size_t plan_lds_bytes);
+bool supported_group(int G);
+
+}  // namespace mac

@@ -1,0 +1,1006 @@
+// mac_kernels.hip -- gfx950 kernels of the MAC-Attention decode step.
+//
+// MAC-Attention (arXiv 2604.00235), paper card, Figure 2 and Figure 3:
+//   match_kernel     (a) pre-RoPE L2 nearest neighbour over the ring, threshold,
+//                    RoPE of the query, per-head and per-group key spans
+//   complete_kernel  (b) split-KV flash-decode over each group's union span,
+//                    equal page shares per wave (the load-balanced plan of
+//                    Figure 3 (b), built on the device)
+//   reduce_kernel    (b) combine the per-wave partial summaries, log-domain
+//                    merge (+) with the matched entry's stored AS_{1:p-r}
+//   amend_kernel     (c) recompute the last-r band, log-domain removal (-),
+//                    ring insert; runs on the amend stream
+//   append_kernel    KV manager side: write this step's key/value rows
+//
+// Wave64 throughout.  Key/value rows stream as 16-byte loads: for bf16 a row
+// of 128 elements is 16 lanes, a wave load covers 4 tokens and a 16-token page
+// is 4 loads of K and 4 of V; fp32 rows take 32 lanes.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+
+#include "mac_internal.h"
+
+namespace mac {
+namespace {
+
+constexpr float NEG_INF = -INFINITY;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ------------------------------------------------------------ lane exchange
+// DPP for exchanges inside a quad, ds_swizzle (bit mode) inside 32 lanes,
+// ds_bpermute across the two halves.
+template <int OFF>
+__device__ __forceinline__ int xor_lanes_i(int v)
+{
+    static_assert(OFF > 0 && OFF < 64 && (OFF & (OFF - 1)) == 0, "power of two");
+    if constexpr (OFF == 1)
+        return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+    else if constexpr (OFF == 2)
+        return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+    else if constexpr (OFF < 32)
+        return __builtin_amdgcn_ds_swizzle(v, (OFF << 10) | 0x1F);   // xor mask, and 0x1F
+    else
+        return __shfl_xor(v, 32, 64);
+}
+
+template <int OFF>
+__device__ __forceinline__ float xor_lanes(float v)
+{
+    return __int_as_float(xor_lanes_i<OFF>(__float_as_int(v)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each 16-lane row: after the two quad exchanges every quad is
+// uniform, so the half mirror and the full mirror finish the reduction.
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);   // row_half_mirror
+    v += dpp_f<0x140>(v);   // row_mirror
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = row16_sum(v);
+    v += xor_lanes<16>(v);
+    v += xor_lanes<32>(v);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = fmaxf(v, xor_lanes<1>(v));
+    v = fmaxf(v, xor_lanes<2>(v));
+    v = fmaxf(v, xor_lanes<4>(v));
+    v = fmaxf(v, xor_lanes<8>(v));
+    v = fmaxf(v, xor_lanes<16>(v));
+    v = fmaxf(v, xor_lanes<32>(v));
+    return v;
+}
+
+// ------------------------------------------------------- key/value element
+template <typename T>
+struct Kv;
+template <>
+struct Kv<uint16_t> {           // bf16 bit patterns
+    static constexpr int E = 8;     // elements per 16-byte lane load
+    static constexpr int LPR = 16;  // lanes per 128-element row
+    static constexpr int RPL = 4;   // rows (tokens) per wave load
+    static constexpr int LPP = 4;   // wave loads per 16-token page
+};
+template <>
+struct Kv<float> {
+    static constexpr int E = 4;
+    static constexpr int LPR = 32;
+    static constexpr int RPL = 2;
+    static constexpr int LPP = 8;
+};
+
+__device__ __forceinline__ void to_f32(const uint4 &w, float (&f)[8])
+{
+    f[0] = __uint_as_float(w.x << 16);
+    f[1] = __uint_as_float(w.x & 0xffff0000u);
+    f[2] = __uint_as_float(w.y << 16);
+    f[3] = __uint_as_float(w.y & 0xffff0000u);
+    f[4] = __uint_as_float(w.z << 16);
+    f[5] = __uint_as_float(w.z & 0xffff0000u);
+    f[6] = __uint_as_float(w.w << 16);
+    f[7] = __uint_as_float(w.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ void to_f32(const uint4 &w, float (&f)[4])
+{
+    f[0] = __uint_as_float(w.x);
+    f[1] = __uint_as_float(w.y);
+    f[2] = __uint_as_float(w.z);
+    f[3] = __uint_as_float(w.w);
+}
+
+template <typename T>
+__device__ __forceinline__ float row_sum(float v)
+{
+    v = row16_sum(v);
+    if constexpr (Kv<T>::LPR == 32)
+        v += xor_lanes<16>(v);
+    return v;
+}
+
+// Address of the 16 x D block holding tokens [16*page, 16*page+16) of
+// (request b, KV head kvh).  A page id outside the pool is replaced by page 0
+// and counted, so a corrupt table never reads outside the cache.
+template <typename T>
+__device__ __forceinline__ const T *kv_page(const KvView &kv, const void *base, int b, int kvh,
+                                            int Hkv, int page, unsigned long long *bad)
+{
+    long off;
+    if (kv.paged) {
+        int pid = kv.page_table[(long)b * kv.max_pages + page];
+        if ((unsigned)pid >= (unsigned)kv.num_pages) {
+            atomicAdd(bad, 1ULL);
+            pid = 0;
+        }
+        off = ((long)pid * Hkv + kvh) * (PAGE * D);
+    } else {
+        off = ((long)b * Hkv + kvh) * (long)kv.max_seq_len * D + (long)page * (PAGE * D);
+    }
+    return reinterpret_cast<const T *>(base) + off;
+}
+
+// ------------------------------------------------ flash-decode wave worker
+// One wave keeps, per head of its GQA group and per row group of lanes (the
+// tokens it loads), a running max M (log2 units), normaliser L and
+// unnormalised output acc over its E output columns.
+template <int G, int E>
+struct WaveAcc {
+    float M[G], L[G], acc[G][E];
+    __device__ __forceinline__ void init()
+    {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            M[g] = NEG_INF;
+            L[g] = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                acc[g][e] = 0.f;
+        }
+    }
+};
+
+template <typename T>
+struct PageRegs {
+    uint4 k[Kv<T>::LPP], v[Kv<T>::LPP];
+};
+
+template <typename T>
+__device__ __forceinline__ void load_page(PageRegs<T> &r, const T *kp, const T *vp)
+{
+    using K = Kv<T>;
+    const int lane = lane_id(), row = lane / K::LPR, col = lane % K::LPR;
+#pragma unroll
+    for (int s = 0; s < K::LPP; ++s)
+        r.k[s] = *reinterpret_cast<const uint4 *>(kp + (s * K::RPL + row) * D + col * K::E);
+#pragma unroll
+    for (int s = 0; s < K::LPP; ++s)
+        r.v[s] = *reinterpret_cast<const uint4 *>(vp + (s * K::RPL + row) * D + col * K::E);
+}
+
+// Fold one page into the wave's state.  Token t of the page is valid for
+// head g iff hs[g] <= t <= m; `masked` is false when every token is valid for
+// every head (the common case), and rows past m are zeroed since a cache slot
+// that was never written may hold any bits.
+template <typename T, int G>
+__device__ __forceinline__ void compute_page(const PageRegs<T> &r, int tok0, int m,
+                                             const int (&hs)[G], bool masked,
+                                             const float (&q)[G][Kv<T>::E],
+                                             WaveAcc<G, Kv<T>::E> &st)
+{
+    using K = Kv<T>;
+    constexpr int E = K::E;
+    const int row = lane_id() / K::LPR;
+    float lg[K::LPP][G];
+#pragma unroll
+    for (int s = 0; s < K::LPP; ++s) {
+        float kf[E];
+        to_f32(r.k[s], kf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float a = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                a = fmaf(q[g][e], kf[e], a);
+            lg[s][g] = row_sum<T>(a);
+        }
+    }
+    if (masked) {
+#pragma unroll
+        for (int s = 0; s < K::LPP; ++s) {
+            const int t = tok0 + s * K::RPL + row;
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                if (t < hs[g] || t > m)
+                    lg[s][g] = NEG_INF;
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float mx = lg[0][g];
+#pragma unroll
+        for (int s = 1; s < K::LPP; ++s)
+            mx = fmaxf(mx, lg[s][g]);
+        const float mn = fmaxf(st.M[g], mx);
+        const float base = mn == NEG_INF ? 0.f : mn;
+        const float alpha = exp2f(st.M[g] - base);
+        st.M[g] = mn;
+        st.L[g] *= alpha;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            st.acc[g][e] *= alpha;
+#pragma unroll
+        for (int s = 0; s < K::LPP; ++s)
+            lg[s][g] = exp2f(lg[s][g] - base);
+    }
+#pragma unroll
+    for (int s = 0; s < K::LPP; ++s) {
+        float vf[E];
+        to_f32(r.v[s], vf);
+        if (masked && tok0 + s * K::RPL + row > m) {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                vf[e] = 0.f;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            st.L[g] += lg[s][g];
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                st.acc[g][e] = fmaf(lg[s][g], vf[e], st.acc[g][e]);
+        }
+    }
+}
+
+// Combine the wave's row groups and store, per head, the unnormalised
+// summary (acc[D], M, L) at dst[g*SUMM ..] (global memory or LDS).
+template <typename T, int G>
+__device__ __forceinline__ void store_wave_summary(WaveAcc<G, Kv<T>::E> &st, float *dst)
+{
+    using K = Kv<T>;
+    constexpr int E = K::E;
+    const int lane = lane_id(), row = lane / K::LPR, col = lane % K::LPR;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float Mt = st.M[g];
+        if constexpr (K::LPR == 16)
+            Mt = fmaxf(Mt, xor_lanes<16>(Mt));
+        Mt = fmaxf(Mt, xor_lanes<32>(Mt));
+        const float base = Mt == NEG_INF ? 0.f : Mt;
+        const float sc = exp2f(st.M[g] - base);
+        float Lr = st.L[g] * sc;
+        float a[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            a[e] = st.acc[g][e] * sc;
+        if constexpr (K::LPR == 16) {
+            Lr += xor_lanes<16>(Lr);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                a[e] += xor_lanes<16>(a[e]);
+        }
+        Lr += xor_lanes<32>(Lr);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            a[e] += xor_lanes<32>(a[e]);
+        if (row == 0) {
+#pragma unroll
+            for (int e = 0; e < E; e += 4)
+                *reinterpret_cast<float4 *>(dst + g * SUMM + col * E + e) =
+                    make_float4(a[e], a[e + 1], a[e + 2], a[e + 3]);
+        }
+        if (lane == 0) {
+            dst[g * SUMM + D] = Mt;
+            dst[g * SUMM + D + 1] = Lr;
+        }
+    }
+}
+
+// Queries of the G heads of (b, kvh), this lane's E columns, scaled so that
+// q.k is the logit in log2 units.
+template <typename T, int G>
+__device__ __forceinline__ void load_group_queries(const Shape &s, const State &st, int b, int kvh,
+                                                   float (&q)[G][Kv<T>::E])
+{
+    using K = Kv<T>;
+    const int col = lane_id() % K::LPR;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float *src = st.q_rot + ((long)b * s.Hq + kvh * G + g) * D + col * K::E;
+#pragma unroll
+        for (int e = 0; e < K::E; e += 4) {
+            float4 x = *reinterpret_cast<const float4 *>(src + e);
+            q[g][e + 0] = x.x * s.scale_log2;
+            q[g][e + 1] = x.y * s.scale_log2;
+            q[g][e + 2] = x.z * s.scale_log2;
+            q[g][e + 3] = x.w * s.scale_log2;
+        }
+    }
+}
+
+// ------------------------------------------------------------------- plan
+// Exclusive prefix sum of a[0..n) in LDS by the whole block; a[n] = total.
+__device__ void block_exclusive_scan(int *a, int n)
+{
+    __shared__ int wsum[WAVES];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int per = (n + BLOCK - 1) / BLOCK;
+    const int lo = min(n, t * per), hi = min(n, lo + per);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i)
+        sum += a[i];
+    int x = sum;
+    for (int off = 1; off < 64; off <<= 1) {
+        int y = __shfl_up(x, off, 64);
+        if (lane >= off)
+            x += y;
+    }
+    if (lane == 63)
+        wsum[wv] = x;
+    __syncthreads();
+    int pre = 0, tot = 0;
+    for (int i = 0; i < WAVES; ++i) {
+        if (i < wv)
+            pre += wsum[i];
+        tot += wsum[i];
+    }
+    int run = pre + x - sum;
+    for (int i = lo; i < hi; ++i) {
+        int v = a[i];
+        a[i] = run;
+        run += v;
+    }
+    if (t == 0)
+        a[n] = tot;
+    __syncthreads();
+}
+
+// Page offsets of every group's union span in the flattened work list:
+// off[g] = pages of groups before g, off[nG] = all pages of the step.
+__device__ void build_plan(const Shape &s, const State &st, int *off)
+{
+    const int nG = s.B * s.Hkv;
+    for (int g = threadIdx.x; g < nG; g += BLOCK) {
+        const int gs = st.grp_start[g];
+        const int m = st.m_buf[g / s.Hkv];
+        off[g] = (gs < 0 || m < 0) ? 0 : (m / PAGE - gs / PAGE + 1);
+    }
+    __syncthreads();
+    block_exclusive_scan(off, nG);
+}
+
+// Waves that take part: every worker gets at least MIN_PAGES_PER_WORKER pages.
+__device__ __forceinline__ int active_workers(int n_workers, int P)
+{
+    return min(n_workers, (P + MIN_PAGES_PER_WORKER - 1) / MIN_PAGES_PER_WORKER);
+}
+
+// Worker w owns flattened pages [w*P/nW, (w+1)*P/nW); owner of page x:
+__device__ __forceinline__ int page_owner(long x, int nW, int P)
+{
+    return (int)(((x + 1) * (long)nW - 1) / P);
+}
+
+// Last group g with off[g] <= x (groups with no pages are skipped by caller).
+__device__ __forceinline__ int find_group(const int *off, int nG, long x)
+{
+    int lo = 0, hi = nG - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= x)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// ================================================================== match
+// Grid (Hkv, B), 64 to 256 threads: the block owns one GQA group, its waves
+// take the group's query heads in turn.  Each head's ring tile (W x D fp32) is staged in
+// LDS with coalesced 16-byte loads; 64/W lanes share a slot's distance, and a
+// DPP/ds_swizzle butterfly finds the nearest entry.
+__global__ __launch_bounds__(BLOCK) void match_kernel(Shape s, State st, KvView kv,
+                                                      const int32_t *__restrict__ seq_lens,
+                                                      const float *__restrict__ q_pre,
+                                                      const int32_t *__restrict__ ovr)
+{
+    extern __shared__ float lds[];
+    __shared__ int h_start[64];
+    __shared__ int cnt[4];   // hits, misses, near tau, invalid overrides
+    const int b = blockIdx.y, kvh = blockIdx.x;
+    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    constexpr int RS = D + 4;   // LDS row stride (floats)
+
+    int m = seq_lens[b] - 1;
+    bool bad = false;
+    if (m >= 0 && (m >= kv.max_seq_len || (kv.paged && m / PAGE >= kv.max_pages)))
+        bad = true;
+    if (bad)
+        m = -1;
+    if (threadIdx.x < 4)
+        cnt[threadIdx.x] = 0;
+    if (kvh == 0 && threadIdx.x == 0) {
+        st.m_buf[b] = m;
+        if (bad)
+            atomicAdd(&st.stats[ST_BAD_INPUT], 1ULL);
+    }
+    __syncthreads();
+
+    // lanes per ring slot: a power of two, at most 32 so each lane owns a
+    // whole number of float4 columns (D / L >= 4)
+    int L = 64 / s.W;
+    while (L & (L - 1))
+        L &= L - 1;
+    if (L > 32)
+        L = 32;
+    const int nwv = blockDim.x >> 6;   // waves in the block (sized to the LDS budget)
+    float *tile = lds + wv * (s.W * RS + D);
+    float *qs = tile + s.W * RS;
+
+    for (int hb = 0; hb < s.G; hb += nwv) {
+        const int hh = hb + wv;
+        const bool head = hh < s.G;
+        const bool act = head && m >= 0;
+        const long idx = (long)b * s.Hq + kvh * s.G + hh;
+        float qa = 0.f, qb = 0.f;
+        if (act) {
+            qa = q_pre[idx * D + lane];
+            qb = q_pre[idx * D + lane + 64];
+            st.q_copy[idx * D + lane] = qa;
+            st.q_copy[idx * D + lane + 64] = qb;
+            // rotate-half RoPE, angle m * theta^(-2i/D) formed in fp64
+            const double phi = (double)m * st.inv_freq[lane];
+            double sn, cs;
+            sincos(phi, &sn, &cs);
+            st.q_rot[idx * D + lane] = (float)((double)qa * cs - (double)qb * sn);
+            st.q_rot[idx * D + lane + 64] = (float)((double)qb * cs + (double)qa * sn);
+            if (s.reuse) {
+                const float *src = st.ring_q + idx * s.W * D;
+                for (int i = lane; i < s.W * (D / 4); i += 64) {
+                    const int j = i / (D / 4), c4 = i % (D / 4);
+                    *reinterpret_cast<float4 *>(tile + j * RS + c4 * 4) =
+                        *reinterpret_cast<const float4 *>(src + (long)j * D + c4 * 4);
+                }
+                qs[lane] = qa;
+                qs[lane + 64] = qb;
+            }
+        }
+        __syncthreads();
+        int slot = -1, p = -1, start = 0;
+        float rel = NAN;
+        if (act && s.reuse) {
+            const int j = lane / L, part = lane % L, span = D / L;
+            float dp = 0.f;
+            if (j < s.W) {
+                const float *rr = tile + j * RS + part * span;
+                const float *qq = qs + part * span;
+                for (int e = 0; e < span; e += 4) {
+                    const float4 x = *reinterpret_cast<const float4 *>(rr + e);
+                    const float4 y = *reinterpret_cast<const float4 *>(qq + e);
+                    const float t0 = y.x - x.x, t1 = y.y - x.y, t2 = y.z - x.z, t3 = y.w - x.w;
+                    dp = fmaf(t0, t0, dp);
+                    dp = fmaf(t1, t1, dp);
+                    dp = fmaf(t2, t2, dp);
+                    dp = fmaf(t3, t3, dp);
+                }
+            }
+            if (L >= 2) dp += xor_lanes<1>(dp);
+            if (L >= 4) dp += xor_lanes<2>(dp);
+            if (L >= 8) dp += xor_lanes<4>(dp);
+            if (L >= 16) dp += xor_lanes<8>(dp);
+            if (L >= 32) dp += xor_lanes<16>(dp);
+            const int pos = j < s.W ? st.ring_pos[(long)b * s.W + j] : -1;
+            const bool valid = j < s.W && pos >= 0 && pos <= m;
+            float kd = valid ? dp : INFINITY;
+            int kp = valid ? pos : INT_MIN;
+            int kj = valid ? j : -1;
+            // nearest entry: smallest distance, then newest position, then larger slot
+#define MAC_ARGMIN_STEP(OFF)                                                                 \
+    {                                                                                       \
+        const float d2 = xor_lanes<OFF>(kd);                                                \
+        const int p2 = xor_lanes_i<OFF>(kp);                                                \
+        const int j2 = xor_lanes_i<OFF>(kj);                                                \
+        if (d2 < kd || (d2 == kd && (p2 > kp || (p2 == kp && j2 > kj)))) {                  \
+            kd = d2;                                                                        \
+            kp = p2;                                                                        \
+            kj = j2;                                                                        \
+        }                                                                                   \
+    }
+            MAC_ARGMIN_STEP(1)
+            MAC_ARGMIN_STEP(2)
+            MAC_ARGMIN_STEP(4)
+            MAC_ARGMIN_STEP(8)
+            MAC_ARGMIN_STEP(16)
+            MAC_ARGMIN_STEP(32)
+#undef MAC_ARGMIN_STEP
+            const float q2 = wave_sum(qa * qa + qb * qb);
+            if (kp >= 0) {
+                rel = q2 > 0.f ? sqrtf(kd / q2) : (kd == 0.f ? 0.f : INFINITY);
+                // relative-L2 test compared squared: D <= tau^2 |q~|^2
+                if (s.tau >= 0.f && kd <= s.tau * s.tau * q2) {
+                    slot = kj;
+                    p = kp;
+                }
+                if (lane == 0 && fabsf(rel - s.tau) < 1e-4f)
+                    atomicAdd(&cnt[2], 1);
+            }
+            if (ovr) {
+                const int ov = ovr[idx];
+                if (ov != -2) {
+                    slot = -1;
+                    p = -1;
+                    if (ov >= 0) {
+                        const bool mine = lane < s.W && ov <= m &&
+                                          st.ring_pos[(long)b * s.W + lane] == ov;
+                        const unsigned long long bal = __ballot(mine);
+                        if (bal) {
+                            slot = 63 - __clzll(bal);
+                            p = ov;
+                        } else if (lane == 0) {
+                            atomicAdd(&cnt[3], 1);
+                        }
+                    }
+                }
+            }
+            if (slot >= 0)
+                start = max(p - s.r + 1, 0);
+        }
+        if (head && lane == 0) {
+            st.dec_slot[idx] = slot;
+            st.dec_p[idx] = p;
+            st.dec_start[idx] = start;
+            st.dec_rel[idx] = rel;
+            h_start[hh] = start;
+            if (act)
+                atomicAdd(&cnt[slot >= 0 ? 0 : 1], 1);
+        }
+        __syncthreads();
+    }
+
+    if (threadIdx.x == 0) {
+        int gs = -1;
+        if (m >= 0) {
+            gs = m + 1;
+            for (int h = 0; h < s.G; ++h)
+                gs = min(gs, h_start[h]);
+        }
+        st.grp_start[(long)b * s.Hkv + kvh] = gs;
+        if (m >= 0) {
+            atomicAdd(&st.stats[ST_HITS], (unsigned long long)cnt[0]);
+            atomicAdd(&st.stats[ST_MISSES], (unsigned long long)cnt[1]);
+            atomicAdd(&st.stats[ST_DECISIONS], (unsigned long long)(cnt[0] + cnt[1]));
+            atomicAdd(&st.stats[ST_NEAR_TAU], (unsigned long long)cnt[2]);
+            atomicAdd(&st.stats[ST_OVR_INVALID], (unsigned long long)cnt[3]);
+            atomicAdd(&st.stats[ST_TOK_CRIT], (unsigned long long)(m - gs + 1));
+            if (s.reuse && m - s.r >= 0)
+                atomicAdd(&st.stats[ST_TOK_AMEND], (unsigned long long)s.r);
+        }
+    }
+}
+
+// =============================================================== complete
+// Persistent grid of independent wave workers.  Every block rebuilds the
+// plan (a scan over B*Hkv group spans) in LDS; the step's pages, group after
+// group, are split into equal contiguous shares, one per active wave.  A
+// worker writes one partial summary per group it touches, into slot
+// (worker + group), which is unique along the flattened list.
+template <typename T, int G>
+__global__ __launch_bounds__(BLOCK) void complete_kernel(Shape s, State st, KvView kv)
+{
+    extern __shared__ int s_off[];
+    using K = Kv<T>;
+    const int nG = s.B * s.Hkv;
+    build_plan(s, st, s_off);
+    const int P = s_off[nG];
+    if (P == 0)
+        return;
+    const int nW = active_workers(st.n_workers, P);
+    const int w = blockIdx.x * WAVES + (threadIdx.x >> 6);
+    if (w >= nW)
+        return;
+    long x = (long)w * P / nW;
+    const long x1 = (long)(w + 1) * P / nW;
+    int g = find_group(s_off, nG, x);
+    while (x < x1) {
+        while (s_off[g + 1] <= x)
+            ++g;
+        const long gend = min((long)s_off[g + 1], x1);
+        const int b = g / s.Hkv, kvh = g % s.Hkv;
+        const int m = st.m_buf[b];
+        const int first_page = st.grp_start[g] / PAGE;
+        int hs[G];
+        int hmax = 0;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            hs[h] = st.dec_start[(long)b * s.Hq + kvh * G + h];
+            hmax = max(hmax, hs[h]);
+        }
+        float q[G][K::E];
+        load_group_queries<T, G>(s, st, b, kvh, q);
+        WaveAcc<G, K::E> acc;
+        acc.init();
+
+        PageRegs<T> r0, r1;
+        int page = first_page + (int)(x - s_off[g]);
+        const int last = first_page + (int)(gend - s_off[g]) - 1;
+        load_page<T>(r0, kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page, &st.stats[ST_BAD_INPUT]),
+                     kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page, &st.stats[ST_BAD_INPUT]));
+        while (true) {
+            if (page + 1 <= last)
+                load_page<T>(r1,
+                             kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page + 1, &st.stats[ST_BAD_INPUT]),
+                             kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page + 1, &st.stats[ST_BAD_INPUT]));
+            {
+                const int tok0 = page * PAGE;
+                compute_page<T, G>(r0, tok0, m, hs, tok0 < hmax || tok0 + PAGE - 1 > m, q, acc);
+            }
+            if (++page > last)
+                break;
+            if (page + 1 <= last)
+                load_page<T>(r0,
+                             kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page + 1, &st.stats[ST_BAD_INPUT]),
+                             kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page + 1, &st.stats[ST_BAD_INPUT]));
+            {
+                const int tok0 = page * PAGE;
+                compute_page<T, G>(r1, tok0, m, hs, tok0 < hmax || tok0 + PAGE - 1 > m, q, acc);
+            }
+            if (++page > last)
+                break;
+        }
+        store_wave_summary<T, G>(acc, st.partials + ((long)w + g) * G * SUMM);
+        x = gend;
+    }
+}
+
+// ================================================================= reduce
+// Grid (Hkv, B): combine a group's partial summaries per head, then merge
+// (+) with the matched entry's stored AS_{1:p-r}.  Writes out (normalised)
+// and keeps AS_{1:m} for amend.  Each lane owns two output columns.
+template <int G>
+__global__ __launch_bounds__(BLOCK) void reduce_kernel(Shape s, State st, float *__restrict__ out)
+{
+    extern __shared__ int s_off[];
+    const int nG = s.B * s.Hkv;
+    build_plan(s, st, s_off);
+    const int P = s_off[nG];
+    const int nW = P > 0 ? active_workers(st.n_workers, P) : 1;
+    const int b = blockIdx.y, kvh = blockIdx.x, g = b * s.Hkv + kvh;
+    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const int m = st.m_buf[b];
+    const bool idle = m < 0 || s_off[g + 1] == s_off[g];
+    for (int hh = wv; hh < G; hh += WAVES) {
+        const long idx = (long)b * s.Hq + kvh * G + hh;
+        float *o = out + idx * D;
+        float *asf = st.as_full + idx * SUMM;
+        if (idle) {
+            *reinterpret_cast<float2 *>(o + 2 * lane) = make_float2(0.f, 0.f);
+            *reinterpret_cast<float2 *>(asf + 2 * lane) = make_float2(0.f, 0.f);
+            if (lane == 0) {
+                asf[D] = NEG_INF;
+                asf[D + 1] = 0.f;
+            }
+            continue;
+        }
+        const int wlo = page_owner(s_off[g], nW, P);
+        const int whi = page_owner((long)s_off[g + 1] - 1, nW, P);
+        float Mx = NEG_INF;
+        for (int w = wlo + lane; w <= whi; w += 64)
+            Mx = fmaxf(Mx, st.partials[(((long)w + g) * G + hh) * SUMM + D]);
+        Mx = wave_max(Mx);
+        const float base = Mx == NEG_INF ? 0.f : Mx;
+        float a0 = 0.f, a1 = 0.f, Lf = 0.f;
+        for (int w = wlo; w <= whi; ++w) {
+            const float *pp = st.partials + (((long)w + g) * G + hh) * SUMM;
+            const float sc = exp2f(pp[D] - base);
+            const float2 v = *reinterpret_cast<const float2 *>(pp + 2 * lane);
+            Lf = fmaf(pp[D + 1], sc, Lf);
+            a0 = fmaf(v.x, sc, a0);
+            a1 = fmaf(v.y, sc, a1);
+        }
+        float o0 = a0 / Lf, o1 = a1 / Lf, Mo = Mx, Lo = Lf;
+        const int slot = st.dec_slot[idx];
+        if (slot >= 0) {
+            const float *rs = st.ring_s + (idx * s.W + slot) * SUMM;
+            const float Ms = rs[D], Ls = rs[D + 1];
+            if (Ls > 0.f) {
+                const float Mn = fmaxf(Ms, Mx);
+                const float ca = Ls * exp2f(Ms - Mn), cb = Lf * exp2f(Mx - Mn);
+                const float Ln = ca + cb;
+                const float2 so = *reinterpret_cast<const float2 *>(rs + 2 * lane);
+                o0 = (ca * so.x + cb * o0) / Ln;
+                o1 = (ca * so.y + cb * o1) / Ln;
+                Mo = Mn;
+                Lo = Ln;
+            }
+        }
+        *reinterpret_cast<float2 *>(o + 2 * lane) = make_float2(o0, o1);
+        *reinterpret_cast<float2 *>(asf + 2 * lane) = make_float2(o0, o1);
+        if (lane == 0) {
+            asf[D] = Mo;
+            asf[D + 1] = Lo;
+        }
+    }
+}
+
+// ================================================================== amend
+// Grid (Hkv, B): the block's waves share the band [m-r+1, m] page by page,
+// combine in LDS, then per head AS_{1:m-r} = AS_{1:m} (-) band and the ring
+// slot receives (q~_m, AS_{1:m-r}, m).
+template <typename T, int G>
+__global__ __launch_bounds__(BLOCK) void amend_kernel(Shape s, State st, KvView kv, int slot_new)
+{
+    __shared__ float red[WAVES][G][SUMM];
+    using K = Kv<T>;
+    const int b = blockIdx.y, kvh = blockIdx.x;
+    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const int m = st.m_buf[b];
+    if (m < 0)
+        return;
+    const bool has_prefix = m - s.r >= 0;
+    if (has_prefix) {
+        const int lo = m - s.r + 1;
+        int hs[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+            hs[h] = lo;
+        float q[G][K::E];
+        load_group_queries<T, G>(s, st, b, kvh, q);
+        WaveAcc<G, K::E> acc;
+        acc.init();
+        PageRegs<T> r;
+        for (int page = lo / PAGE + wv; page <= m / PAGE; page += WAVES) {
+            load_page<T>(r, kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page, &st.stats[ST_BAD_INPUT]),
+                         kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page, &st.stats[ST_BAD_INPUT]));
+            const int tok0 = page * PAGE;
+            compute_page<T, G>(r, tok0, m, hs, tok0 < lo || tok0 + PAGE - 1 > m, q, acc);
+        }
+        store_wave_summary<T, G>(acc, &red[wv][0][0]);
+    }
+    __syncthreads();
+    for (int hh = wv; hh < G; hh += WAVES) {
+        const long idx = (long)b * s.Hq + kvh * G + hh;
+        float so0 = 0.f, so1 = 0.f, sM = NEG_INF, sL = 0.f;   // EMPTY
+        if (has_prefix) {
+            float Mx = NEG_INF;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w)
+                Mx = fmaxf(Mx, red[w][hh][D]);
+            const float base = Mx == NEG_INF ? 0.f : Mx;
+            float a0 = 0.f, a1 = 0.f, Lb = 0.f;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) {
+                const float sc = exp2f(red[w][hh][D] - base);
+                Lb = fmaf(red[w][hh][D + 1], sc, Lb);
+                a0 = fmaf(red[w][hh][2 * lane], sc, a0);
+                a1 = fmaf(red[w][hh][2 * lane + 1], sc, a1);
+            }
+            const float *z = st.as_full + idx * SUMM;
+            const float Mz = z[D], Lz = z[D + 1];
+            const float c = Lb * exp2f(Mx - Mz);
+            const float l = Lz - c;
+            if (l > Lz * 0x1p-24f) {
+                const float2 zo = *reinterpret_cast<const float2 *>(z + 2 * lane);
+                so0 = (Lz * zo.x - c * (a0 / Lb)) / l;
+                so1 = (Lz * zo.y - c * (a1 / Lb)) / l;
+                sM = Mz;
+                sL = l;
+            }
+        }
+        float *dst = st.ring_s + (idx * s.W + slot_new) * SUMM;
+        *reinterpret_cast<float2 *>(dst + 2 * lane) = make_float2(so0, so1);
+        if (lane == 0) {
+            dst[D] = sM;
+            dst[D + 1] = sL;
+        }
+        const float2 qv = *reinterpret_cast<const float2 *>(st.q_copy + idx * D + 2 * lane);
+        *reinterpret_cast<float2 *>(st.ring_q + (idx * s.W + slot_new) * D + 2 * lane) = qv;
+    }
+    if (kvh == 0 && threadIdx.x == 0)
+        st.ring_pos[(long)b * s.W + slot_new] = m;
+}
+
+// ================================================================= append
+// Grid (Hkv, B), 64 threads: copy one K row and one V row, 16 bytes a thread.
+template <typename T>
+__global__ __launch_bounds__(64) void append_kernel(Shape s, State st, KvView kv,
+                                                    const T *__restrict__ kn,
+                                                    const T *__restrict__ vn,
+                                                    const int32_t *__restrict__ positions)
+{
+    constexpr int CH = D * (int)sizeof(T) / 16;
+    const int b = blockIdx.y, kvh = blockIdx.x, t = threadIdx.x;
+    const int pos = positions[b];
+    if (pos < 0)
+        return;
+    bool bad = pos >= kv.max_seq_len || (kv.paged && pos / PAGE >= kv.max_pages);
+    long off = 0;
+    if (!bad) {
+        if (kv.paged) {
+            const int pid = kv.page_table[(long)b * kv.max_pages + pos / PAGE];
+            if ((unsigned)pid >= (unsigned)kv.num_pages)
+                bad = true;
+            else
+                off = (((long)pid * s.Hkv + kvh) * PAGE + pos % PAGE) * D;
+        } else {
+            off = (((long)b * s.Hkv + kvh) * kv.max_seq_len + pos) * D;
+        }
+    }
+    if (bad) {
+        if (t == 0 && kvh == 0)
+            atomicAdd(&st.stats[ST_BAD_INPUT], 1ULL);
+        return;
+    }
+    const long src = ((long)b * s.Hkv + kvh) * D;
+    T *k = reinterpret_cast<T *>(kv.k);
+    T *v = reinterpret_cast<T *>(kv.v);
+    if (t < CH)
+        reinterpret_cast<uint4 *>(k + off)[t] = reinterpret_cast<const uint4 *>(kn + src)[t];
+    else if (t < 2 * CH)
+        reinterpret_cast<uint4 *>(v + off)[t - CH] =
+            reinterpret_cast<const uint4 *>(vn + src)[t - CH];
+}
+
+// ================================================================== reset
+__global__ void reset_kernel(int32_t *ring_pos, long n_pos, unsigned long long *stats)
+{
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n_pos)
+        ring_pos[i] = -1;
+    if (i < MAC_NSTAT)
+        stats[i] = 0ULL;
+}
+
+size_t plan_lds_bytes(const Shape &s) { return (size_t)(s.B * s.Hkv + 1) * sizeof(int); }
+
+template <typename T>
+hipError_t launch_complete_t(const Shape &s, const State &st, const KvView &kv, int n_blocks,
+                             hipStream_t stream)
+{
+    const size_t lds = plan_lds_bytes(s);
+    switch (s.G) {
+#define MAC_CASE(GG)                                                                          \
+    case GG:                                                                                  \
+        hipLaunchKernelGGL((complete_kernel<T, GG>), dim3(n_blocks), dim3(BLOCK), lds, stream, \
+                           s, st, kv);                                                        \
+        break;
+        MAC_CASE(1)
+        MAC_CASE(2)
+        MAC_CASE(4)
+        MAC_CASE(8)
+#undef MAC_CASE
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_amend_t(const Shape &s, const State &st, const KvView &kv, int slot_new,
+                          hipStream_t stream)
+{
+    const dim3 grid(s.Hkv, s.B);
+    switch (s.G) {
+#define MAC_CASE(GG)                                                                          \
+    case GG:                                                                                  \
+        hipLaunchKernelGGL((amend_kernel<T, GG>), grid, dim3(BLOCK), 0, stream, s, st, kv,     \
+                           slot_new);                                                         \
+        break;
+        MAC_CASE(1)
+        MAC_CASE(2)
+        MAC_CASE(4)
+        MAC_CASE(8)
+#undef MAC_CASE
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
+
+int match_waves(const Shape &s, size_t max_lds)
+{
+    const size_t per_wave = (size_t)(s.W * (D + 4) + D) * sizeof(float);
+    int n = (int)(max_lds / per_wave);
+    n = n < 1 ? 1 : (n > WAVES ? WAVES : n);
+    return n > s.G ? s.G : n;
+}
+
+hipError_t launch_match(const Shape &s, const State &st, const KvView &kv, const int32_t *seq_lens,
+                        const float *q_pre, const int32_t *override_pos, int waves,
+                        hipStream_t stream)
+{
+    const size_t lds = (size_t)waves * (s.W * (D + 4) + D) * sizeof(float);
+    hipLaunchKernelGGL(match_kernel, dim3(s.Hkv, s.B), dim3(64 * waves), lds, stream, s, st, kv,
+                       seq_lens, q_pre, override_pos);
+    return hipGetLastError();
+}
+
+hipError_t launch_complete(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
+                           int n_blocks, hipStream_t stream)
+{
+    return kv_fp32 ? launch_complete_t<float>(s, st, kv, n_blocks, stream)
+                   : launch_complete_t<uint16_t>(s, st, kv, n_blocks, stream);
+}
+
+hipError_t launch_reduce(const Shape &s, const State &st, float *out, hipStream_t stream)
+{
+    const size_t lds = plan_lds_bytes(s);
+    const dim3 grid(s.Hkv, s.B);
+    switch (s.G) {
+    case 1: hipLaunchKernelGGL(reduce_kernel<1>, grid, dim3(BLOCK), lds, stream, s, st, out); break;
+    case 2: hipLaunchKernelGGL(reduce_kernel<2>, grid, dim3(BLOCK), lds, stream, s, st, out); break;
+    case 4: hipLaunchKernelGGL(reduce_kernel<4>, grid, dim3(BLOCK), lds, stream, s, st, out); break;
+    case 8: hipLaunchKernelGGL(reduce_kernel<8>, grid, dim3(BLOCK), lds, stream, s, st, out); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_amend(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
+                        int slot_new, hipStream_t stream)
+{
+    return kv_fp32 ? launch_amend_t<float>(s, st, kv, slot_new, stream)
+                   : launch_amend_t<uint16_t>(s, st, kv, slot_new, stream);
+}
+
+hipError_t launch_append(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
+                         const void *k_new, const void *v_new, const int32_t *positions,
+                         hipStream_t stream)
+{
+    const dim3 grid(s.Hkv, s.B);
+    if (kv_fp32)
+        hipLaunchKernelGGL(append_kernel<float>, grid, dim3(64), 0, stream, s, st, kv,
+                           (const float *)k_new, (const float *)v_new, positions);
+    else
+        hipLaunchKernelGGL(append_kernel<uint16_t>, grid, dim3(64), 0, stream, s, st, kv,
+                           (const uint16_t *)k_new, (const uint16_t *)v_new, positions);
+    return hipGetLastError();
+}
+
+hipError_t launch_reset(const Shape &s, const State &st, hipStream_t stream)
+{
+    const long n = (long)s.B * s.W;
+    const long tot = n > MAC_NSTAT ? n : MAC_NSTAT;
+    hipLaunchKernelGGL(reset_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream,
+                       st.ring_pos, n, st.stats);
+    return hipGetLastError();
+}
+
+int complete_blocks_per_cu(bool kv_fp32, int G, size_t lds)
+{
+    int n = 0;
+    hipError_t e = hipErrorInvalidValue;
+#define MAC_OCC(TT, GG)                                                                        \
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_kernel<TT, GG>, BLOCK, lds)
+    if (kv_fp32) {
+        if (G == 1) MAC_OCC(float, 1); else if (G == 2) MAC_OCC(float, 2);
+        else if (G == 4) MAC_OCC(float, 4); else MAC_OCC(float, 8);
+    } else {
+        if (G == 1) MAC_OCC(uint16_t, 1); else if (G == 2) MAC_OCC(uint16_t, 2);
+        else if (G == 4) MAC_OCC(uint16_t, 4); else MAC_OCC(uint16_t, 8);
+    }
+#undef MAC_OCC
+    return (e == hipSuccess && n > 0) ? n : 1;
+}
+
+}  // namespace mac

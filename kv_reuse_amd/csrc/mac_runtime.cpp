@@ -1,0 +1,522 @@
+// mac_runtime.cpp -- host side of the C ABI declared in include/mac.h.
+//
+// Owns a layer's device state, the amend stream and the events that order
+// match(m) after amend(m-1) (the pages' "async cache update", MAC-Attention
+// Figure 2 (c)).  No host synchronisation happens inside a decode step: the
+// hit/miss decisions, the work plan and the merge all stay on the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "mac.h"
+#include "mac_internal.h"
+
+struct mac_ctx {
+    mac_config cfg{};
+    mac::Shape shape{};
+    mac::State st{};
+    int device = 0;
+    int n_blocks = 0;
+    int match_waves = 1;
+    bool kv_fp32 = false;
+    hipStream_t main_stream = nullptr;
+    hipStream_t amend_stream = nullptr;
+    bool own_amend = false;
+    hipEvent_t ev_attn = nullptr, ev_amend = nullptr;
+    bool amend_pending = false;
+    hipEvent_t tm[6] = {};
+    bool timed_step = false;
+    long long calls = 0;
+    size_t aux_bytes = 0;
+    void *blocks[16] = {};
+    int n_alloc = 0;
+    std::string err;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+mac_status fail(mac_handle h, mac_status s, const std::string &msg)
+{
+    if (h)
+        h->err = msg;
+    else
+        g_err = msg;
+    return s;
+}
+
+mac_status fail_hip(mac_handle h, const char *what, hipError_t e)
+{
+    return fail(h, MAC_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define MAC_HIP(h, call)                                                                    \
+    do {                                                                                    \
+        hipError_t e_ = (call);                                                             \
+        if (e_ != hipSuccess)                                                               \
+            return fail_hip((h), #call, e_);                                                \
+    } while (0)
+
+struct Sizes {
+    size_t ring_q, ring_s, ring_pos, qvec, m_buf, dec_i, dec_f, grp, partials, as_full, stats,
+        inv_freq;
+    size_t total() const
+    {
+        return ring_q + ring_s + ring_pos + 2 * qvec + m_buf + 3 * dec_i + dec_f + grp +
+               partials + as_full + stats + inv_freq;
+    }
+};
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+Sizes sizes_for(const mac_config &c, int n_workers)
+{
+    const size_t B = c.batch, Hq = c.num_q_heads, Hkv = c.num_kv_heads, W = c.ring_size;
+    const size_t G = Hq / Hkv;
+    Sizes s;
+    s.ring_q = round256(B * Hq * W * mac::D * sizeof(float));
+    s.ring_s = round256(B * Hq * W * mac::SUMM * sizeof(float));
+    s.ring_pos = round256(B * W * sizeof(int32_t));
+    s.qvec = round256(B * Hq * mac::D * sizeof(float));
+    s.m_buf = round256(B * sizeof(int32_t));
+    s.dec_i = round256(B * Hq * sizeof(int32_t));
+    s.dec_f = round256(B * Hq * sizeof(float));
+    s.grp = round256(B * Hkv * sizeof(int32_t));
+    s.partials = round256(((size_t)n_workers + B * Hkv) * G * mac::SUMM * sizeof(float));
+    s.as_full = round256(B * Hq * mac::SUMM * sizeof(float));
+    s.stats = round256(mac::MAC_NSTAT * sizeof(unsigned long long));
+    s.inv_freq = round256(mac::D / 2 * sizeof(double));
+    return s;
+}
+
+mac_status validate(const mac_config *c, std::string &why)
+{
+    if (!c) {
+        why = "cfg is NULL";
+        return MAC_EINVAL;
+    }
+    if (c->batch < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1) {
+        why = "batch, num_q_heads and num_kv_heads must be >= 1";
+        return MAC_EINVAL;
+    }
+    if (c->num_q_heads % c->num_kv_heads != 0) {
+        why = "num_q_heads must be a multiple of num_kv_heads";
+        return MAC_EINVAL;
+    }
+    if (c->head_dim != mac::D) {
+        why = "head_dim must be 128";
+        return c->head_dim > 0 ? MAC_EUNSUPPORTED : MAC_EINVAL;
+    }
+    if (!mac::supported_group(c->num_q_heads / c->num_kv_heads)) {
+        why = "query heads per KV head must be 1, 2, 4 or 8";
+        return MAC_EUNSUPPORTED;
+    }
+    if (c->ring_size < 1 || c->ring_size > mac::MAX_W) {
+        why = "ring_size must be in [1, 64]";
+        return MAC_EINVAL;
+    }
+    if (c->band < 1) {
+        why = "band must be >= 1";
+        return MAC_EINVAL;
+    }
+    if (!std::isfinite(c->tau)) {
+        why = "tau must be finite";
+        return MAC_EINVAL;
+    }
+    if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta)) {
+        why = "rope_theta must be a positive finite number";
+        return MAC_EINVAL;
+    }
+    if (!(c->sm_scale >= 0.f) || !std::isfinite(c->sm_scale)) {
+        why = "sm_scale must be finite and >= 0";
+        return MAC_EINVAL;
+    }
+    if (c->layout != MAC_KV_CONTIGUOUS && c->layout != MAC_KV_PAGED) {
+        why = "unknown layout";
+        return MAC_EINVAL;
+    }
+    if (c->kv_dtype != MAC_BF16 && c->kv_dtype != MAC_FP32) {
+        why = "unknown kv_dtype";
+        return MAC_EINVAL;
+    }
+    if (c->page_size != mac::PAGE) {
+        why = "page_size must be 16";
+        return c->page_size > 0 ? MAC_EUNSUPPORTED : MAC_EINVAL;
+    }
+    if (c->max_seq_len < mac::PAGE || c->max_seq_len % mac::PAGE != 0) {
+        why = "max_seq_len must be a positive multiple of page_size";
+        return MAC_EINVAL;
+    }
+    if ((long long)c->batch * c->num_kv_heads > mac::MAX_GROUPS) {
+        why = "batch * num_kv_heads must be <= 4096";
+        return MAC_EUNSUPPORTED;
+    }
+    const uint32_t known = MAC_F_DISABLE_REUSE | MAC_F_SYNC_AMEND | MAC_F_TIMING |
+                           MAC_F_RECORD_DEBUG;
+    if (c->flags & ~known) {
+        why = "unknown flag bits";
+        return MAC_EINVAL;
+    }
+    return MAC_OK;
+}
+
+mac_status check_view(mac_handle h, const mac_kv_view *kv)
+{
+    if (!kv)
+        return fail(h, MAC_EINVAL, "kv view is NULL");
+    if (!kv->k || !kv->v)
+        return fail(h, MAC_EINVAL, "kv view has a NULL key or value pointer");
+    if (!kv->seq_lens)
+        return fail(h, MAC_EINVAL, "kv view has NULL seq_lens");
+    if (h->cfg.layout == MAC_KV_PAGED &&
+        (!kv->page_table || kv->max_pages_per_req < 1 || kv->num_pages < 1))
+        return fail(h, MAC_EINVAL, "paged kv view needs page_table, max_pages_per_req and num_pages");
+    return MAC_OK;
+}
+
+mac::KvView to_view(const mac_ctx *h, const mac_kv_view *kv)
+{
+    mac::KvView v{};
+    v.k = kv->k;
+    v.v = kv->v;
+    v.paged = h->cfg.layout == MAC_KV_PAGED;
+    v.page_table = v.paged ? kv->page_table : nullptr;
+    v.max_pages = v.paged ? kv->max_pages_per_req : 0;
+    v.num_pages = v.paged ? kv->num_pages : 0;
+    v.max_seq_len = h->cfg.max_seq_len;
+    return v;
+}
+
+void release(mac_ctx *h)
+{
+    if (h->main_stream || h->amend_stream) {
+        if (h->amend_stream)
+            (void)hipStreamSynchronize(h->amend_stream);
+        (void)hipStreamSynchronize(h->main_stream);
+    }
+    for (int i = 0; i < h->n_alloc; ++i)
+        (void)hipFree(h->blocks[i]);
+    h->n_alloc = 0;
+    if (h->ev_attn) (void)hipEventDestroy(h->ev_attn);
+    if (h->ev_amend) (void)hipEventDestroy(h->ev_amend);
+    for (auto &e : h->tm)
+        if (e) (void)hipEventDestroy(e);
+    if (h->own_amend && h->amend_stream)
+        (void)hipStreamDestroy(h->amend_stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mac_status_string(mac_status s)
+{
+    switch (s) {
+    case MAC_OK: return "MAC_OK";
+    case MAC_EINVAL: return "MAC_EINVAL";
+    case MAC_ENOMEM: return "MAC_ENOMEM";
+    case MAC_EHIP: return "MAC_EHIP";
+    case MAC_ESTATE: return "MAC_ESTATE";
+    case MAC_EUNSUPPORTED: return "MAC_EUNSUPPORTED";
+    }
+    return "unknown mac_status";
+}
+
+const char *mac_last_error(mac_handle h) { return h ? h->err.c_str() : g_err.c_str(); }
+
+mac_status mac_config_validate(const mac_config *cfg)
+{
+    std::string why;
+    mac_status s = validate(cfg, why);
+    if (s != MAC_OK)
+        return fail(nullptr, s, why);
+    return MAC_OK;
+}
+
+size_t mac_aux_bytes(const mac_config *cfg, int32_t num_cu)
+{
+    std::string why;
+    if (validate(cfg, why) != MAC_OK || num_cu < 1)
+        return 0;
+    // the complete grid is num_cu * (resident blocks per CU) blocks of 4 waves;
+    // count a generous 8 resident blocks per CU here
+    return sizes_for(*cfg, num_cu * 8 * mac::WAVES).total();
+}
+
+mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream, mac_handle *out)
+{
+    std::string why;
+    if (!out)
+        return fail(nullptr, MAC_EINVAL, "out is NULL");
+    *out = nullptr;
+    mac_status vs = validate(cfg, why);
+    if (vs != MAC_OK)
+        return fail(nullptr, vs, why);
+
+    mac_ctx *h = new (std::nothrow) mac_ctx();
+    if (!h)
+        return fail(nullptr, MAC_ENOMEM, "host allocation failed");
+    h->cfg = *cfg;
+    h->kv_fp32 = cfg->kv_dtype == MAC_FP32;
+    h->main_stream = (hipStream_t)main_stream;
+
+    auto bail = [&](mac_status s, const std::string &msg) {
+        release(h);
+        delete h;
+        return fail(nullptr, s, msg);
+    };
+    hipError_t e = hipGetDevice(&h->device);
+    if (e != hipSuccess)
+        return bail(MAC_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    int n_cu = 0;
+    e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, h->device);
+    if (e != hipSuccess || n_cu < 1)
+        return bail(MAC_EHIP, "cannot query the compute-unit count");
+
+    int max_lds = 0;
+    e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, h->device);
+    if (e != hipSuccess || max_lds < 1)
+        return bail(MAC_EHIP, "cannot query the LDS size per block");
+    const int G = cfg->num_q_heads / cfg->num_kv_heads;
+    const size_t plan_lds = (size_t)(cfg->batch * cfg->num_kv_heads + 1) * sizeof(int);
+    h->n_blocks = n_cu * mac::complete_blocks_per_cu(h->kv_fp32, G, plan_lds);
+    h->st.n_workers = h->n_blocks * mac::WAVES;
+
+    Sizes sz = sizes_for(*cfg, h->st.n_workers);
+    h->aux_bytes = sz.total();
+    auto grab = [&](size_t bytes) -> void * {
+        void *p = nullptr;
+        if (hipMalloc(&p, bytes) != hipSuccess)
+            return nullptr;
+        h->blocks[h->n_alloc++] = p;
+        return p;
+    };
+    void *base = grab(sz.total());
+    if (!base)
+        return bail(MAC_ENOMEM, "device allocation of the handle state failed");
+    char *p = (char *)base;
+    auto take = [&](size_t bytes) {
+        void *r = p;
+        p += bytes;
+        return r;
+    };
+    h->st.ring_q = (float *)take(sz.ring_q);
+    h->st.ring_s = (float *)take(sz.ring_s);
+    h->st.ring_pos = (int32_t *)take(sz.ring_pos);
+    h->st.q_copy = (float *)take(sz.qvec);
+    h->st.q_rot = (float *)take(sz.qvec);
+    h->st.m_buf = (int32_t *)take(sz.m_buf);
+    h->st.dec_slot = (int32_t *)take(sz.dec_i);
+    h->st.dec_p = (int32_t *)take(sz.dec_i);
+    h->st.dec_start = (int32_t *)take(sz.dec_i);
+    h->st.dec_rel = (float *)take(sz.dec_f);
+    h->st.grp_start = (int32_t *)take(sz.grp);
+    h->st.partials = (float *)take(sz.partials);
+    h->st.as_full = (float *)take(sz.as_full);
+    h->st.stats = (unsigned long long *)take(sz.stats);
+    h->st.inv_freq = (const double *)take(sz.inv_freq);
+
+    e = hipMemset(base, 0, sz.total());
+    if (e != hipSuccess)
+        return bail(MAC_EHIP, std::string("hipMemset: ") + hipGetErrorString(e));
+    double inv[mac::D / 2];
+    for (int i = 0; i < mac::D / 2; ++i)
+        inv[i] = std::pow((double)cfg->rope_theta, -2.0 * i / (double)mac::D);
+    e = hipMemcpy((void *)h->st.inv_freq, inv, sizeof inv, hipMemcpyHostToDevice);
+    if (e != hipSuccess)
+        return bail(MAC_EHIP, std::string("hipMemcpy: ") + hipGetErrorString(e));
+
+    h->shape.B = cfg->batch;
+    h->shape.Hq = cfg->num_q_heads;
+    h->shape.Hkv = cfg->num_kv_heads;
+    h->shape.G = G;
+    h->shape.W = cfg->ring_size;
+    h->shape.r = cfg->band;
+    h->shape.tau = cfg->tau;
+    const double scale = cfg->sm_scale > 0.f ? (double)cfg->sm_scale : 1.0 / std::sqrt((double)mac::D);
+    h->shape.scale_log2 = (float)(scale * 1.4426950408889634);
+    h->shape.reuse = !(cfg->flags & MAC_F_DISABLE_REUSE) && cfg->tau >= 0.f;
+    h->match_waves = mac::match_waves(h->shape, (size_t)max_lds);
+
+    if (amend_stream) {
+        h->amend_stream = (hipStream_t)amend_stream;
+    } else {
+        e = hipStreamCreateWithFlags(&h->amend_stream, hipStreamNonBlocking);
+        if (e != hipSuccess)
+            return bail(MAC_EHIP, std::string("hipStreamCreate: ") + hipGetErrorString(e));
+        h->own_amend = true;
+    }
+    if (hipEventCreateWithFlags(&h->ev_attn, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_amend, hipEventDisableTiming) != hipSuccess)
+        return bail(MAC_EHIP, "hipEventCreate failed");
+    for (auto &ev : h->tm)
+        if (hipEventCreate(&ev) != hipSuccess)
+            return bail(MAC_EHIP, "hipEventCreate failed");
+
+    e = mac::launch_reset(h->shape, h->st, h->main_stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(h->main_stream);
+    if (e != hipSuccess)
+        return bail(MAC_EHIP, std::string("ring reset: ") + hipGetErrorString(e));
+    *out = h;
+    return MAC_OK;
+}
+
+mac_status mac_destroy(mac_handle h)
+{
+    if (!h)
+        return fail(nullptr, MAC_EINVAL, "handle is NULL");
+    release(h);
+    delete h;
+    return MAC_OK;
+}
+
+mac_status mac_reset(mac_handle h)
+{
+    if (!h)
+        return fail(nullptr, MAC_EINVAL, "handle is NULL");
+    if (h->amend_pending)
+        MAC_HIP(h, hipStreamWaitEvent(h->main_stream, h->ev_amend, 0));
+    MAC_HIP(h, mac::launch_reset(h->shape, h->st, h->main_stream));
+    h->calls = 0;
+    h->timed_step = false;
+    return MAC_OK;
+}
+
+mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv, const void *k_new, const void *v_new,
+                         const int32_t *positions, void *stream)
+{
+    if (!h)
+        return fail(nullptr, MAC_EINVAL, "handle is NULL");
+    mac_status s = check_view(h, kv);
+    if (s != MAC_OK)
+        return s;
+    if (!k_new || !v_new || !positions)
+        return fail(h, MAC_EINVAL, "k_new, v_new and positions must be non-NULL");
+    hipStream_t st = stream ? (hipStream_t)stream : h->main_stream;
+    MAC_HIP(h, mac::launch_append(h->shape, h->st, to_view(h, kv), h->kv_fp32, k_new, v_new,
+                                  positions, st));
+    return MAC_OK;
+}
+
+mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_pre_rope, float *out,
+                           const int32_t *override_pos, void *stream)
+{
+    if (!h)
+        return fail(nullptr, MAC_EINVAL, "handle is NULL");
+    mac_status s = check_view(h, kv);
+    if (s != MAC_OK)
+        return s;
+    if (!q_pre_rope || !out)
+        return fail(h, MAC_EINVAL, "q_pre_rope and out must be non-NULL");
+    hipStream_t st = stream ? (hipStream_t)stream : h->main_stream;
+    const mac::KvView v = to_view(h, kv);
+    const bool timing = h->cfg.flags & MAC_F_TIMING;
+
+    // match(m) reads the ring amend(m-1) writes
+    if (h->amend_pending)
+        MAC_HIP(h, hipStreamWaitEvent(st, h->ev_amend, 0));
+    if (timing)
+        MAC_HIP(h, hipEventRecord(h->tm[0], st));
+    MAC_HIP(h, mac::launch_match(h->shape, h->st, v, kv->seq_lens, q_pre_rope, override_pos,
+                                 h->match_waves, st));
+    if (timing)
+        MAC_HIP(h, hipEventRecord(h->tm[1], st));
+    MAC_HIP(h, mac::launch_complete(h->shape, h->st, v, h->kv_fp32, h->n_blocks, st));
+    if (timing)
+        MAC_HIP(h, hipEventRecord(h->tm[2], st));
+    MAC_HIP(h, mac::launch_reduce(h->shape, h->st, out, st));
+    if (timing)
+        MAC_HIP(h, hipEventRecord(h->tm[3], st));
+
+    if (h->shape.reuse) {
+        const int slot_new = (int)(h->calls % h->cfg.ring_size);
+        hipStream_t as = (h->cfg.flags & MAC_F_SYNC_AMEND) ? st : h->amend_stream;
+        if (as != st) {
+            MAC_HIP(h, hipEventRecord(h->ev_attn, st));
+            MAC_HIP(h, hipStreamWaitEvent(as, h->ev_attn, 0));
+        }
+        if (timing)
+            MAC_HIP(h, hipEventRecord(h->tm[4], as));
+        MAC_HIP(h, mac::launch_amend(h->shape, h->st, v, h->kv_fp32, slot_new, as));
+        if (timing)
+            MAC_HIP(h, hipEventRecord(h->tm[5], as));
+        MAC_HIP(h, hipEventRecord(h->ev_amend, as));
+        h->amend_pending = true;
+    }
+    h->timed_step = timing;
+    h->calls += 1;
+    return MAC_OK;
+}
+
+mac_status mac_stats(mac_handle h, mac_stats_t *out)
+{
+    if (!h || !out)
+        return fail(h, MAC_EINVAL, "handle and out must be non-NULL");
+    MAC_HIP(h, hipStreamSynchronize(h->main_stream));
+    if (h->amend_stream)
+        MAC_HIP(h, hipStreamSynchronize(h->amend_stream));
+    MAC_HIP(h, hipDeviceSynchronize());
+    unsigned long long c[mac::MAC_NSTAT];
+    MAC_HIP(h, hipMemcpy(c, h->st.stats, sizeof c, hipMemcpyDeviceToHost));
+    std::memset(out, 0, sizeof *out);
+    const uint64_t row = 2ull * mac::D * (h->kv_fp32 ? 4 : 2);   // one key row + one value row
+    out->steps = (uint64_t)h->calls;
+    out->decisions = c[mac::ST_DECISIONS];
+    out->hits = c[mac::ST_HITS];
+    out->misses = c[mac::ST_MISSES];
+    out->near_tau = c[mac::ST_NEAR_TAU];
+    out->override_invalid = c[mac::ST_OVR_INVALID];
+    out->kv_tokens_critical = c[mac::ST_TOK_CRIT];
+    out->kv_tokens_amend = c[mac::ST_TOK_AMEND];
+    out->kv_bytes_critical = c[mac::ST_TOK_CRIT] * row;
+    out->kv_bytes_amend = c[mac::ST_TOK_AMEND] * row;
+    out->aux_bytes = h->aux_bytes;
+    out->bad_input = c[mac::ST_BAD_INPUT];
+    if (h->timed_step) {
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, h->tm[0], h->tm[1]) == hipSuccess) out->last_us_match = t * 1e3f;
+        if (hipEventElapsedTime(&t, h->tm[1], h->tm[2]) == hipSuccess) out->last_us_complete = t * 1e3f;
+        if (hipEventElapsedTime(&t, h->tm[2], h->tm[3]) == hipSuccess) out->last_us_reduce = t * 1e3f;
+        if (hipEventElapsedTime(&t, h->tm[0], h->tm[3]) == hipSuccess) out->last_us_attention = t * 1e3f;
+        if (h->shape.reuse && hipEventElapsedTime(&t, h->tm[4], h->tm[5]) == hipSuccess)
+            out->last_us_amend = t * 1e3f;
+    }
+    return MAC_OK;
+}
+
+mac_status mac_debug_last(mac_handle h, int32_t *p, uint8_t *hit, float *rel)
+{
+    if (!h)
+        return fail(nullptr, MAC_EINVAL, "handle is NULL");
+    if (!(h->cfg.flags & MAC_F_RECORD_DEBUG))
+        return fail(h, MAC_ESTATE, "mac_debug_last needs MAC_F_RECORD_DEBUG");
+    MAC_HIP(h, hipStreamSynchronize(h->main_stream));
+    MAC_HIP(h, hipDeviceSynchronize());
+    const size_t n = (size_t)h->cfg.batch * h->cfg.num_q_heads;
+    if (p)
+        MAC_HIP(h, hipMemcpy(p, h->st.dec_p, n * sizeof(int32_t), hipMemcpyDeviceToHost));
+    if (hit) {
+        int32_t *tmp = new (std::nothrow) int32_t[n];
+        if (!tmp)
+            return fail(h, MAC_ENOMEM, "host allocation failed");
+        hipError_t e = hipMemcpy(tmp, h->st.dec_slot, n * sizeof(int32_t), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) {
+            delete[] tmp;
+            return fail_hip(h, "hipMemcpy", e);
+        }
+        for (size_t i = 0; i < n; ++i)
+            hit[i] = tmp[i] >= 0;
+        delete[] tmp;
+    }
+    if (rel)
+        MAC_HIP(h, hipMemcpy(rel, h->st.dec_rel, n * sizeof(float), hipMemcpyDeviceToHost));
+    return MAC_OK;
+}
+
+}  // extern "C"

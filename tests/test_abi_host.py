@@ -1,0 +1,109 @@
+"""Host-side checks of the C-ABI library: it loads, exports every entry point the
+header declares, and validates configurations without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_reuse_amd as mac
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "mac.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mac_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mac.load()
+    names = _declared()
+    assert set(names) == set(mac.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def _cfg(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, ring_size=16, band=64, tau=0.3,
+                max_seq_len=4096)
+    base.update(kw)
+    return mac.make_config(**base)
+
+
+def test_valid_config_passes():
+    mac.mac_config_validate(_cfg())
+    mac.mac_config_validate(_cfg(layout=mac.MAC_KV_PAGED, kv_dtype=mac.MAC_FP32, ring_size=64,
+                                 num_q_heads=32, num_kv_heads=4, tau=-1.0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), mac.MAC_EINVAL),
+    (dict(num_q_heads=6, num_kv_heads=4), mac.MAC_EINVAL),
+    (dict(head_dim=64), mac.MAC_EUNSUPPORTED),
+    (dict(head_dim=0), mac.MAC_EINVAL),
+    (dict(num_q_heads=32, num_kv_heads=2), mac.MAC_EUNSUPPORTED),   # 16 q heads per KV head
+    (dict(ring_size=0), mac.MAC_EINVAL),
+    (dict(ring_size=65), mac.MAC_EINVAL),
+    (dict(band=0), mac.MAC_EINVAL),
+    (dict(tau=float("nan")), mac.MAC_EINVAL),
+    (dict(rope_theta=0.0), mac.MAC_EINVAL),
+    (dict(sm_scale=-1.0), mac.MAC_EINVAL),
+    (dict(layout=7), mac.MAC_EINVAL),
+    (dict(kv_dtype=3), mac.MAC_EINVAL),
+    (dict(page_size=32), mac.MAC_EUNSUPPORTED),
+    (dict(max_seq_len=100), mac.MAC_EINVAL),
+    (dict(batch=1024, num_q_heads=8, num_kv_heads=8), mac.MAC_EUNSUPPORTED),
+    (dict(flags=1 << 9), mac.MAC_EINVAL),
+])
+def test_invalid_configs_rejected(kw, status):
+    with pytest.raises(mac.MacError) as ei:
+        mac.mac_config_validate(_cfg(**kw))
+    assert ei.value.status == status
+    assert mac.mac_last_error()
+
+
+def test_status_strings():
+    assert mac.mac_status_string(mac.MAC_OK) == "MAC_OK"
+    assert mac.mac_status_string(mac.MAC_EHIP) == "MAC_EHIP"
+
+
+def _table7():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "table7_aux_overhead.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, pct = line.split()
+            rows.append((int(k), float(pct)))
+    return rows
+
+
+def test_aux_memory_is_linear_in_window_like_table7():
+    """Table 7 of the pages: aux HBM overhead doubles with the search window.
+    Our ring memory (the part that depends on W) must scale the same way."""
+    rows = _table7()
+    ks = [k for k, _ in rows]
+    pcts = [p for _, p in rows]
+    for (k0, p0), (k1, p1) in zip(rows, rows[1:]):
+        assert k1 == 2 * k0
+        assert abs(p1 / p0 - 2.0) < 0.1       # printed to one decimal
+    base = mac.mac_aux_bytes(_cfg(ring_size=1), 256)
+    per_slot = mac.mac_aux_bytes(_cfg(ring_size=2), 256) - base
+    assert per_slot > 0
+    for w in (4, 8, 16, 32, 64):
+        assert mac.mac_aux_bytes(_cfg(ring_size=w), 256) == pytest.approx(base + (w - 1) * per_slot,
+                                                                           rel=1e-3)
+    assert ks == [256, 512, 1024, 2048] and pcts[0] == 1.2
+
+
+def test_aux_bytes_rejects_bad_config():
+    assert mac.mac_aux_bytes(_cfg(batch=0), 256) == 0
+
+
+def test_init_rejects_bad_config_before_any_device_work():
+    with pytest.raises(mac.MacError) as ei:
+        mac.mac_init(_cfg(band=0))
+    assert ei.value.status == mac.MAC_EINVAL

@@ -1,0 +1,81 @@
+"""GPU parity: the HIP decode path through the C ABI against the fp64 oracle.
+
+Decisions (hit/miss and matched position) bit-exact; outputs within max-abs
+2e-3 and per-row relative 1e-2 (bf16 or fp32 KV, fp32 accumulation).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from workloads import get_config, scaled
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, steps, **kw):
+    from gpu_harness import Lockstep
+    print("case", w.name, "B", w.B, "Hq", w.Hq, "Hkv", w.Hkv, "C", w.C, "steps", steps,
+          w.kv, w.layout, kw, flush=True)
+    ls = Lockstep(w, **kw)
+    hits = forced = 0
+    try:
+        for t in range(steps):
+            info = ls.step(t)
+            hits += info["hits"]
+            forced += info["forced"]
+    finally:
+        ls.close()
+    emax = max(e for e, _ in ls.stats)
+    rmax = max(r for _, r in ls.stats)
+    print("  hits", hits, "of", steps * w.B * w.Hq, "forced", forced,
+          "max-abs %.2e row-rel %.2e" % (emax, rmax), flush=True)
+    return hits, ls
+
+
+def test_cpu_sized_workload_all_steps(gpu_lib):
+    """1 request, 8q/2kv, fp32 KV, 4096 + 256 steps, rho 0.95, ring 16, r 64."""
+    w = get_config("cpu4k")
+    hits, _ = _run(w, w.steps)
+    assert 0 < hits < w.steps * w.B * w.Hq
+
+
+def test_llama_shape_32k_contiguous_bf16(gpu_lib):
+    w = get_config("llama32k")
+    hits, _ = _run(w, 96)
+    assert hits > 0.5 * 95 * w.Hq
+
+
+@pytest.mark.parametrize("C", [3000, 4096])
+def test_paged_batch_mixed_rho(gpu_lib, C):
+    """The 128K batch workload's recipe at a small context: paged (permuted
+    table), per-request rho in [0.8, 0.99], a ragged prefill length."""
+    w = scaled(get_config("b16_128k"), B=4, C=C, steps=48)
+    _run(w, w.steps)
+
+
+@pytest.mark.parametrize("r", [64, 256, 1024])
+def test_moe_heads_per_head_rho(gpu_lib, r):
+    """32q/4kv (8 query heads per KV head), per-head rho 0.5..0.99, r swept."""
+    w = scaled(get_config("moe_122k"), B=2, C=2500, steps=40)
+    _run(w, w.steps, r=r)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (8, 1)])
+def test_group_sizes(gpu_lib, Hq, Hkv):
+    w = scaled(get_config("b16_128k"), B=2, Hq=Hq, Hkv=Hkv, C=1000, steps=24,
+               rho=("const", 0.96))
+    _run(w, w.steps)
+
+
+def test_small_window_and_band(gpu_lib):
+    w = scaled(get_config("cpu4k"), C=300, steps=40, W=1, r=1, kv="bf16")
+    _run(w, w.steps)
+
+
+def test_disable_reuse_is_full_attention(gpu_lib):
+    import kv_reuse_amd as mac
+    import oracle
+    w = scaled(get_config("b16_128k"), B=2, C=2000, steps=12)
+    hits, _ = _run(w, w.steps, flags=mac.MAC_F_DISABLE_REUSE, oracle_flags=oracle.F_DISABLE_REUSE)
+    assert hits == 0

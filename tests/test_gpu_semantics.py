@@ -1,0 +1,206 @@
+"""GPU checks of the decode step's semantics through the C ABI.
+
+- async amend on its own stream and amend on the decode stream give bit-identical
+  outputs over many steps (amend(m-1) -> match(m) ordering; MAC-Attention
+  Figure 2 (c), "async cache update");
+- a paged cache with a permuted table gives the same bits as a contiguous one;
+- a forced hit at the query's own position after a miss reproduces full
+  attention; an override naming no stored position is a counted miss;
+- mac_reset empties the rings; idle requests produce zeros and store nothing;
+- sequence lengths and page ids out of range are caught on the device;
+- the counters agree with the oracle's decisions and key counts.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_reuse_amd as mac
+import oracle
+from workloads import get_config, kv_logical, page_table, queries, scaled, to_paged
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(**kw):
+    base = dict(B=3, C=900, steps=40, rho=("const", 0.965))
+    base.update(kw)
+    return scaled(get_config("b16_128k"), **base)
+
+
+class Plain:
+    """The library alone (no oracle): for GPU-vs-GPU bit comparisons."""
+
+    def __init__(self, w, paged, flags=0, K=None, V=None):
+        self.w = w
+        dev = "cuda"
+        if K is None:
+            K, V = kv_logical(w, dev)
+        self.K, self.V = K, V
+        if paged:
+            tab = page_table(w)
+            self.kc, self.vc = to_paged(K, tab), to_paged(V, tab)
+            self.tab = torch.as_tensor(tab, device=dev)
+        else:
+            self.kc, self.vc, self.tab = K.clone(), V.clone(), None
+        self.seq = torch.zeros(w.B, dtype=torch.int32, device=dev)
+        self.cfg = mac.make_config(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, ring_size=w.W,
+                                   band=w.r, tau=w.tau, rope_theta=w.theta,
+                                   layout=mac.MAC_KV_PAGED if paged else mac.MAC_KV_CONTIGUOUS,
+                                   kv_dtype=mac.MAC_BF16, max_seq_len=w.n_cap,
+                                   flags=flags | mac.MAC_F_RECORD_DEBUG)
+        self.layer = mac.MacLayer(self.cfg)
+        self.view = mac.make_kv_view(self.kc, self.vc, self.seq, self.tab,
+                                     num_pages=self.kc.shape[0] if paged else 0)
+        self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+
+    def step(self, seq_h, q, override=None):
+        self.seq.copy_(torch.as_tensor(np.asarray(seq_h, np.int32)))
+        ov = None if override is None else torch.as_tensor(override, device="cuda")
+        self.layer.decode_step(self.view, torch.as_tensor(q, device="cuda"), self.out, ov)
+        return self.out.clone()
+
+
+def test_async_amend_bit_identical_to_sync():
+    w = _case(steps=160, W=8, r=64)
+    a = Plain(w, paged=True)
+    s = Plain(w, paged=True, flags=mac.MAC_F_SYNC_AMEND, K=a.K, V=a.V)
+    qs = queries(w)
+    for t in range(w.steps):
+        seq = np.full(w.B, w.C + t + 1)
+        oa = a.step(seq, qs[t])
+        os_ = s.step(seq, qs[t])
+        assert torch.equal(oa, os_), t
+    ha = a.layer.stats()["hits"]
+    assert ha == s.layer.stats()["hits"] and ha > 0
+
+
+def test_paged_bit_identical_to_contiguous():
+    w = _case(steps=24)
+    pg = Plain(w, paged=True)
+    ct = Plain(w, paged=False, K=pg.K, V=pg.V)
+    qs = queries(w)
+    for t in range(w.steps):
+        seq = np.full(w.B, w.C + t + 1)
+        assert torch.equal(pg.step(seq, qs[t]), ct.step(seq, qs[t])), t
+
+
+def test_forced_redecode_at_own_position_is_full_attention():
+    from gpu_harness import Lockstep
+    w = _case(steps=6)
+    ls = Lockstep(w)
+    try:
+        for t in range(4):
+            ls.step(t)
+        miss = np.full((w.B, w.Hq), -1, np.int32)
+        first = ls.step(4, override=miss)
+        # re-decode the same position, forced onto the entry stored just now
+        own = np.full((w.B, w.Hq), w.C + 4, np.int32)
+        again = ls.step(4, override=own)
+        assert again["hit_gpu"].all()
+        np.testing.assert_allclose(again["out_gpu"], first["out_gpu"], atol=2e-6, rtol=0)
+    finally:
+        ls.close()
+
+
+def test_override_to_absent_position_is_counted_miss():
+    from gpu_harness import Lockstep
+    w = _case(steps=5)
+    ls = Lockstep(w)
+    try:
+        for t in range(4):
+            ls.step(t)
+        before = ls.layer.stats()["override_invalid"]
+        ov = np.full((w.B, w.Hq), -2, np.int32)
+        ov[0, 3] = 5          # nothing stored at position 5
+        info = ls.step(4, override=ov)
+        assert info["hit_gpu"][0, 3] == 0
+        assert info["res"]["override_invalid"] == 1
+        assert ls.layer.stats()["override_invalid"] == before + 1
+    finally:
+        ls.close()
+
+
+def test_reset_then_all_misses_equal_full_attention():
+    from gpu_harness import Lockstep
+    w = _case(steps=12)
+    ls = Lockstep(w)
+    try:
+        for t in range(6):
+            ls.step(t)
+        ls.layer.reset()
+        ls.orc.reset()
+        info = ls.step(6)
+        assert not info["hit_gpu"].any()
+        for t in range(7, 12):
+            ls.step(t)
+    finally:
+        ls.close()
+
+
+def test_idle_request_outputs_zero_and_stores_nothing():
+    from gpu_harness import Lockstep
+    w = _case(steps=10)
+    ls = Lockstep(w)
+    try:
+        for t in range(10):
+            seq = np.full(w.B, w.C + t + 1, np.int32)
+            if t % 3 == 1:
+                seq[1] = 0                  # request 1 idle this step
+            info = ls.step(t, seq_lens=seq)
+            if t % 3 == 1:
+                assert not info["out_gpu"][1].any()
+    finally:
+        ls.close()
+
+
+def test_stats_match_oracle_counts():
+    from gpu_harness import Lockstep
+    w = _case(steps=20)
+    ls = Lockstep(w)
+    try:
+        hits = toks = 0
+        for t in range(20):
+            info = ls.step(t)
+            hits += int(info["res"]["hit"].sum())
+            toks += int(info["res"]["kv_tokens"].sum())
+        st = ls.layer.stats()
+        assert st["steps"] == 20 and st["decisions"] == 20 * w.B * w.Hq
+        assert st["hits"] == hits and st["misses"] == 20 * w.B * w.Hq - hits
+        assert st["kv_tokens_critical"] == toks
+        assert st["kv_bytes_critical"] == toks * 2 * w.d * 2
+        assert st["bad_input"] == 0 and st["aux_bytes"] > 0
+    finally:
+        ls.close()
+
+
+def test_device_bounds_checks_idle_bad_requests():
+    """seq_len past the cache capacity, and a page id outside the pool, are
+    caught by the kernels' own checks: counted, never dereferenced."""
+    w = _case(B=2, steps=2)
+    pl = Plain(w, paged=True)
+    qs = queries(w)
+    out = pl.step(np.full(w.B, w.C + 1), qs[0])
+    before = pl.layer.stats()["bad_input"]
+    out = pl.step(np.array([w.n_cap + 5, w.C + 2]), qs[1])     # request 0 beyond capacity
+    torch.cuda.synchronize()
+    assert not out[0].any() and out[1].abs().sum() > 0
+    assert pl.layer.stats()["bad_input"] == before + 1
+    tab = pl.tab.clone()
+    m = w.C + 2
+    pl.tab[1, m // 16] = 1 << 28          # page holding the query position: always read
+    out = pl.step(np.array([m + 1, m + 1]), qs[1])
+    torch.cuda.synchronize()
+    assert pl.layer.stats()["bad_input"] > before + 1
+    assert torch.isfinite(out).all()
+    pl.tab.copy_(tab)
+
+
+def test_timing_flag_reports_kernel_times():
+    w = _case(B=2, steps=3)
+    pl = Plain(w, paged=True, flags=mac.MAC_F_TIMING)
+    qs = queries(w)
+    for t in range(3):
+        pl.step(np.full(w.B, w.C + t + 1), qs[t])
+    st = pl.layer.stats()
+    assert st["last_us_attention"] > 0 and st["last_us_complete"] > 0
+    assert st["last_us_amend"] > 0
