@@ -29,6 +29,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "complete_kernel_b16_128k_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "kv_reuse_amd", "csrc", "mac_kernels.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per complete launch from the committed rocprofv3 counter
+    summary, valid only while the kernel source is the one it was taken on."""
+    import hashlib
+    if workload != "b16_128k" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    return rec["traffic_bytes_per_launch"] if rec.get("kernel_sha16") == sha else None
 
 
 def parse():
@@ -229,7 +242,7 @@ def main():
         "kernel_us": {"match": float(np.mean(match)), "complete": comp_us,
                       "reduce": float(np.mean(red)), "amend": float(np.mean(amend))},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(w.name),
                      "kernel": "complete_kernel", "bytes_per_launch": float(np.mean(comp_bytes))},
         "attention_phase_bytes_per_step": att_bytes,
         "full_attention_kernel": base,

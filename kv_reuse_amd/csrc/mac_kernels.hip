@@ -19,6 +19,7 @@
 
 #include <climits>
 #include <cmath>
+#include <type_traits>
 
 #include "mac_internal.h"
 
@@ -669,6 +670,268 @@ __global__ __launch_bounds__(BLOCK) void complete_kernel(Shape s, State st, KvVi
     }
 }
 
+// ========================================================== complete (MFMA)
+// bf16 cache, G <= 4 query heads per KV head.  Q.K^T runs on the matrix cores:
+// v_mfma_f32_16x16x32_bf16 with the page's 16 tokens as the 16 columns of B
+// (lane l feeds token l%16, columns 32s + 8(l/16) .. +7 at k-step s, straight
+// from its 16-byte K load) and the group's queries as the rows of A,
+// replicated so that row i holds head i % G: every lane receives the logits of
+// all G heads for token l%16.  A carries the query split into two bf16 parts
+// (hi + lo), so the logits keep ~16 mantissa bits of the fp32 query.
+// P.V stays on the vector units with V loaded as contiguous 1 KB wave loads
+// (lane (r, c) = (l/16, l%16) holds token 4s + r, columns 8c .. 8c+7); each
+// token's probabilities reach the lanes that hold its V row through a
+// 256-byte per-wave LDS exchange.  The softmax reference max is uniform over
+// the wave (one per head) and only moves when a logit exceeds it by more than
+// LAZY_RESCALE (log2 units): exp2(s - M) <= 256 is accumulated as is, and the
+// rescale, when it happens, is exact.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr float LAZY_RESCALE = 8.f;
+
+struct MPage {
+    uint4 k[4], v[4];
+};
+
+__device__ __forceinline__ void load_mpage(MPage &r, const uint16_t *kp, const uint16_t *vp)
+{
+    const int lane = lane_id(), t = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        r.k[s] = *reinterpret_cast<const uint4 *>(kp + t * D + 32 * s + 8 * q);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        r.v[s] = *reinterpret_cast<const uint4 *>(vp + (4 * s + q) * D + 8 * t);
+}
+
+template <int G>
+struct MAcc {
+    float M[G], L[G], acc[G][8];
+};
+
+// qa: this wave's A operands in LDS, [8][64] (register i of lane l at qa[i*64 + l]).
+template <int G>
+__device__ __forceinline__ void compute_mpage(const MPage &r, const uint4 *qa, float4 *px,
+                                              int tok0, int m, const int (&hs)[G], bool masked,
+                                              MAcc<G> &st)
+{
+    const int lane = lane_id(), t = lane & 15, q = lane >> 4;
+    floatx4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const bf16x8 kb = __builtin_bit_cast(bf16x8, r.k[s]);
+        const uint4 ahi = qa[(2 * s) * 64 + lane], alo = qa[(2 * s + 1) * 64 + lane];
+        S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ahi), kb, S0, 0,
+                                                     0, 0);
+        S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, alo), kb, S1, 0,
+                                                     0, 0);
+    }
+    float lg[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        lg[g] = S0[g] + S1[g];
+    if (masked) {
+        const int tok = tok0 + t;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            if (tok < hs[g] || tok > m)
+                lg[g] = NEG_INF;
+    }
+    bool need = false;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        need |= lg[g] > st.M[g] + LAZY_RESCALE;
+    if (__any(need)) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float mn = fmaxf(st.M[g], wave_max(lg[g]));
+            const float alpha = mn == st.M[g] ? 1.f : exp2f(st.M[g] - mn);   // 0 from -inf
+            st.M[g] = mn;
+            st.L[g] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                st.acc[g][e] *= alpha;
+        }
+    }
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        p[g] = lg[g] == NEG_INF ? 0.f : exp2f(lg[g] - st.M[g]);
+        st.L[g] += p[g];
+    }
+    // token t's probabilities -> the lanes holding V rows of token t
+    if (q == 0)
+        px[t] = make_float4(p[0], p[1], p[2], p[3]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float4 pt[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        pt[s] = px[4 * s + q];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        float vf[8];
+        to_f32(r.v[s], vf);
+        if (masked && tok0 + 4 * s + q > m) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                vf[e] = 0.f;
+        }
+        const float pp[4] = {pt[s].x, pt[s].y, pt[s].z, pt[s].w};
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                st.acc[g][e] = fmaf(pp[g], vf[e], st.acc[g][e]);
+    }
+}
+
+// Sum over the four row groups (tokens 4s + r) and, for L, over the 16 token
+// lanes; the first row stores columns 8c .. 8c+7.
+template <int G>
+__device__ __forceinline__ void store_msummary(MAcc<G> &st, float *dst)
+{
+    const int lane = lane_id(), t = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float a[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a[e] = st.acc[g][e];
+            a[e] += xor_lanes<16>(a[e]);
+            a[e] += xor_lanes<32>(a[e]);
+        }
+        const float Lt = row16_sum(st.L[g]);
+        if (q == 0) {
+            float *o = dst + g * SUMM + 8 * t;
+            *reinterpret_cast<float4 *>(o) = make_float4(a[0], a[1], a[2], a[3]);
+            *reinterpret_cast<float4 *>(o + 4) = make_float4(a[4], a[5], a[6], a[7]);
+        }
+        if (lane == 0) {
+            dst[g * SUMM + D] = st.M[g];
+            dst[g * SUMM + D + 1] = Lt;
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// A operands of this lane (row l%16 -> head (l%16) % G, k-group l/16) for the
+// 4 k-steps, hi and lo parts interleaved: qa[2s] = hi, qa[2s+1] = lo.  hi
+// keeps the top 16 bits of the scaled fp32 query; lo = bf16(q - hi), where
+// q - hi is exact in fp32.
+template <int G>
+__device__ __forceinline__ void build_qa(const Shape &s, const State &st, int b, int kvh,
+                                         uint4 *qa)
+{
+    const int lane = lane_id(), row = lane & 15, q = lane >> 4;
+    const float *src = st.q_rot + ((long)b * s.Hq + kvh * G + row % G) * D;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = src[32 * k + 8 * q + e] * s.scale_log2;
+            hi[e] = __float_as_uint(x) >> 16;
+            lo[e] = bf16_rne_bits(x - __uint_as_float(hi[e] << 16));
+        }
+        qa[2 * k] = make_uint4(hi[0] | hi[1] << 16, hi[2] | hi[3] << 16, hi[4] | hi[5] << 16,
+                               hi[6] | hi[7] << 16);
+        qa[2 * k + 1] = make_uint4(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16,
+                                   lo[6] | lo[7] << 16);
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(BLOCK) void complete_mfma_kernel(Shape s, State st, KvView kv)
+{
+    extern __shared__ int s_off[];
+    __shared__ uint4 qlds[WAVES][8][64];   // per wave: 8 A-operand registers x 64 lanes
+    __shared__ float4 plds[WAVES][16];     // per wave: probabilities of the page's 16 tokens
+    const int nG = s.B * s.Hkv;
+    build_plan(s, st, s_off);
+    const int P = s_off[nG];
+    if (P == 0)
+        return;
+    const int nW = active_workers(st.n_workers, P);
+    const int wv = threadIdx.x >> 6, lane = lane_id();
+    const int w = blockIdx.x * WAVES + wv;
+    if (w >= nW)
+        return;
+    long x = (long)w * P / nW;
+    const long x1 = (long)(w + 1) * P / nW;
+    int g = find_group(s_off, nG, x);
+    unsigned long long *bad = &st.stats[ST_BAD_INPUT];
+    const uint16_t *kb = reinterpret_cast<const uint16_t *>(kv.k);
+    const uint16_t *vb = reinterpret_cast<const uint16_t *>(kv.v);
+    while (x < x1) {
+        while (s_off[g + 1] <= x)
+            ++g;
+        const long gend = min((long)s_off[g + 1], x1);
+        const int b = g / s.Hkv, kvh = g % s.Hkv;
+        const int m = st.m_buf[b];
+        const int first_page = st.grp_start[g] / PAGE;
+        int hs[G];
+        int hmax = 0;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            hs[h] = st.dec_start[(long)b * s.Hq + kvh * G + h];
+            hmax = max(hmax, hs[h]);
+        }
+        {
+            uint4 qa[8];
+            build_qa<G>(s, st, b, kvh, qa);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                qlds[wv][i][lane] = qa[i];
+        }
+        MAcc<G> acc;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            acc.M[h] = NEG_INF;
+            acc.L[h] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc.acc[h][e] = 0.f;
+        }
+        int page = first_page + (int)(x - s_off[g]);
+        const int last = first_page + (int)(gend - s_off[g]) - 1;
+        MPage r0, r1;
+        load_mpage(r0, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad),
+                   kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page, bad));
+        while (true) {
+            if (page + 1 <= last)
+                load_mpage(r1, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page + 1, bad),
+                           kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page + 1, bad));
+            {
+                const int tok0 = page * PAGE;
+                compute_mpage<G>(r0, &qlds[wv][0][0], plds[wv], tok0, m, hs,
+                                 tok0 < hmax || tok0 + PAGE - 1 > m, acc);
+            }
+            if (++page > last)
+                break;
+            if (page + 1 <= last)
+                load_mpage(r0, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page + 1, bad),
+                           kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page + 1, bad));
+            {
+                const int tok0 = page * PAGE;
+                compute_mpage<G>(r1, &qlds[wv][0][0], plds[wv], tok0, m, hs,
+                                 tok0 < hmax || tok0 + PAGE - 1 > m, acc);
+            }
+            if (++page > last)
+                break;
+        }
+        store_msummary<G>(acc, st.partials + ((long)w + g) * G * SUMM);
+        x = gend;
+    }
+}
+
 // ================================================================= reduce
 // Grid (Hkv, B): combine a group's partial summaries per head, then merge
 // (+) with the matched entry's stored AS_{1:p-r}.  Writes out (normalised)
@@ -874,6 +1137,17 @@ hipError_t launch_complete_t(const Shape &s, const State &st, const KvView &kv, 
                              hipStream_t stream)
 {
     const size_t lds = plan_lds_bytes(s);
+    if (std::is_same<T, uint16_t>::value && s.G <= 4) {
+        switch (s.G) {
+        case 1: hipLaunchKernelGGL(complete_mfma_kernel<1>, dim3(n_blocks), dim3(BLOCK), lds,
+                                   stream, s, st, kv); break;
+        case 2: hipLaunchKernelGGL(complete_mfma_kernel<2>, dim3(n_blocks), dim3(BLOCK), lds,
+                                   stream, s, st, kv); break;
+        default: hipLaunchKernelGGL(complete_mfma_kernel<4>, dim3(n_blocks), dim3(BLOCK), lds,
+                                    stream, s, st, kv); break;
+        }
+        return hipGetLastError();
+    }
     switch (s.G) {
 #define MAC_CASE(GG)                                                                          \
     case GG:                                                                                  \
@@ -995,6 +1269,13 @@ int complete_blocks_per_cu(bool kv_fp32, int G, size_t lds)
     if (kv_fp32) {
         if (G == 1) MAC_OCC(float, 1); else if (G == 2) MAC_OCC(float, 2);
         else if (G == 4) MAC_OCC(float, 4); else MAC_OCC(float, 8);
+    } else if (G <= 4) {
+        if (G == 1)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_mfma_kernel<1>, BLOCK, lds);
+        else if (G == 2)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_mfma_kernel<2>, BLOCK, lds);
+        else
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_mfma_kernel<4>, BLOCK, lds);
     } else {
         if (G == 1) MAC_OCC(uint16_t, 1); else if (G == 2) MAC_OCC(uint16_t, 2);
         else if (G == 4) MAC_OCC(uint16_t, 4); else MAC_OCC(uint16_t, 8);
