@@ -112,7 +112,7 @@ typedef struct {
     uint64_t bad_input;          /* device-side index checks that idled a request or row */
     float last_us_match;         /* MAC_F_TIMING: last step, microseconds */
     float last_us_complete;
-    float last_us_reduce;
+    float last_us_reduce;        /* combine of the partial summaries + merge with the stored one */
     float last_us_amend;
     float last_us_attention;     /* match + complete + reduce, one event pair */
 } mac_stats_t;

@@ -15,7 +15,7 @@
 //   grp_start  [B][Hkv] int32       first key of the group's union span (-1 idle)
 //   partials   [NW + B*Hkv][G][SUMM] per-(worker, group) unnormalised summaries
 //   as_full    [B][Hq][SUMM]        AS_{1:m} of this step, input of amend
-//   stats      [MAC_NSTAT] uint64
+//   stats      [MAC_NSTAT + B*Hkv*GRP_NSTAT] uint64
 // M values inside the library are in log2 units of the scaled logit
 // (s * log2 e); every summary the library stores uses the same units.
 #pragma once
@@ -33,10 +33,16 @@ constexpr int MAX_W = 64;       // ring slots per (request, head)
 constexpr int MAX_GROUPS = 4096;  // B * Hkv
 constexpr int MIN_PAGES_PER_WORKER = 2;
 
+// Counters: stats[0 .. MAC_NSTAT) are device-wide (only ST_BAD_INPUT is used
+// there, by atomics on error paths); each GQA group g then owns
+// stats[MAC_NSTAT + g*GRP_NSTAT ..], updated without atomics by the one match
+// block that handles g in a step.  The host sums the groups.
 enum Stat {
     ST_DECISIONS = 0, ST_HITS, ST_MISSES, ST_NEAR_TAU, ST_OVR_INVALID, ST_TOK_CRIT, ST_TOK_AMEND,
     ST_BAD_INPUT, MAC_NSTAT = 16
 };
+constexpr int GRP_NSTAT = 8;
+inline long stats_count(long n_groups) { return MAC_NSTAT + n_groups * GRP_NSTAT; }
 
 struct KvView {
     void *k;
@@ -64,7 +70,7 @@ struct State {
 
 // Launchers (enqueue only; return the launch status).
 hipError_t launch_match(const Shape &s, const State &st, const KvView &kv, const int32_t *seq_lens,
-                        const float *q_pre, const int32_t *override_pos, int waves,
+                        const float *q_pre, const int32_t *override_pos, float *out, int waves,
                         hipStream_t stream);
 // Waves per match block whose ring tiles fit in max_lds bytes of LDS.
 int match_waves(const Shape &s, size_t max_lds);

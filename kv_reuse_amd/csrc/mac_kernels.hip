@@ -177,6 +177,16 @@ struct WaveAcc {
     }
 };
 
+// Key/value rows are streamed once per step: non-temporal 16-byte loads keep
+// them from displacing reusable lines in L2 and the Infinity Cache (used where
+// a wave load covers whole 128-byte lines).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const void *p)
+{
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
 template <typename T>
 struct PageRegs {
     uint4 k[Kv<T>::LPP], v[Kv<T>::LPP];
@@ -189,10 +199,10 @@ __device__ __forceinline__ void load_page(PageRegs<T> &r, const T *kp, const T *
     const int lane = lane_id(), row = lane / K::LPR, col = lane % K::LPR;
 #pragma unroll
     for (int s = 0; s < K::LPP; ++s)
-        r.k[s] = *reinterpret_cast<const uint4 *>(kp + (s * K::RPL + row) * D + col * K::E);
+        r.k[s] = load_stream(kp + (s * K::RPL + row) * D + col * K::E);
 #pragma unroll
     for (int s = 0; s < K::LPP; ++s)
-        r.v[s] = *reinterpret_cast<const uint4 *>(vp + (s * K::RPL + row) * D + col * K::E);
+        r.v[s] = load_stream(vp + (s * K::RPL + row) * D + col * K::E);
 }
 
 // Fold one page into the wave's state.  Token t of the page is valid for
@@ -414,35 +424,27 @@ __device__ __forceinline__ int find_group(const int *off, int nG, long x)
 
 // ================================================================== match
 // Grid (Hkv, B), 64 to 256 threads: the block owns one GQA group, its waves
-// take the group's query heads in turn.  Each head's ring tile (W x D fp32) is staged in
-// LDS with coalesced 16-byte loads; 64/W lanes share a slot's distance, and a
-// DPP/ds_swizzle butterfly finds the nearest entry.
+// take the group's query heads in turn.  Each head's ring tile (W x D fp32) is
+// staged in the wave's own LDS region with coalesced 16-byte loads; 64/W lanes
+// share a slot's distance, and a DPP/ds_swizzle butterfly finds the nearest
+// entry.  The kernel is latency-bound, so every load that does not depend on
+// the query position (queries, angles, ring tile, stamps, override, the
+// group's counters) is issued before any of them is waited on.
 __global__ __launch_bounds__(BLOCK) void match_kernel(Shape s, State st, KvView kv,
                                                       const int32_t *__restrict__ seq_lens,
                                                       const float *__restrict__ q_pre,
-                                                      const int32_t *__restrict__ ovr)
+                                                      const int32_t *__restrict__ ovr,
+                                                      float *__restrict__ out)
 {
     extern __shared__ float lds[];
     __shared__ int h_start[64];
-    __shared__ int cnt[4];   // hits, misses, near tau, invalid overrides
+    __shared__ int wcnt[WAVES][4];   // per wave: hits, misses, near tau, invalid overrides
     const int b = blockIdx.y, kvh = blockIdx.x;
     const int lane = lane_id(), wv = threadIdx.x >> 6;
-    constexpr int RS = D + 4;   // LDS row stride (floats)
-
-    int m = seq_lens[b] - 1;
-    bool bad = false;
-    if (m >= 0 && (m >= kv.max_seq_len || (kv.paged && m / PAGE >= kv.max_pages)))
-        bad = true;
-    if (bad)
-        m = -1;
-    if (threadIdx.x < 4)
-        cnt[threadIdx.x] = 0;
-    if (kvh == 0 && threadIdx.x == 0) {
-        st.m_buf[b] = m;
-        if (bad)
-            atomicAdd(&st.stats[ST_BAD_INPUT], 1ULL);
-    }
-    __syncthreads();
+    const int nwv = blockDim.x >> 6;   // waves in the block (sized to the LDS budget)
+    constexpr int RS = D + 4;          // LDS row stride (floats)
+    const long g = (long)b * s.Hkv + kvh;
+    unsigned long long *gstat = st.stats + MAC_NSTAT + g * GRP_NSTAT;
 
     // lanes per ring slot: a power of two, at most 32 so each lane owns a
     // whole number of float4 columns (D / L >= 4)
@@ -451,43 +453,91 @@ __global__ __launch_bounds__(BLOCK) void match_kernel(Shape s, State st, KvView 
         L &= L - 1;
     if (L > 32)
         L = 32;
-    const int nwv = blockDim.x >> 6;   // waves in the block (sized to the LDS budget)
+    const int j = lane / L, part = lane % L, span = D / L;
+    const int jc = j < s.W ? j : s.W - 1;
+    const int lc = lane < s.W ? lane : s.W - 1;
+
+    // ---- loads independent of the position
+    const int seq = seq_lens[b];
+    const int pos_j = st.ring_pos[(long)b * s.W + jc];    // stamp of this lane's slot
+    const int pos_l = st.ring_pos[(long)b * s.W + lc];    // stamp of slot `lane`
+    const double inv = st.inv_freq[lane];
+    unsigned long long old[GRP_NSTAT] = {};
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int k = 0; k < GRP_NSTAT; ++k)
+            old[k] = gstat[k];
+    }
     float *tile = lds + wv * (s.W * RS + D);
     float *qs = tile + s.W * RS;
+    int my_cnt[4] = {0, 0, 0, 0};
+
+    int m = seq - 1;
+    const bool bad = m >= 0 && (m >= kv.max_seq_len || (kv.paged && m / PAGE >= kv.max_pages));
+    if (bad)
+        m = -1;
 
     for (int hb = 0; hb < s.G; hb += nwv) {
         const int hh = hb + wv;
         const bool head = hh < s.G;
-        const bool act = head && m >= 0;
-        const long idx = (long)b * s.Hq + kvh * s.G + hh;
+        const long idx = (long)b * s.Hq + kvh * s.G + (head ? hh : 0);
         float qa = 0.f, qb = 0.f;
-        if (act) {
+        int ov = -2;
+        if (head) {
             qa = q_pre[idx * D + lane];
             qb = q_pre[idx * D + lane + 64];
-            st.q_copy[idx * D + lane] = qa;
-            st.q_copy[idx * D + lane + 64] = qb;
-            // rotate-half RoPE, angle m * theta^(-2i/D) formed in fp64
-            const double phi = (double)m * st.inv_freq[lane];
-            double sn, cs;
-            sincos(phi, &sn, &cs);
-            st.q_rot[idx * D + lane] = (float)((double)qa * cs - (double)qb * sn);
-            st.q_rot[idx * D + lane + 64] = (float)((double)qb * cs + (double)qa * sn);
+            if (ovr)
+                ov = ovr[idx];
             if (s.reuse) {
-                const float *src = st.ring_q + idx * s.W * D;
-                for (int i = lane; i < s.W * (D / 4); i += 64) {
-                    const int j = i / (D / 4), c4 = i % (D / 4);
-                    *reinterpret_cast<float4 *>(tile + j * RS + c4 * 4) =
-                        *reinterpret_cast<const float4 *>(src + (long)j * D + c4 * 4);
+                // a batch of 8 loads per lane is in flight before its LDS writes;
+                // indices past the tile are clamped (in-bounds re-reads whose
+                // values are not stored), so the batch stays in registers
+                const float4 *src = reinterpret_cast<const float4 *>(st.ring_q + idx * s.W * D);
+                const int n4 = s.W * (D / 4);
+                for (int base = 0; base < n4; base += 64 * 8) {
+                    float4 t0, t1, t2, t3, t4, t5, t6, t7;
+#define MAC_LD(T, C) T = src[min(base + (C) * 64 + lane, n4 - 1)];
+                    MAC_LD(t0, 0) MAC_LD(t1, 1) MAC_LD(t2, 2) MAC_LD(t3, 3)
+                    MAC_LD(t4, 4) MAC_LD(t5, 5) MAC_LD(t6, 6) MAC_LD(t7, 7)
+#undef MAC_LD
+#define MAC_ST(T, C)                                                                         \
+    {                                                                                       \
+        const int i = base + (C) * 64 + lane;                                               \
+        if (i < n4)                                                                         \
+            *reinterpret_cast<float4 *>(tile + (i / (D / 4)) * RS + (i % (D / 4)) * 4) = T; \
+    }
+                    MAC_ST(t0, 0) MAC_ST(t1, 1) MAC_ST(t2, 2) MAC_ST(t3, 3)
+                    MAC_ST(t4, 4) MAC_ST(t5, 5) MAC_ST(t6, 6) MAC_ST(t7, 7)
+#undef MAC_ST
                 }
                 qs[lane] = qa;
                 qs[lane + 64] = qb;
             }
         }
-        __syncthreads();
+        const bool act = head && m >= 0;
         int slot = -1, p = -1, start = 0;
         float rel = NAN;
+        if (act) {
+            st.q_copy[idx * D + lane] = qa;
+            st.q_copy[idx * D + lane + 64] = qb;
+            // rotate-half RoPE, angle m * theta^(-2i/D) formed in fp64 and
+            // reduced to [-pi, pi] in fp64 (Cody-Waite, 2*pi split in two
+            // doubles, fma), so sincos stays on its short-argument path
+            const double phi = (double)m * inv;
+            const double k = rint(phi * 0.15915494309189535);   // 1 / (2*pi)
+            double red = fma(-k, 6.283185307179586232, phi);      // 2*pi rounded to double
+            red = fma(-k, 2.4492935982947064e-16, red);            // 2*pi minus that double
+            double sn, cs;
+            sincos(red, &sn, &cs);
+            st.q_rot[idx * D + lane] = (float)((double)qa * cs - (double)qb * sn);
+            st.q_rot[idx * D + lane + 64] = (float)((double)qb * cs + (double)qa * sn);
+        } else if (head) {
+            // idle request: its output is zero (no group of it gets work)
+            out[idx * D + lane] = 0.f;
+            out[idx * D + lane + 64] = 0.f;
+        }
         if (act && s.reuse) {
-            const int j = lane / L, part = lane % L, span = D / L;
+            // this wave wrote its own tile above; LDS accesses of a wave are ordered
             float dp = 0.f;
             if (j < s.W) {
                 const float *rr = tile + j * RS + part * span;
@@ -507,10 +557,9 @@ __global__ __launch_bounds__(BLOCK) void match_kernel(Shape s, State st, KvView 
             if (L >= 8) dp += xor_lanes<4>(dp);
             if (L >= 16) dp += xor_lanes<8>(dp);
             if (L >= 32) dp += xor_lanes<16>(dp);
-            const int pos = j < s.W ? st.ring_pos[(long)b * s.W + j] : -1;
-            const bool valid = j < s.W && pos >= 0 && pos <= m;
+            const bool valid = j < s.W && pos_j >= 0 && pos_j <= m;
             float kd = valid ? dp : INFINITY;
-            int kp = valid ? pos : INT_MIN;
+            int kp = valid ? pos_j : INT_MIN;
             int kj = valid ? j : -1;
             // nearest entry: smallest distance, then newest position, then larger slot
 #define MAC_ARGMIN_STEP(OFF)                                                                 \
@@ -539,59 +588,70 @@ __global__ __launch_bounds__(BLOCK) void match_kernel(Shape s, State st, KvView 
                     slot = kj;
                     p = kp;
                 }
-                if (lane == 0 && fabsf(rel - s.tau) < 1e-4f)
-                    atomicAdd(&cnt[2], 1);
+                if (fabsf(rel - s.tau) < 1e-4f)
+                    my_cnt[2] += 1;
             }
-            if (ovr) {
-                const int ov = ovr[idx];
-                if (ov != -2) {
-                    slot = -1;
-                    p = -1;
-                    if (ov >= 0) {
-                        const bool mine = lane < s.W && ov <= m &&
-                                          st.ring_pos[(long)b * s.W + lane] == ov;
-                        const unsigned long long bal = __ballot(mine);
-                        if (bal) {
-                            slot = 63 - __clzll(bal);
-                            p = ov;
-                        } else if (lane == 0) {
-                            atomicAdd(&cnt[3], 1);
-                        }
+            if (ov != -2) {
+                slot = -1;
+                p = -1;
+                if (ov >= 0) {
+                    const bool mine = lane < s.W && ov <= m && pos_l == ov;
+                    const unsigned long long bal = __ballot(mine);
+                    if (bal) {
+                        slot = 63 - __clzll(bal);
+                        p = ov;
+                    } else {
+                        my_cnt[3] += 1;
                     }
                 }
             }
             if (slot >= 0)
                 start = max(p - s.r + 1, 0);
         }
+        if (act)
+            my_cnt[slot >= 0 ? 0 : 1] += 1;
         if (head && lane == 0) {
             st.dec_slot[idx] = slot;
             st.dec_p[idx] = p;
             st.dec_start[idx] = start;
             st.dec_rel[idx] = rel;
             h_start[hh] = start;
-            if (act)
-                atomicAdd(&cnt[slot >= 0 ? 0 : 1], 1);
         }
-        __syncthreads();
     }
+    if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            wcnt[wv][k] = my_cnt[k];
+    }
+    __syncthreads();
 
     if (threadIdx.x == 0) {
+        if (kvh == 0) {
+            st.m_buf[b] = m;
+            if (bad)
+                atomicAdd(&st.stats[ST_BAD_INPUT], 1ULL);
+        }
         int gs = -1;
         if (m >= 0) {
             gs = m + 1;
             for (int h = 0; h < s.G; ++h)
                 gs = min(gs, h_start[h]);
         }
-        st.grp_start[(long)b * s.Hkv + kvh] = gs;
+        st.grp_start[g] = gs;
         if (m >= 0) {
-            atomicAdd(&st.stats[ST_HITS], (unsigned long long)cnt[0]);
-            atomicAdd(&st.stats[ST_MISSES], (unsigned long long)cnt[1]);
-            atomicAdd(&st.stats[ST_DECISIONS], (unsigned long long)(cnt[0] + cnt[1]));
-            atomicAdd(&st.stats[ST_NEAR_TAU], (unsigned long long)cnt[2]);
-            atomicAdd(&st.stats[ST_OVR_INVALID], (unsigned long long)cnt[3]);
-            atomicAdd(&st.stats[ST_TOK_CRIT], (unsigned long long)(m - gs + 1));
+            // this block owns the group's counters for the step: no atomics
+            unsigned long long c[4] = {0, 0, 0, 0};
+            for (int w = 0; w < nwv; ++w)
+                for (int k = 0; k < 4; ++k)
+                    c[k] += (unsigned long long)wcnt[w][k];
+            gstat[ST_HITS] = old[ST_HITS] + c[0];
+            gstat[ST_MISSES] = old[ST_MISSES] + c[1];
+            gstat[ST_DECISIONS] = old[ST_DECISIONS] + c[0] + c[1];
+            gstat[ST_NEAR_TAU] = old[ST_NEAR_TAU] + c[2];
+            gstat[ST_OVR_INVALID] = old[ST_OVR_INVALID] + c[3];
+            gstat[ST_TOK_CRIT] = old[ST_TOK_CRIT] + (unsigned long long)(m - gs + 1);
             if (s.reuse && m - s.r >= 0)
-                atomicAdd(&st.stats[ST_TOK_AMEND], (unsigned long long)s.r);
+                gstat[ST_TOK_AMEND] = old[ST_TOK_AMEND] + (unsigned long long)s.r;
         }
     }
 }
@@ -694,6 +754,10 @@ struct MPage {
     uint4 k[4], v[4];
 };
 
+// K arrives in the MFMA layout: one wave load covers 64 of the 128 bytes of 16
+// rows, so every cache line is shared by two consecutive loads and is read
+// with the default policy (a streaming hint makes the second half refetch).
+// V arrives as contiguous 1 KB wave loads of whole lines and is streamed.
 __device__ __forceinline__ void load_mpage(MPage &r, const uint16_t *kp, const uint16_t *vp)
 {
     const int lane = lane_id(), t = lane & 15, q = lane >> 4;
@@ -702,7 +766,7 @@ __device__ __forceinline__ void load_mpage(MPage &r, const uint16_t *kp, const u
         r.k[s] = *reinterpret_cast<const uint4 *>(kp + t * D + 32 * s + 8 * q);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        r.v[s] = *reinterpret_cast<const uint4 *>(vp + (4 * s + q) * D + 8 * t);
+        r.v[s] = load_stream(vp + (4 * s + q) * D + 8 * t);
 }
 
 template <int G>
@@ -932,43 +996,54 @@ __global__ __launch_bounds__(BLOCK) void complete_mfma_kernel(Shape s, State st,
     }
 }
 
-// ================================================================= reduce
-// Grid (Hkv, B): combine a group's partial summaries per head, then merge
-// (+) with the matched entry's stored AS_{1:p-r}.  Writes out (normalised)
-// and keeps AS_{1:m} for amend.  Each lane owns two output columns.
+// ================================================================== reduce
+// Grid (Hkv, B): combine a group's partial summaries (slots w + g, w in
+// [wlo, whi]) per head, one wave per head, then merge (+) with the matched
+// entry's stored AS_{1:p-r}.  Writes out (normalised) and keeps AS_{1:m} for
+// amend.  Each lane owns two output columns.  Latency-bound: the decision and
+// the stored summary are fetched before they are needed.
 template <int G>
 __global__ __launch_bounds__(BLOCK) void reduce_kernel(Shape s, State st, float *__restrict__ out)
 {
     extern __shared__ int s_off[];
+    constexpr int HPW = (G + WAVES - 1) / WAVES;   // heads per wave
+    const int b = blockIdx.y, kvh = blockIdx.x, g = b * s.Hkv + kvh;
+    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    int slot[HPW];
+#pragma unroll
+    for (int i = 0; i < HPW; ++i) {
+        const int hh = wv + i * WAVES;
+        slot[i] = hh < G ? st.dec_slot[(long)b * s.Hq + kvh * G + hh] : -1;
+    }
     const int nG = s.B * s.Hkv;
     build_plan(s, st, s_off);
     const int P = s_off[nG];
-    const int nW = P > 0 ? active_workers(st.n_workers, P) : 1;
-    const int b = blockIdx.y, kvh = blockIdx.x, g = b * s.Hkv + kvh;
-    const int lane = lane_id(), wv = threadIdx.x >> 6;
-    const int m = st.m_buf[b];
-    const bool idle = m < 0 || s_off[g + 1] == s_off[g];
-    for (int hh = wv; hh < G; hh += WAVES) {
+    if (st.m_buf[b] < 0 || s_off[g + 1] == s_off[g])
+        return;   // idle request: match wrote its zero output
+    const int nW = active_workers(st.n_workers, P);
+    const int wlo = page_owner(s_off[g], nW, P);
+    const int whi = page_owner((long)s_off[g + 1] - 1, nW, P);
+#pragma unroll
+    for (int i = 0; i < HPW; ++i) {
+        const int hh = wv + i * WAVES;
+        if (hh >= G)
+            break;
         const long idx = (long)b * s.Hq + kvh * G + hh;
-        float *o = out + idx * D;
-        float *asf = st.as_full + idx * SUMM;
-        if (idle) {
-            *reinterpret_cast<float2 *>(o + 2 * lane) = make_float2(0.f, 0.f);
-            *reinterpret_cast<float2 *>(asf + 2 * lane) = make_float2(0.f, 0.f);
-            if (lane == 0) {
-                asf[D] = NEG_INF;
-                asf[D + 1] = 0.f;
-            }
-            continue;
+        const float *rs = st.ring_s + (idx * s.W + (slot[i] >= 0 ? slot[i] : 0)) * SUMM;
+        float2 so = make_float2(0.f, 0.f);
+        float Ms = NEG_INF, Ls = 0.f;
+        if (slot[i] >= 0) {
+            so = *reinterpret_cast<const float2 *>(rs + 2 * lane);
+            Ms = rs[D];
+            Ls = rs[D + 1];
         }
-        const int wlo = page_owner(s_off[g], nW, P);
-        const int whi = page_owner((long)s_off[g + 1] - 1, nW, P);
         float Mx = NEG_INF;
         for (int w = wlo + lane; w <= whi; w += 64)
             Mx = fmaxf(Mx, st.partials[(((long)w + g) * G + hh) * SUMM + D]);
         Mx = wave_max(Mx);
         const float base = Mx == NEG_INF ? 0.f : Mx;
         float a0 = 0.f, a1 = 0.f, Lf = 0.f;
+#pragma unroll 4
         for (int w = wlo; w <= whi; ++w) {
             const float *pp = st.partials + (((long)w + g) * G + hh) * SUMM;
             const float sc = exp2f(pp[D] - base);
@@ -978,22 +1053,17 @@ __global__ __launch_bounds__(BLOCK) void reduce_kernel(Shape s, State st, float 
             a1 = fmaf(v.y, sc, a1);
         }
         float o0 = a0 / Lf, o1 = a1 / Lf, Mo = Mx, Lo = Lf;
-        const int slot = st.dec_slot[idx];
-        if (slot >= 0) {
-            const float *rs = st.ring_s + (idx * s.W + slot) * SUMM;
-            const float Ms = rs[D], Ls = rs[D + 1];
-            if (Ls > 0.f) {
-                const float Mn = fmaxf(Ms, Mx);
-                const float ca = Ls * exp2f(Ms - Mn), cb = Lf * exp2f(Mx - Mn);
-                const float Ln = ca + cb;
-                const float2 so = *reinterpret_cast<const float2 *>(rs + 2 * lane);
-                o0 = (ca * so.x + cb * o0) / Ln;
-                o1 = (ca * so.y + cb * o1) / Ln;
-                Mo = Mn;
-                Lo = Ln;
-            }
+        if (Ls > 0.f) {
+            const float Mn = fmaxf(Ms, Mx);
+            const float ca = Ls * exp2f(Ms - Mn), cb = Lf * exp2f(Mx - Mn);
+            const float Ln = ca + cb;
+            o0 = (ca * so.x + cb * o0) / Ln;
+            o1 = (ca * so.y + cb * o1) / Ln;
+            Mo = Mn;
+            Lo = Ln;
         }
-        *reinterpret_cast<float2 *>(o + 2 * lane) = make_float2(o0, o1);
+        *reinterpret_cast<float2 *>(out + idx * D + 2 * lane) = make_float2(o0, o1);
+        float *asf = st.as_full + idx * SUMM;
         *reinterpret_cast<float2 *>(asf + 2 * lane) = make_float2(o0, o1);
         if (lane == 0) {
             asf[D] = Mo;
@@ -1003,13 +1073,16 @@ __global__ __launch_bounds__(BLOCK) void reduce_kernel(Shape s, State st, float 
 }
 
 // ================================================================== amend
-// Grid (Hkv, B): the block's waves share the band [m-r+1, m] page by page,
-// combine in LDS, then per head AS_{1:m-r} = AS_{1:m} (-) band and the ring
-// slot receives (q~_m, AS_{1:m-r}, m).
+// Grid (Hkv, B), 8 waves: the waves share the band [m-r+1, m] page by page
+// (two or three pages each at r = 256), combine in LDS, then per head
+// AS_{1:m-r} = AS_{1:m} (-) band and the ring slot receives (q~_m, AS_{1:m-r}, m).
+constexpr int AMEND_WAVES = 8;
+
 template <typename T, int G>
-__global__ __launch_bounds__(BLOCK) void amend_kernel(Shape s, State st, KvView kv, int slot_new)
+__global__ __launch_bounds__(64 * AMEND_WAVES) void amend_kernel(Shape s, State st, KvView kv,
+                                                                 int slot_new)
 {
-    __shared__ float red[WAVES][G][SUMM];
+    __shared__ float red[AMEND_WAVES][G][SUMM];
     using K = Kv<T>;
     const int b = blockIdx.y, kvh = blockIdx.x;
     const int lane = lane_id(), wv = threadIdx.x >> 6;
@@ -1028,7 +1101,7 @@ __global__ __launch_bounds__(BLOCK) void amend_kernel(Shape s, State st, KvView 
         WaveAcc<G, K::E> acc;
         acc.init();
         PageRegs<T> r;
-        for (int page = lo / PAGE + wv; page <= m / PAGE; page += WAVES) {
+        for (int page = lo / PAGE + wv; page <= m / PAGE; page += AMEND_WAVES) {
             load_page<T>(r, kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page, &st.stats[ST_BAD_INPUT]),
                          kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page, &st.stats[ST_BAD_INPUT]));
             const int tok0 = page * PAGE;
@@ -1037,18 +1110,18 @@ __global__ __launch_bounds__(BLOCK) void amend_kernel(Shape s, State st, KvView 
         store_wave_summary<T, G>(acc, &red[wv][0][0]);
     }
     __syncthreads();
-    for (int hh = wv; hh < G; hh += WAVES) {
+    for (int hh = wv; hh < G; hh += AMEND_WAVES) {
         const long idx = (long)b * s.Hq + kvh * G + hh;
         float so0 = 0.f, so1 = 0.f, sM = NEG_INF, sL = 0.f;   // EMPTY
         if (has_prefix) {
             float Mx = NEG_INF;
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w)
+            for (int w = 0; w < AMEND_WAVES; ++w)
                 Mx = fmaxf(Mx, red[w][hh][D]);
             const float base = Mx == NEG_INF ? 0.f : Mx;
             float a0 = 0.f, a1 = 0.f, Lb = 0.f;
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w) {
+            for (int w = 0; w < AMEND_WAVES; ++w) {
                 const float sc = exp2f(red[w][hh][D] - base);
                 Lb = fmaf(red[w][hh][D + 1], sc, Lb);
                 a0 = fmaf(red[w][hh][2 * lane], sc, a0);
@@ -1121,12 +1194,13 @@ __global__ __launch_bounds__(64) void append_kernel(Shape s, State st, KvView kv
 }
 
 // ================================================================== reset
-__global__ void reset_kernel(int32_t *ring_pos, long n_pos, unsigned long long *stats)
+__global__ void reset_kernel(int32_t *ring_pos, long n_pos, unsigned long long *stats,
+                             long n_stats)
 {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n_pos)
         ring_pos[i] = -1;
-    if (i < MAC_NSTAT)
+    if (i < n_stats)
         stats[i] = 0ULL;
 }
 
@@ -1173,8 +1247,8 @@ hipError_t launch_amend_t(const Shape &s, const State &st, const KvView &kv, int
     switch (s.G) {
 #define MAC_CASE(GG)                                                                          \
     case GG:                                                                                  \
-        hipLaunchKernelGGL((amend_kernel<T, GG>), grid, dim3(BLOCK), 0, stream, s, st, kv,     \
-                           slot_new);                                                         \
+        hipLaunchKernelGGL((amend_kernel<T, GG>), grid, dim3(64 * AMEND_WAVES), 0, stream, s,  \
+                           st, kv, slot_new);                                                 \
         break;
         MAC_CASE(1)
         MAC_CASE(2)
@@ -1200,12 +1274,12 @@ int match_waves(const Shape &s, size_t max_lds)
 }
 
 hipError_t launch_match(const Shape &s, const State &st, const KvView &kv, const int32_t *seq_lens,
-                        const float *q_pre, const int32_t *override_pos, int waves,
+                        const float *q_pre, const int32_t *override_pos, float *out, int waves,
                         hipStream_t stream)
 {
     const size_t lds = (size_t)waves * (s.W * (D + 4) + D) * sizeof(float);
     hipLaunchKernelGGL(match_kernel, dim3(s.Hkv, s.B), dim3(64 * waves), lds, stream, s, st, kv,
-                       seq_lens, q_pre, override_pos);
+                       seq_lens, q_pre, override_pos, out);
     return hipGetLastError();
 }
 
@@ -1254,9 +1328,10 @@ hipError_t launch_append(const Shape &s, const State &st, const KvView &kv, bool
 hipError_t launch_reset(const Shape &s, const State &st, hipStream_t stream)
 {
     const long n = (long)s.B * s.W;
-    const long tot = n > MAC_NSTAT ? n : MAC_NSTAT;
+    const long ns = stats_count(s.B * s.Hkv);
+    const long tot = n > ns ? n : ns;
     hipLaunchKernelGGL(reset_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream,
-                       st.ring_pos, n, st.stats);
+                       st.ring_pos, n, st.stats, ns);
     return hipGetLastError();
 }
 

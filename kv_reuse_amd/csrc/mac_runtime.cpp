@@ -11,6 +11,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "mac.h"
 #include "mac_internal.h"
@@ -89,7 +90,7 @@ Sizes sizes_for(const mac_config &c, int n_workers)
     s.grp = round256(B * Hkv * sizeof(int32_t));
     s.partials = round256(((size_t)n_workers + B * Hkv) * G * mac::SUMM * sizeof(float));
     s.as_full = round256(B * Hq * mac::SUMM * sizeof(float));
-    s.stats = round256(mac::MAC_NSTAT * sizeof(unsigned long long));
+    s.stats = round256(mac::stats_count((long)B * Hkv) * sizeof(unsigned long long));
     s.inv_freq = round256(mac::D / 2 * sizeof(double));
     return s;
 }
@@ -423,7 +424,7 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
         MAC_HIP(h, hipStreamWaitEvent(st, h->ev_amend, 0));
     if (timing)
         MAC_HIP(h, hipEventRecord(h->tm[0], st));
-    MAC_HIP(h, mac::launch_match(h->shape, h->st, v, kv->seq_lens, q_pre_rope, override_pos,
+    MAC_HIP(h, mac::launch_match(h->shape, h->st, v, kv->seq_lens, q_pre_rope, override_pos, out,
                                  h->match_waves, st));
     if (timing)
         MAC_HIP(h, hipEventRecord(h->tm[1], st));
@@ -462,8 +463,17 @@ mac_status mac_stats(mac_handle h, mac_stats_t *out)
     if (h->amend_stream)
         MAC_HIP(h, hipStreamSynchronize(h->amend_stream));
     MAC_HIP(h, hipDeviceSynchronize());
+    const long n_groups = (long)h->cfg.batch * h->cfg.num_kv_heads;
+    std::vector<unsigned long long> raw(mac::stats_count(n_groups));
+    MAC_HIP(h, hipMemcpy(raw.data(), h->st.stats, raw.size() * sizeof(unsigned long long),
+                         hipMemcpyDeviceToHost));
     unsigned long long c[mac::MAC_NSTAT];
-    MAC_HIP(h, hipMemcpy(c, h->st.stats, sizeof c, hipMemcpyDeviceToHost));
+    for (int k = 0; k < mac::MAC_NSTAT; ++k)
+        c[k] = raw[k];
+    for (long g = 0; g < n_groups; ++g)
+        for (int k = 0; k < mac::GRP_NSTAT; ++k)
+            if (k != mac::ST_BAD_INPUT)
+                c[k] += raw[mac::MAC_NSTAT + g * mac::GRP_NSTAT + k];
     std::memset(out, 0, sizeof *out);
     const uint64_t row = 2ull * mac::D * (h->kv_fp32 ? 4 : 2);   // one key row + one value row
     out->steps = (uint64_t)h->calls;
