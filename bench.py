@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--config", default="b16_128k")
     ap.add_argument("--r", type=int, default=0, help="override the band width")
+    ap.add_argument("--set", action="append", default=[], metavar="FIELD=VALUE",
+                    help="override a workload field (B, Hq, Hkv, C, W, r, tau, ...)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline-kernel", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -122,6 +124,15 @@ def main():
     w = get_config(args.config)
     if args.r:
         w = scaled(w, r=args.r)
+    for kv_pair in args.set:
+        key, val = kv_pair.split("=", 1)
+        cur = getattr(w, key)
+        if key == "rho":
+            parts = val.split(",")
+            val = (parts[0],) + tuple(float(x) for x in parts[1:])
+        else:
+            val = type(cur)(val)
+        w = scaled(w, **{key: val})
     total = args.warmup + args.steps
     assert total <= w.steps, "at most %d steps for this workload" % w.steps
     paged = w.layout == "paged"

@@ -769,18 +769,48 @@ __device__ __forceinline__ void load_mpage(MPage &r, const uint16_t *kp, const u
         r.v[s] = load_stream(vp + (4 * s + q) * D + 8 * t);
 }
 
+// HPL: heads whose logits one lane receives from the MFMA (4 row groups of 4
+// rows; row i holds head i % G).  For G = 8 the lanes of row groups 0 and 2
+// hold heads 0..3 and those of row groups 1 and 3 hold heads 4..7.
 template <int G>
 struct MAcc {
-    float M[G], L[G], acc[G][8];
+    static constexpr int HPL = G < 4 ? G : 4;
+    float M[G];           // wave-uniform reference max per head (log2 units)
+    float Ml[HPL];        // M of this lane's own heads (M[v], or M[4 + v] for G = 8)
+    float L[HPL];         // normaliser of this lane's heads over this lane's tokens
+    float acc[G][8];      // P.V over this lane's V rows and 8 columns
 };
 
-// qa: this wave's A operands in LDS, [8][64] (register i of lane l at qa[i*64 + l]).
+// Per-lane choice between two registers by a lane mask.  Written as the
+// instruction itself: a C select between two elements of a register array is
+// folded by the compiler into an indexed access, which moves the array to
+// scratch memory.
+__device__ __forceinline__ float lane_pick(unsigned long long mask, float if_set, float if_clear)
+{
+    float r;
+    asm volatile("v_cndmask_b32_e64 %0, %1, %2, %3"
+                 : "=v"(r)
+                 : "v"(if_clear), "v"(if_set), "s"(mask));
+    return r;
+}
+
+__device__ __forceinline__ int lane_pick(unsigned long long mask, int if_set, int if_clear)
+{
+    return __float_as_int(lane_pick(mask, __int_as_float(if_set), __int_as_float(if_clear)));
+}
+
+// hsl: first key of each of this lane's own heads' spans.  half_mask: lanes
+// holding heads 4..7 (G = 8; zero otherwise).
 template <int G>
 __device__ __forceinline__ void compute_mpage(const MPage &r, const uint4 *qa, float4 *px,
-                                              int tok0, int m, const int (&hs)[G], bool masked,
+                                              int tok0, int m, const int (&hsl)[MAcc<G>::HPL],
+                                              bool masked, unsigned long long half_mask,
                                               MAcc<G> &st)
 {
+    constexpr int HPL = MAcc<G>::HPL;
+    constexpr int NPX = G > 4 ? 2 : 1;   // float4 of probabilities per token
     const int lane = lane_id(), t = lane & 15, q = lane >> 4;
+    const int half = G > 4 ? (q & 1) : 0;   // which four heads this lane holds
     floatx4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -791,49 +821,68 @@ __device__ __forceinline__ void compute_mpage(const MPage &r, const uint4 *qa, f
         S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, alo), kb, S1, 0,
                                                      0, 0);
     }
-    float lg[G];
+    float lg[HPL];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-        lg[g] = S0[g] + S1[g];
+    for (int v = 0; v < HPL; ++v)
+        lg[v] = S0[v] + S1[v];
     if (masked) {
         const int tok = tok0 + t;
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-            if (tok < hs[g] || tok > m)
-                lg[g] = NEG_INF;
+        for (int v = 0; v < HPL; ++v)
+            if (tok < hsl[v] || tok > m)
+                lg[v] = NEG_INF;
     }
     bool need = false;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-        need |= lg[g] > st.M[g] + LAZY_RESCALE;
+    for (int v = 0; v < HPL; ++v)
+        need |= lg[v] > st.Ml[v] + LAZY_RESCALE;
     if (__any(need)) {
+        float alpha[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float mn = fmaxf(st.M[g], wave_max(lg[g]));
-            const float alpha = mn == st.M[g] ? 1.f : exp2f(st.M[g] - mn);   // 0 from -inf
-            st.M[g] = mn;
-            st.L[g] *= alpha;
+        for (int h = 0; h < G; ++h) {
+            const bool mine = G > 4 ? (h / 4 == half) : true;
+            const float cand = mine ? lg[h % HPL] : NEG_INF;
+            const float mn = fmaxf(st.M[h], wave_max(cand));
+            alpha[h] = mn == st.M[h] ? 1.f : exp2f(st.M[h] - mn);   // 0 from -inf
+            st.M[h] = mn;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                st.acc[g][e] *= alpha;
+                st.acc[h][e] *= alpha[h];
+        }
+#pragma unroll
+        for (int v = 0; v < HPL; ++v) {
+            if constexpr (G > 4) {
+                st.L[v] *= lane_pick(half_mask, alpha[4 + v], alpha[v]);
+                st.Ml[v] = lane_pick(half_mask, st.M[4 + v], st.M[v]);
+            } else {
+                st.L[v] *= alpha[v];
+                st.Ml[v] = st.M[v];
+            }
         }
     }
     float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        p[g] = lg[g] == NEG_INF ? 0.f : exp2f(lg[g] - st.M[g]);
-        st.L[g] += p[g];
+    for (int v = 0; v < HPL; ++v) {
+        p[v] = lg[v] == NEG_INF ? 0.f : exp2f(lg[v] - st.Ml[v]);
+        st.L[v] += p[v];
     }
     // token t's probabilities -> the lanes holding V rows of token t
-    if (q == 0)
-        px[t] = make_float4(p[0], p[1], p[2], p[3]);
+    if (q < NPX)
+        px[t * NPX + q] = make_float4(p[0], p[1], p[2], p[3]);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float4 pt[4];
+    float pt[4][4 * NPX];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        pt[s] = px[4 * s + q];
+#pragma unroll
+        for (int k = 0; k < NPX; ++k) {
+            const float4 x = px[(4 * s + q) * NPX + k];
+            pt[s][4 * k + 0] = x.x;
+            pt[s][4 * k + 1] = x.y;
+            pt[s][4 * k + 2] = x.z;
+            pt[s][4 * k + 3] = x.w;
+        }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         float vf[8];
@@ -843,40 +892,54 @@ __device__ __forceinline__ void compute_mpage(const MPage &r, const uint4 *qa, f
             for (int e = 0; e < 8; ++e)
                 vf[e] = 0.f;
         }
-        const float pp[4] = {pt[s].x, pt[s].y, pt[s].z, pt[s].w};
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                st.acc[g][e] = fmaf(pp[g], vf[e], st.acc[g][e]);
+                st.acc[h][e] = fmaf(pt[s][h], vf[e], st.acc[h][e]);
     }
 }
 
+__device__ __forceinline__ float row16_max(float v)
+{
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    return v;
+}
+
 // Sum over the four row groups (tokens 4s + r) and, for L, over the 16 token
-// lanes; the first row stores columns 8c .. 8c+7.
+// lanes of a row holding the head; the first row stores columns 8c .. 8c+7.
 template <int G>
 __device__ __forceinline__ void store_msummary(MAcc<G> &st, float *dst)
 {
+    constexpr int HPL = MAcc<G>::HPL;
     const int lane = lane_id(), t = lane & 15, q = lane >> 4;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int h = 0; h < G; ++h) {
         float a[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            a[e] = st.acc[g][e];
+            a[e] = st.acc[h][e];
             a[e] += xor_lanes<16>(a[e]);
             a[e] += xor_lanes<32>(a[e]);
         }
-        const float Lt = row16_sum(st.L[g]);
         if (q == 0) {
-            float *o = dst + g * SUMM + 8 * t;
+            float *o = dst + h * SUMM + 8 * t;
             *reinterpret_cast<float4 *>(o) = make_float4(a[0], a[1], a[2], a[3]);
             *reinterpret_cast<float4 *>(o + 4) = make_float4(a[4], a[5], a[6], a[7]);
         }
-        if (lane == 0) {
-            dst[g * SUMM + D] = st.M[g];
-            dst[g * SUMM + D + 1] = Lt;
-        }
+        if (lane == 0)
+            dst[h * SUMM + D] = st.M[h];
+    }
+#pragma unroll
+    for (int v = 0; v < HPL; ++v) {
+        const float Lt = row16_sum(st.L[v]);
+        if (lane == 0)
+            dst[v * SUMM + D + 1] = Lt;
+        if (G > 4 && lane == 16)
+            dst[((4 + v) % G) * SUMM + D + 1] = Lt;
     }
 }
 
@@ -913,11 +976,12 @@ __device__ __forceinline__ void build_qa(const Shape &s, const State &st, int b,
 }
 
 template <int G>
-__global__ __launch_bounds__(BLOCK) void complete_mfma_kernel(Shape s, State st, KvView kv)
+__global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Shape s, State st,
+                                                                     KvView kv)
 {
     extern __shared__ int s_off[];
     __shared__ uint4 qlds[WAVES][8][64];   // per wave: 8 A-operand registers x 64 lanes
-    __shared__ float4 plds[WAVES][16];     // per wave: probabilities of the page's 16 tokens
+    __shared__ float4 plds[WAVES][32];     // per wave: probabilities of the page's 16 tokens
     const int nG = s.B * s.Hkv;
     build_plan(s, st, s_off);
     const int P = s_off[nG];
@@ -941,12 +1005,22 @@ __global__ __launch_bounds__(BLOCK) void complete_mfma_kernel(Shape s, State st,
         const int b = g / s.Hkv, kvh = g % s.Hkv;
         const int m = st.m_buf[b];
         const int first_page = st.grp_start[g] / PAGE;
+        constexpr int HPL = MAcc<G>::HPL;
+        const unsigned long long half_mask = G > 4 ? __ballot((lane >> 4) & 1) : 0ULL;
         int hs[G];
         int hmax = 0;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             hs[h] = st.dec_start[(long)b * s.Hq + kvh * G + h];
             hmax = max(hmax, hs[h]);
+        }
+        int hsl[HPL];
+#pragma unroll
+        for (int v = 0; v < HPL; ++v) {
+            if constexpr (G > 4)
+                hsl[v] = lane_pick(half_mask, hs[(4 + v) % G], hs[v]);
+            else
+                hsl[v] = hs[v];
         }
         {
             uint4 qa[8];
@@ -959,35 +1033,27 @@ __global__ __launch_bounds__(BLOCK) void complete_mfma_kernel(Shape s, State st,
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             acc.M[h] = NEG_INF;
-            acc.L[h] = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 acc.acc[h][e] = 0.f;
         }
+#pragma unroll
+        for (int v = 0; v < HPL; ++v) {
+            acc.L[v] = 0.f;
+            acc.Ml[v] = NEG_INF;
+        }
         int page = first_page + (int)(x - s_off[g]);
         const int last = first_page + (int)(gend - s_off[g]) - 1;
-        MPage r0, r1;
-        load_mpage(r0, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad),
-                   kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page, bad));
+        // one page in flight per wave: at <= 168 VGPRs (G <= 4) three waves
+        // share each SIMD, which hides the load latency better than double
+        // buffering at two waves per SIMD (measured)
+        MPage r0;
         while (true) {
-            if (page + 1 <= last)
-                load_mpage(r1, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page + 1, bad),
-                           kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page + 1, bad));
-            {
-                const int tok0 = page * PAGE;
-                compute_mpage<G>(r0, &qlds[wv][0][0], plds[wv], tok0, m, hs,
-                                 tok0 < hmax || tok0 + PAGE - 1 > m, acc);
-            }
-            if (++page > last)
-                break;
-            if (page + 1 <= last)
-                load_mpage(r0, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page + 1, bad),
-                           kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page + 1, bad));
-            {
-                const int tok0 = page * PAGE;
-                compute_mpage<G>(r1, &qlds[wv][0][0], plds[wv], tok0, m, hs,
-                                 tok0 < hmax || tok0 + PAGE - 1 > m, acc);
-            }
+            load_mpage(r0, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad),
+                       kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page, bad));
+            const int tok0 = page * PAGE;
+            compute_mpage<G>(r0, &qlds[wv][0][0], plds[wv], tok0, m, hsl,
+                             tok0 < hmax || tok0 + PAGE - 1 > m, half_mask, acc);
             if (++page > last)
                 break;
         }
@@ -1211,32 +1277,35 @@ hipError_t launch_complete_t(const Shape &s, const State &st, const KvView &kv, 
                              hipStream_t stream)
 {
     const size_t lds = plan_lds_bytes(s);
-    if (std::is_same<T, uint16_t>::value && s.G <= 4) {
+    if constexpr (std::is_same<T, uint16_t>::value) {
         switch (s.G) {
         case 1: hipLaunchKernelGGL(complete_mfma_kernel<1>, dim3(n_blocks), dim3(BLOCK), lds,
                                    stream, s, st, kv); break;
         case 2: hipLaunchKernelGGL(complete_mfma_kernel<2>, dim3(n_blocks), dim3(BLOCK), lds,
                                    stream, s, st, kv); break;
-        default: hipLaunchKernelGGL(complete_mfma_kernel<4>, dim3(n_blocks), dim3(BLOCK), lds,
+        case 4: hipLaunchKernelGGL(complete_mfma_kernel<4>, dim3(n_blocks), dim3(BLOCK), lds,
+                                   stream, s, st, kv); break;
+        default: hipLaunchKernelGGL(complete_mfma_kernel<8>, dim3(n_blocks), dim3(BLOCK), lds,
                                     stream, s, st, kv); break;
         }
         return hipGetLastError();
-    }
-    switch (s.G) {
+    } else {
+        switch (s.G) {
 #define MAC_CASE(GG)                                                                          \
     case GG:                                                                                  \
         hipLaunchKernelGGL((complete_kernel<T, GG>), dim3(n_blocks), dim3(BLOCK), lds, stream, \
                            s, st, kv);                                                        \
         break;
-        MAC_CASE(1)
-        MAC_CASE(2)
-        MAC_CASE(4)
-        MAC_CASE(8)
+            MAC_CASE(1)
+            MAC_CASE(2)
+            MAC_CASE(4)
+            MAC_CASE(8)
 #undef MAC_CASE
-    default:
-        return hipErrorInvalidValue;
+        default:
+            return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
     }
-    return hipGetLastError();
 }
 
 template <typename T>
@@ -1344,16 +1413,15 @@ int complete_blocks_per_cu(bool kv_fp32, int G, size_t lds)
     if (kv_fp32) {
         if (G == 1) MAC_OCC(float, 1); else if (G == 2) MAC_OCC(float, 2);
         else if (G == 4) MAC_OCC(float, 4); else MAC_OCC(float, 8);
-    } else if (G <= 4) {
+    } else {
         if (G == 1)
             e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_mfma_kernel<1>, BLOCK, lds);
         else if (G == 2)
             e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_mfma_kernel<2>, BLOCK, lds);
-        else
+        else if (G == 4)
             e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_mfma_kernel<4>, BLOCK, lds);
-    } else {
-        if (G == 1) MAC_OCC(uint16_t, 1); else if (G == 2) MAC_OCC(uint16_t, 2);
-        else if (G == 4) MAC_OCC(uint16_t, 4); else MAC_OCC(uint16_t, 8);
+        else
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_mfma_kernel<8>, BLOCK, lds);
     }
 #undef MAC_OCC
     return (e == hipSuccess && n > 0) ? n : 1;
