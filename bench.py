@@ -55,6 +55,7 @@ def parse():
                     help="override a workload field (B, Hq, Hkv, C, W, r, tau, ...)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline-kernel", action="store_true")
+    ap.add_argument("--no-32k", action="store_true", help="skip the 32K speedup point")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 2 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -82,13 +83,62 @@ class Bench:
                                      num_pages=self.kc.shape[0] if paged else 0)
         self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
 
-    def step(self, t, q, k_new, v_new):
+    def step(self, t, q, k_new, v_new, scrub=None):
         w = self.w
+        if scrub is not None:
+            # read 1 GiB: evicts the KV cache from L2 and the Infinity Cache
+            # without leaving dirty lines for the timed kernels to write back
+            scrub[1].copy_(scrub[0].sum())
         self.pos.fill_(w.C + t)
         self.seq.fill_(w.C + t + 1)
         self.layer.append_kv(self.view, k_new, v_new, self.pos, self.stream)
         self.layer.decode_step(self.view, q, self.out, None, self.stream)
         return self.layer.stats()          # synchronises; last step's kernel times
+
+
+def speedup_point(name, steps=24, warmup=40):
+    """MAC attention phase vs the in-house full-attention kernel on one workload,
+    with a 1 GiB scrub read before every step (the KV of small contexts fits in
+    the 256 MB Infinity Cache).  Kernel times are HIP events, so the scrub is not
+    in them."""
+    import torch
+    import kv_reuse_amd as mac
+    from workloads import get_config, kv_logical, page_table, queries, to_paged
+    w = get_config(name)
+    total = warmup + steps
+    K, V = kv_logical(w, "cuda")
+    idx = torch.arange(w.C, w.C + total, device="cuda")
+    k_rows = K[:, :, idx].permute(2, 0, 1, 3).contiguous()
+    v_rows = V[:, :, idx].permute(2, 0, 1, 3).contiguous()
+    q_dev = torch.as_tensor(queries(w, steps=total), device="cuda")
+    paged = w.layout == "paged"
+    if paged:
+        tab = page_table(w)
+        kc, vc, table = to_paged(K, tab), to_paged(V, tab), torch.as_tensor(tab, device="cuda")
+    else:
+        kc, vc, table = K, V, None
+    scrub = [torch.ones(1 << 28, dtype=torch.float32, device="cuda"),
+             torch.zeros((), dtype=torch.float32, device="cuda")]
+    res = {}
+    for label, flags in (("mac", 0), ("full", mac.MAC_F_DISABLE_REUSE)):
+        bn = Bench(w, flags, kc, vc, paged, table)
+        att, comp, hits = [], [], []
+        prev = None
+        for t in range(total):
+            st = bn.step(t, q_dev[t], k_rows[t], v_rows[t], scrub)
+            if t >= warmup:
+                att.append(st["last_us_attention"])
+                comp.append(st["last_us_complete"])
+                hits.append(st["hits"] - prev["hits"])
+            prev = st
+        bn.layer.close()
+        res[label] = (float(np.mean(att)), float(np.mean(comp)),
+                      float(np.sum(hits)) / (len(hits) * w.B * w.Hq))
+    return {"workload": name, "context": w.C, "batch": w.B,
+            "mac_attention_us": res["mac"][0], "mac_complete_us": res["mac"][1],
+            "full_attention_us": res["full"][0], "full_complete_us": res["full"][1],
+            "head_hit_rate": res["mac"][2], "speedup": res["full"][0] / res["mac"][0],
+            "steps": steps, "warmup": warmup}
 
 
 def oracle_baseline(w, K, V, qs, n_req, n_steps):
@@ -208,6 +258,11 @@ def main():
                 "speedup_vs_full": float(np.mean(fa)) / att_us}
         fb.layer.close()
 
+    point_32k = None
+    if not args.no_32k and args.config == "b16_128k" and not args.set and not args.r:
+        del bench
+        point_32k = speedup_point("llama32k")
+
     cpu = None
     if host_sample is not None:
         n_req = host_sample[0].shape[0]
@@ -257,6 +312,7 @@ def main():
                      "kernel": "complete_kernel", "bytes_per_launch": float(np.mean(comp_bytes))},
         "attention_phase_bytes_per_step": att_bytes,
         "full_attention_kernel": base,
+        "speedup_32k": point_32k,
         "cpu_baseline": cpu,
         "setup_s": t_setup,
         "bad_input": int(st1["bad_input"]),

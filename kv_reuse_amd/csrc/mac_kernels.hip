@@ -1063,23 +1063,36 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
 }
 
 // ================================================================== reduce
-// Grid (Hkv, B): combine a group's partial summaries (slots w + g, w in
-// [wlo, whi]) per head, one wave per head, then merge (+) with the matched
-// entry's stored AS_{1:p-r}.  Writes out (normalised) and keeps AS_{1:m} for
-// amend.  Each lane owns two output columns.  Latency-bound: the decision and
-// the stored summary are fetched before they are needed.
+// Grid (Hkv * G, B), 1024 threads: one block per (request, query head).  A
+// group's partial summaries (slots w + g, w in [wlo, whi]) can number in the
+// hundreds when few long spans share the workers, so the block's 16 waves
+// split them (wave k takes wlo + k, wlo + k + 16, ...); each wave forms the
+// partials' weights lane-parallel, accumulates its share, and one LDS combine
+// follows.  Then the head is merged (+) with the matched entry's stored
+// AS_{1:p-r}; writes out (normalised) and keeps AS_{1:m} for amend.
+constexpr int REDUCE_WAVES = 16;
+
 template <int G>
-__global__ __launch_bounds__(BLOCK) void reduce_kernel(Shape s, State st, float *__restrict__ out)
+__global__ __launch_bounds__(64 * REDUCE_WAVES) void reduce_kernel(Shape s, State st,
+                                                                   float *__restrict__ out)
 {
     extern __shared__ int s_off[];
-    constexpr int HPW = (G + WAVES - 1) / WAVES;   // heads per wave
-    const int b = blockIdx.y, kvh = blockIdx.x, g = b * s.Hkv + kvh;
+    __shared__ float red[REDUCE_WAVES][D + 4];
+    const int b = blockIdx.y, kvh = blockIdx.x / G, hh = blockIdx.x % G;
+    const int g = b * s.Hkv + kvh;
     const int lane = lane_id(), wv = threadIdx.x >> 6;
-    int slot[HPW];
-#pragma unroll
-    for (int i = 0; i < HPW; ++i) {
-        const int hh = wv + i * WAVES;
-        slot[i] = hh < G ? st.dec_slot[(long)b * s.Hq + kvh * G + hh] : -1;
+    const long idx = (long)b * s.Hq + kvh * G + hh;
+    // the stored summary to merge with, fetched before the plan scan
+    float2 so = make_float2(0.f, 0.f);
+    float Ms = NEG_INF, Ls = 0.f;
+    if (wv == 0) {
+        const int slot = st.dec_slot[idx];
+        if (slot >= 0) {
+            const float *rs = st.ring_s + (idx * s.W + slot) * SUMM;
+            so = *reinterpret_cast<const float2 *>(rs + 2 * lane);
+            Ms = rs[D];
+            Ls = rs[D + 1];
+        }
     }
     const int nG = s.B * s.Hkv;
     build_plan(s, st, s_off);
@@ -1089,52 +1102,72 @@ __global__ __launch_bounds__(BLOCK) void reduce_kernel(Shape s, State st, float 
     const int nW = active_workers(st.n_workers, P);
     const int wlo = page_owner(s_off[g], nW, P);
     const int whi = page_owner((long)s_off[g + 1] - 1, nW, P);
-#pragma unroll
-    for (int i = 0; i < HPW; ++i) {
-        const int hh = wv + i * WAVES;
-        if (hh >= G)
-            break;
-        const long idx = (long)b * s.Hq + kvh * G + hh;
-        const float *rs = st.ring_s + (idx * s.W + (slot[i] >= 0 ? slot[i] : 0)) * SUMM;
-        float2 so = make_float2(0.f, 0.f);
-        float Ms = NEG_INF, Ls = 0.f;
-        if (slot[i] >= 0) {
-            so = *reinterpret_cast<const float2 *>(rs + 2 * lane);
-            Ms = rs[D];
-            Ls = rs[D + 1];
+    const float *part = st.partials + hh * SUMM;
+    const long pstride = (long)G * SUMM;   // one slot
+
+    // this wave's partials: wlo + wv + REDUCE_WAVES * k
+    float Mx = NEG_INF;
+    for (int w = wlo + wv + REDUCE_WAVES * lane; w <= whi; w += REDUCE_WAVES * 64)
+        Mx = fmaxf(Mx, part[((long)w + g) * pstride + D]);
+    Mx = wave_max(Mx);
+    const float base = Mx == NEG_INF ? 0.f : Mx;
+    float Lw = 0.f, a0 = 0.f, a1 = 0.f;
+    for (int w0 = wlo + wv; w0 <= whi; w0 += REDUCE_WAVES * 64) {
+        const int wl = w0 + REDUCE_WAVES * lane;
+        float sc_l = 0.f;
+        if (wl <= whi) {
+            const float *pl = part + ((long)wl + g) * pstride;
+            sc_l = exp2f(pl[D] - base);
+            Lw = fmaf(pl[D + 1], sc_l, Lw);
         }
-        float Mx = NEG_INF;
-        for (int w = wlo + lane; w <= whi; w += 64)
-            Mx = fmaxf(Mx, st.partials[(((long)w + g) * G + hh) * SUMM + D]);
-        Mx = wave_max(Mx);
-        const float base = Mx == NEG_INF ? 0.f : Mx;
-        float a0 = 0.f, a1 = 0.f, Lf = 0.f;
-#pragma unroll 4
-        for (int w = wlo; w <= whi; ++w) {
-            const float *pp = st.partials + (((long)w + g) * G + hh) * SUMM;
-            const float sc = exp2f(pp[D] - base);
-            const float2 v = *reinterpret_cast<const float2 *>(pp + 2 * lane);
-            Lf = fmaf(pp[D + 1], sc, Lf);
+        const int n = min(64, (whi - w0) / REDUCE_WAVES + 1);
+#pragma unroll 8
+        for (int k = 0; k < n; ++k) {
+            const float sc = __shfl(sc_l, k, 64);
+            const float2 v = *reinterpret_cast<const float2 *>(
+                part + ((long)w0 + REDUCE_WAVES * k + g) * pstride + 2 * lane);
             a0 = fmaf(v.x, sc, a0);
             a1 = fmaf(v.y, sc, a1);
         }
-        float o0 = a0 / Lf, o1 = a1 / Lf, Mo = Mx, Lo = Lf;
-        if (Ls > 0.f) {
-            const float Mn = fmaxf(Ms, Mx);
-            const float ca = Ls * exp2f(Ms - Mn), cb = Lf * exp2f(Mx - Mn);
-            const float Ln = ca + cb;
-            o0 = (ca * so.x + cb * o0) / Ln;
-            o1 = (ca * so.y + cb * o1) / Ln;
-            Mo = Mn;
-            Lo = Ln;
-        }
-        *reinterpret_cast<float2 *>(out + idx * D + 2 * lane) = make_float2(o0, o1);
-        float *asf = st.as_full + idx * SUMM;
-        *reinterpret_cast<float2 *>(asf + 2 * lane) = make_float2(o0, o1);
-        if (lane == 0) {
-            asf[D] = Mo;
-            asf[D + 1] = Lo;
-        }
+    }
+    Lw = wave_sum(Lw);
+    *reinterpret_cast<float2 *>(&red[wv][2 * lane]) = make_float2(a0, a1);
+    if (lane == 0) {
+        red[wv][D] = Mx;
+        red[wv][D + 1] = Lw;
+    }
+    __syncthreads();
+    if (wv != 0)
+        return;
+    float Mt = NEG_INF;
+#pragma unroll
+    for (int k = 0; k < REDUCE_WAVES; ++k)
+        Mt = fmaxf(Mt, red[k][D]);
+    const float bt = Mt == NEG_INF ? 0.f : Mt;
+    float c0 = 0.f, c1 = 0.f, Lt = 0.f;
+#pragma unroll
+    for (int k = 0; k < REDUCE_WAVES; ++k) {
+        const float sc = exp2f(red[k][D] - bt);   // 0 for a wave with no partials
+        Lt = fmaf(red[k][D + 1], sc, Lt);
+        c0 = fmaf(red[k][2 * lane], sc, c0);
+        c1 = fmaf(red[k][2 * lane + 1], sc, c1);
+    }
+    float o0 = c0 / Lt, o1 = c1 / Lt, Mo = Mt, Lo = Lt;
+    if (Ls > 0.f) {
+        const float Mn = fmaxf(Ms, Mt);
+        const float ca = Ls * exp2f(Ms - Mn), cb = Lt * exp2f(Mt - Mn);
+        const float Ln = ca + cb;
+        o0 = (ca * so.x + cb * o0) / Ln;
+        o1 = (ca * so.y + cb * o1) / Ln;
+        Mo = Mn;
+        Lo = Ln;
+    }
+    *reinterpret_cast<float2 *>(out + idx * D + 2 * lane) = make_float2(o0, o1);
+    float *asf = st.as_full + idx * SUMM;
+    *reinterpret_cast<float2 *>(asf + 2 * lane) = make_float2(o0, o1);
+    if (lane == 0) {
+        asf[D] = Mo;
+        asf[D + 1] = Lo;
     }
 }
 
@@ -1362,12 +1395,12 @@ hipError_t launch_complete(const Shape &s, const State &st, const KvView &kv, bo
 hipError_t launch_reduce(const Shape &s, const State &st, float *out, hipStream_t stream)
 {
     const size_t lds = plan_lds_bytes(s);
-    const dim3 grid(s.Hkv, s.B);
+    const dim3 grid(s.Hq, s.B), block(64 * REDUCE_WAVES);
     switch (s.G) {
-    case 1: hipLaunchKernelGGL(reduce_kernel<1>, grid, dim3(BLOCK), lds, stream, s, st, out); break;
-    case 2: hipLaunchKernelGGL(reduce_kernel<2>, grid, dim3(BLOCK), lds, stream, s, st, out); break;
-    case 4: hipLaunchKernelGGL(reduce_kernel<4>, grid, dim3(BLOCK), lds, stream, s, st, out); break;
-    case 8: hipLaunchKernelGGL(reduce_kernel<8>, grid, dim3(BLOCK), lds, stream, s, st, out); break;
+    case 1: hipLaunchKernelGGL(reduce_kernel<1>, grid, block, lds, stream, s, st, out); break;
+    case 2: hipLaunchKernelGGL(reduce_kernel<2>, grid, block, lds, stream, s, st, out); break;
+    case 4: hipLaunchKernelGGL(reduce_kernel<4>, grid, block, lds, stream, s, st, out); break;
+    case 8: hipLaunchKernelGGL(reduce_kernel<8>, grid, block, lds, stream, s, st, out); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
