@@ -141,6 +141,92 @@ def speedup_point(name, steps=24, warmup=40):
             "steps": steps, "warmup": warmup}
 
 
+def contgen(args):
+    """Continuous generation: 32 layers x batch 32, 16384-token prompt then
+    generated tokens, K/V appended every step and amend overlapping the next
+    layers on a shared stream.  Steady state is measured at the mid-run context
+    (position 16384 + 8192): the ring remembers only its last W steps, so the
+    window starts there with a fresh ring, warms up, then times the steps."""
+    import torch
+    import kv_reuse_amd as mac
+    from workloads import get_config, kv_logical, page_table, queries, scaled, to_paged
+    base = get_config("contgen")
+    warm, steps = args.warmup if args.warmup >= base.W + 8 else base.W + 8, args.steps
+    total = warm + steps
+    ctx0 = base.C + base.steps // 2
+    w = scaled(base, C=ctx0, steps=total)
+    L = w.layers
+    t0 = time.perf_counter()
+    tab_np = page_table(w)
+    table = torch.as_tensor(tab_np, device="cuda")
+    kcs, vcs, krows, vrows, qs = [], [], [], [], []
+    idx = torch.arange(w.C, w.C + total, device="cuda")
+    for layer in range(L):
+        K, V = kv_logical(w, "cuda", layer=layer)
+        krows.append(K[:, :, idx].permute(2, 0, 1, 3).contiguous())
+        vrows.append(V[:, :, idx].permute(2, 0, 1, 3).contiguous())
+        kcs.append(to_paged(K, tab_np))
+        vcs.append(to_paged(V, tab_np))
+        del K, V
+        qs.append(torch.as_tensor(queries(w, steps=total, layer=layer), device="cuda"))
+    torch.cuda.synchronize()
+    setup = time.perf_counter() - t0
+    seq = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+    pos = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    main = torch.cuda.current_stream()
+    amend = torch.cuda.Stream()
+    res = {}
+    for label, flags in (("mac", 0), ("full", mac.MAC_F_DISABLE_REUSE)):
+        cfg = mac.make_config(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, ring_size=w.W,
+                              band=w.r, tau=w.tau, rope_theta=w.theta, layout=mac.MAC_KV_PAGED,
+                              kv_dtype=mac.MAC_BF16, max_seq_len=w.n_cap, flags=flags)
+        layers = [mac.MacLayer(cfg, main_stream=main, amend_stream=amend) for _ in range(L)]
+        views = [mac.make_kv_view(kcs[i], vcs[i], seq, table, num_pages=kcs[i].shape[0])
+                 for i in range(L)]
+
+        def run(t):
+            pos.fill_(w.C + t)
+            seq.fill_(w.C + t + 1)
+            for i in range(L):
+                layers[i].append_kv(views[i], krows[i][t], vrows[i][t], pos, main)
+                layers[i].decode_step(views[i], qs[i][t], out, None, main)
+
+        for t in range(warm):
+            run(t)
+        torch.cuda.synchronize()
+        h0 = sum(l.stats()["hits"] for l in layers)
+        k0 = sum(l.stats()["kv_tokens_critical"] for l in layers)
+        wall0 = time.perf_counter()
+        for t in range(warm, total):
+            run(t)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        st = [l.stats() for l in layers]
+        hits = sum(x["hits"] for x in st) - h0
+        toks = sum(x["kv_tokens_critical"] for x in st) - k0
+        for l in layers:
+            l.close()
+        res[label] = {"tokens_per_s": w.B * steps / wall, "ms_per_step": wall * 1e3 / steps,
+                      "head_hit_rate": hits / (steps * L * w.B * w.Hq),
+                      "kv_bytes_per_step": toks * 2 * w.d * 2 / steps,
+                      "hbm_gbps": toks * 2 * w.d * 2 / wall / 1e9}
+    line = {
+        "metric": "steady-state tokens/s, continuous generation (32 layers, batch 32, GQA 32q/8kv)",
+        "value": res["mac"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": res["mac"]["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "contgen", "batch": w.B, "layers": L, "context_at_window": ctx0,
+                   "q_heads": w.Hq, "kv_heads": w.Hkv, "ring": w.W, "band": w.r, "tau": w.tau,
+                   "rho": list(base.rho), "jump_every": base.jump_every,
+                   "note": "attention path only (append, match, complete, reduce, async amend); no FFN"},
+        "mac": res["mac"], "full_attention_kernel": res["full"],
+        "speedup_vs_full": res["mac"]["tokens_per_s"] / res["full"]["tokens_per_s"],
+        "setup_s": setup,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def oracle_baseline(w, K, V, qs, n_req, n_steps):
     """fp64 oracle, as it stands, on the first n_req requests for n_steps steps."""
     import oracle
@@ -171,6 +257,9 @@ def main():
     from workloads import get_config, kv_logical, page_table, queries, scaled, to_paged
     mac.load()
     torch.cuda.set_device(0)
+    if args.config == "contgen":
+        contgen(args)
+        return
     w = get_config(args.config)
     if args.r:
         w = scaled(w, r=args.r)

@@ -25,14 +25,14 @@ def _kv_nan(dtype):
 
 class Lockstep:
     def __init__(self, w, flags=0, track=None, device="cuda", oracle_flags=0, tau=None, r=None,
-                 W=None, sync_amend=False):
+                 W=None, sync_amend=False, layer=0, amend_stream=None):
         self.w = w
         self.tau = w.tau if tau is None else tau
         self.r = w.r if r is None else r
         self.W = w.W if W is None else W
         self.dev = device
         B, Hkv, d = w.B, w.Hkv, w.d
-        K, V = kv_logical(w, device)
+        K, V = kv_logical(w, device, layer=layer)
         self.K, self.V = K, V
         self.paged = w.layout == "paged"
         # oracle views: logical rows per (request, KV head); only tracked groups copied
@@ -62,7 +62,7 @@ class Lockstep:
             self.table_np = None
             self.kc, self.vc = logical_k, logical_v
             self.table = None
-        self.q = queries(w)
+        self.q = queries(w, layer=layer)
         self.seq = torch.zeros(B, dtype=torch.int32, device=device)
         self.pos = torch.zeros(B, dtype=torch.int32, device=device)
         fl = flags | mac.MAC_F_RECORD_DEBUG | (mac.MAC_F_SYNC_AMEND if sync_amend else 0)
@@ -72,7 +72,7 @@ class Lockstep:
             layout=mac.MAC_KV_PAGED if self.paged else mac.MAC_KV_CONTIGUOUS,
             kv_dtype=mac.MAC_FP32 if w.kv == "fp32" else mac.MAC_BF16,
             max_seq_len=w.n_cap, flags=fl)
-        self.layer = mac.MacLayer(self.cfg)
+        self.layer = mac.MacLayer(self.cfg, amend_stream=amend_stream)
         self.view = mac.make_kv_view(self.kc, self.vc, self.seq, self.table,
                                      num_pages=self.kc.shape[0] if self.paged else 0)
         self.orc = oracle.Oracle(B, w.Hq, Hkv, d, self.W, self.r, self.tau, w.theta,
@@ -81,6 +81,10 @@ class Lockstep:
         self.stats = []
 
     def step(self, t, seq_lens=None, override=None, compare=True, q=None):
+        return self.finish(self.launch(t, seq_lens, override, q), compare)
+
+    def launch(self, t, seq_lens=None, override=None, q=None):
+        """Append, run the oracle, enqueue the GPU decode step (no synchronisation)."""
         w = self.w
         B = w.B
         seq_h = np.full(B, w.C + t + 1, np.int32) if seq_lens is None else np.asarray(seq_lens,
@@ -103,10 +107,16 @@ class Lockstep:
         ov = torch.as_tensor(forced, device=self.dev)
         qd = torch.as_tensor(q_h, device=self.dev)
         self.layer.decode_step(self.view, qd, self.out, ov)
+        # keep the step's device inputs alive until it has run
+        return {"t": t, "res": res, "flag": flag, "keep": (k_new, v_new, ov, qd)}
+
+    def finish(self, pending, compare=True):
+        """Synchronise and compare the step launched by launch()."""
         torch.cuda.synchronize()
+        res, t = pending["res"], pending["t"]
         p_g, hit_g, rel_g = self.layer.debug_last()
         out_g = self.out.cpu().numpy().astype(np.float64)
-        info = {"t": t, "forced": int(flag.sum()), "hits": int(res["hit"].sum()),
+        info = {"t": t, "forced": int(pending["flag"].sum()), "hits": int(res["hit"].sum()),
                 "p_gpu": p_g, "hit_gpu": hit_g, "res": res, "out_gpu": out_g}
         if compare:
             self.check(res, p_g, hit_g, out_g, t)
