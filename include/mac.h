@@ -61,7 +61,7 @@ enum {
 };
 
 /* Layer configuration (host struct).  head_dim must be 128; Hq % Hkv == 0;
- * 1 <= ring_size <= 64; band >= 1; page_size must be 16.  tau < 0 disables
+ * 1 <= ring_size <= 2048; band >= 1; page_size must be 16.  tau < 0 disables
  * every hit.  sm_scale == 0 selects 1/sqrt(head_dim). */
 typedef struct {
     int32_t batch;          /* B: requests decoded together */

@@ -13,6 +13,7 @@
 //   dec_start  [B][Hq] int32        first key of the head's span
 //   dec_rel    [B][Hq]              relative distance of the nearest entry
 //   grp_start  [B][Hkv] int32       first key of the group's union span (-1 idle)
+//   tile_best  [B][Hq][W/64][3]     W > 64: nearest entry of each 64-slot tile
 //   partials   [NW + B*Hkv][G][SUMM] per-(worker, group) unnormalised summaries
 //   as_full    [B][Hq][SUMM]        AS_{1:m} of this step, input of amend
 //   stats      [MAC_NSTAT + B*Hkv*GRP_NSTAT] uint64
@@ -29,7 +30,8 @@ constexpr int SUMM = D + 4;     // o[D], M, l, 2 pad floats (16-byte rows)
 constexpr int PAGE = 16;        // tokens per page
 constexpr int BLOCK = 256;      // threads per workgroup (4 waves of 64)
 constexpr int WAVES = BLOCK / 64;
-constexpr int MAX_W = 64;       // ring slots per (request, head)
+constexpr int MAX_W = 2048;     // ring slots per (request, head)
+constexpr int TILE_W = 64;      // ring slots a wave scans at once (LDS tile or one tile wave)
 constexpr int MAX_GROUPS = 4096;  // B * Hkv
 constexpr int MIN_PAGES_PER_WORKER = 2;
 
@@ -65,10 +67,14 @@ struct State {
     int32_t *ring_pos, *m_buf, *dec_slot, *dec_p, *dec_start, *grp_start;
     unsigned long long *stats;
     const double *inv_freq;   // [D/2] theta^(-2i/D), fp64
+    float *tile_best;         // W > TILE_W: [B*Hq][ceil(W/TILE_W)][3] per-tile nearest (D, pos, slot)
     int32_t n_workers;        // waves in the complete grid
 };
 
 // Launchers (enqueue only; return the launch status).
+// W > TILE_W: per-tile nearest entries, read by launch_match's kernel.
+hipError_t launch_match_tiles(const Shape &s, const State &st, const KvView &kv,
+                              const int32_t *seq_lens, const float *q_pre, hipStream_t stream);
 hipError_t launch_match(const Shape &s, const State &st, const KvView &kv, const int32_t *seq_lens,
                         const float *q_pre, const int32_t *override_pos, float *out, int waves,
                         hipStream_t stream);

@@ -422,6 +422,86 @@ __device__ __forceinline__ int find_group(const int *off, int nG, long x)
     return lo;
 }
 
+// =========================================================== match tiles
+// Rings longer than one 64-slot tile (the pages' windows of 512-2048 entries,
+// Figure 6, Tables 5 and 7).  Grid (tiles, Hq, B), one wave per tile: the wave
+// streams the tile's 64 pre-RoPE queries (32 KB) as coalesced 1 KB loads, two
+// slots per load (lanes 0-31 and 32-63, four columns each), sums the squared
+// differences over each half with DPP and ds_swizzle, and keeps the nearest
+// entry (smallest distance, newest position, larger slot).  The match kernel
+// then reduces the tiles of each head.
+__device__ __forceinline__ float half_sum(float v)
+{
+    v = row16_sum(v);
+    v += xor_lanes<16>(v);   // stays within each 32-lane half
+    return v;
+}
+
+__global__ __launch_bounds__(64) void match_tiles_kernel(Shape s, State st, KvView kv,
+                                                         const int32_t *__restrict__ seq_lens,
+                                                         const float *__restrict__ q_pre)
+{
+    const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int ntiles = (s.W + TILE_W - 1) / TILE_W;
+    const long idx = (long)b * s.Hq + h;
+    const int lane = lane_id(), half = lane >> 5, c = lane & 31;
+    const int base = tile * TILE_W;
+    const int nslot = min(TILE_W, s.W - base);
+    int m = seq_lens[b] - 1;
+    if (m >= 0 && (m >= kv.max_seq_len || (kv.paged && m / PAGE >= kv.max_pages)))
+        m = -1;
+    const int pos_l = lane < nslot ? st.ring_pos[(long)b * s.W + base + lane] : -1;
+    const float4 qv = reinterpret_cast<const float4 *>(q_pre + idx * D)[c];
+    const float4 *rq = reinterpret_cast<const float4 *>(st.ring_q + (idx * s.W + base) * D);
+    float kd = INFINITY;
+    int kp = INT_MIN, kj = -1;
+    for (int i = 0; i < TILE_W; i += 16) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int sl = min(i + 2 * u + half, nslot - 1);   // clamped: in-bounds re-read
+            v[u] = rq[(long)sl * (D / 4) + c];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int sl = i + 2 * u + half;
+            const float t0 = qv.x - v[u].x, t1 = qv.y - v[u].y, t2 = qv.z - v[u].z,
+                        t3 = qv.w - v[u].w;
+            float d = t0 * t0;
+            d = fmaf(t1, t1, d);
+            d = fmaf(t2, t2, d);
+            d = fmaf(t3, t3, d);
+            d = half_sum(d);
+            const int pos = __shfl(pos_l, sl & 63, 64);
+            const bool valid = sl < nslot && pos >= 0 && pos <= m;
+            const float cd = valid ? d : INFINITY;
+            const int cp = valid ? pos : INT_MIN;
+            const int cj = valid ? base + sl : -1;
+            if (cd < kd || (cd == kd && (cp > kp || (cp == kp && cj > kj)))) {
+                kd = cd;
+                kp = cp;
+                kj = cj;
+            }
+        }
+    }
+    {   // the two halves saw different slots
+        const float d2 = xor_lanes<32>(kd);
+        const int p2 = xor_lanes_i<32>(kp);
+        const int j2 = xor_lanes_i<32>(kj);
+        if (d2 < kd || (d2 == kd && (p2 > kp || (p2 == kp && j2 > kj)))) {
+            kd = d2;
+            kp = p2;
+            kj = j2;
+        }
+    }
+    if (lane == 0) {
+        float *o = st.tile_best + (idx * ntiles + tile) * 3;
+        o[0] = kd;
+        o[1] = __int_as_float(kp);
+        o[2] = __int_as_float(kj);
+    }
+}
+
 // ================================================================== match
 // Grid (Hkv, B), 64 to 256 threads: the block owns one GQA group, its waves
 // take the group's query heads in turn.  Each head's ring tile (W x D fp32) is
@@ -447,8 +527,9 @@ __global__ __launch_bounds__(BLOCK) void match_kernel(Shape s, State st, KvView 
     unsigned long long *gstat = st.stats + MAC_NSTAT + g * GRP_NSTAT;
 
     // lanes per ring slot: a power of two, at most 32 so each lane owns a
-    // whole number of float4 columns (D / L >= 4)
-    int L = 64 / s.W;
+    // whole number of float4 columns (D / L >= 4); one when the ring is tiled
+    const bool tiled = s.W > TILE_W;   // nearest entries come from match_tiles_kernel
+    int L = tiled ? 1 : 64 / s.W;
     while (L & (L - 1))
         L &= L - 1;
     if (L > 32)
@@ -456,6 +537,7 @@ __global__ __launch_bounds__(BLOCK) void match_kernel(Shape s, State st, KvView 
     const int j = lane / L, part = lane % L, span = D / L;
     const int jc = j < s.W ? j : s.W - 1;
     const int lc = lane < s.W ? lane : s.W - 1;
+    const int ntiles = (s.W + TILE_W - 1) / TILE_W;
 
     // ---- loads independent of the position
     const int seq = seq_lens[b];
@@ -488,7 +570,7 @@ __global__ __launch_bounds__(BLOCK) void match_kernel(Shape s, State st, KvView 
             qb = q_pre[idx * D + lane + 64];
             if (ovr)
                 ov = ovr[idx];
-            if (s.reuse) {
+            if (s.reuse && !tiled) {
                 // a batch of 8 loads per lane is in flight before its LDS writes;
                 // indices past the tile are clamped (in-bounds re-reads whose
                 // values are not stored), so the batch stays in registers
@@ -537,6 +619,20 @@ __global__ __launch_bounds__(BLOCK) void match_kernel(Shape s, State st, KvView 
             out[idx * D + lane + 64] = 0.f;
         }
         if (act && s.reuse) {
+            float kd;
+            int kp, kj;
+            if (tiled) {
+                // nearest entry per 64-slot tile, reduced over the head's tiles
+                kd = INFINITY;
+                kp = INT_MIN;
+                kj = -1;
+                if (lane < ntiles) {
+                    const float *tb = st.tile_best + (idx * ntiles + lane) * 3;
+                    kd = tb[0];
+                    kp = __float_as_int(tb[1]);
+                    kj = __float_as_int(tb[2]);
+                }
+            } else {
             // this wave wrote its own tile above; LDS accesses of a wave are ordered
             float dp = 0.f;
             if (j < s.W) {
@@ -558,9 +654,10 @@ __global__ __launch_bounds__(BLOCK) void match_kernel(Shape s, State st, KvView 
             if (L >= 16) dp += xor_lanes<8>(dp);
             if (L >= 32) dp += xor_lanes<16>(dp);
             const bool valid = j < s.W && pos_j >= 0 && pos_j <= m;
-            float kd = valid ? dp : INFINITY;
-            int kp = valid ? pos_j : INT_MIN;
-            int kj = valid ? j : -1;
+            kd = valid ? dp : INFINITY;
+            kp = valid ? pos_j : INT_MIN;
+            kj = valid ? j : -1;
+            }
             // nearest entry: smallest distance, then newest position, then larger slot
 #define MAC_ARGMIN_STEP(OFF)                                                                 \
     {                                                                                       \
@@ -595,14 +692,20 @@ __global__ __launch_bounds__(BLOCK) void match_kernel(Shape s, State st, KvView 
                 slot = -1;
                 p = -1;
                 if (ov >= 0) {
-                    const bool mine = lane < s.W && ov <= m && pos_l == ov;
-                    const unsigned long long bal = __ballot(mine);
-                    if (bal) {
-                        slot = 63 - __clzll(bal);
-                        p = ov;
-                    } else {
-                        my_cnt[3] += 1;
+                    // the largest slot holding position ov, 64 slots at a time
+                    for (int c0 = 0; c0 < s.W; c0 += 64) {
+                        const int sl = c0 + lane;
+                        const int ps = c0 == 0 ? pos_l
+                                               : (sl < s.W ? st.ring_pos[(long)b * s.W + sl] : -1);
+                        const bool mine = sl < s.W && ov <= m && ps == ov;
+                        const unsigned long long bal = __ballot(mine);
+                        if (bal) {
+                            slot = c0 + 63 - __clzll(bal);
+                            p = ov;
+                        }
                     }
+                    if (slot < 0)
+                        my_cnt[3] += 1;
                 }
             }
             if (slot >= 0)
@@ -1367,9 +1470,26 @@ hipError_t launch_amend_t(const Shape &s, const State &st, const KvView &kv, int
 
 bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 
+hipError_t launch_match_tiles(const Shape &s, const State &st, const KvView &kv,
+                              const int32_t *seq_lens, const float *q_pre, hipStream_t stream)
+{
+    const dim3 grid((s.W + TILE_W - 1) / TILE_W, s.Hq, s.B);
+    hipLaunchKernelGGL(match_tiles_kernel, grid, dim3(64), 0, stream, s, st, kv, seq_lens, q_pre);
+    return hipGetLastError();
+}
+
+// LDS a match wave needs: its ring tile and query (none when the ring is scanned
+// by match_tiles_kernel).
+size_t match_lds_per_wave(const Shape &s)
+{
+    return s.W > TILE_W ? 0 : (size_t)(s.W * (D + 4) + D) * sizeof(float);
+}
+
 int match_waves(const Shape &s, size_t max_lds)
 {
-    const size_t per_wave = (size_t)(s.W * (D + 4) + D) * sizeof(float);
+    const size_t per_wave = match_lds_per_wave(s);
+    if (per_wave == 0)
+        return s.G < WAVES ? s.G : WAVES;
     int n = (int)(max_lds / per_wave);
     n = n < 1 ? 1 : (n > WAVES ? WAVES : n);
     return n > s.G ? s.G : n;
@@ -1379,7 +1499,7 @@ hipError_t launch_match(const Shape &s, const State &st, const KvView &kv, const
                         const float *q_pre, const int32_t *override_pos, float *out, int waves,
                         hipStream_t stream)
 {
-    const size_t lds = (size_t)waves * (s.W * (D + 4) + D) * sizeof(float);
+    const size_t lds = (size_t)waves * match_lds_per_wave(s);
     hipLaunchKernelGGL(match_kernel, dim3(s.Hkv, s.B), dim3(64 * waves), lds, stream, s, st, kv,
                        seq_lens, q_pre, override_pos, out);
     return hipGetLastError();

@@ -65,11 +65,11 @@ mac_status fail_hip(mac_handle h, const char *what, hipError_t e)
 
 struct Sizes {
     size_t ring_q, ring_s, ring_pos, qvec, m_buf, dec_i, dec_f, grp, partials, as_full, stats,
-        inv_freq;
+        inv_freq, tiles;
     size_t total() const
     {
         return ring_q + ring_s + ring_pos + 2 * qvec + m_buf + 3 * dec_i + dec_f + grp +
-               partials + as_full + stats + inv_freq;
+               partials + as_full + stats + inv_freq + tiles;
     }
 };
 
@@ -92,6 +92,8 @@ Sizes sizes_for(const mac_config &c, int n_workers)
     s.as_full = round256(B * Hq * mac::SUMM * sizeof(float));
     s.stats = round256(mac::stats_count((long)B * Hkv) * sizeof(unsigned long long));
     s.inv_freq = round256(mac::D / 2 * sizeof(double));
+    const size_t ntiles = (W + mac::TILE_W - 1) / mac::TILE_W;
+    s.tiles = W > (size_t)mac::TILE_W ? round256(B * Hq * ntiles * 3 * sizeof(float)) : 0;
     return s;
 }
 
@@ -118,7 +120,7 @@ mac_status validate(const mac_config *c, std::string &why)
         return MAC_EUNSUPPORTED;
     }
     if (c->ring_size < 1 || c->ring_size > mac::MAX_W) {
-        why = "ring_size must be in [1, 64]";
+        why = "ring_size must be in [1, 2048]";
         return MAC_EINVAL;
     }
     if (c->band < 1) {
@@ -321,6 +323,7 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     h->st.as_full = (float *)take(sz.as_full);
     h->st.stats = (unsigned long long *)take(sz.stats);
     h->st.inv_freq = (const double *)take(sz.inv_freq);
+    h->st.tile_best = sz.tiles ? (float *)take(sz.tiles) : nullptr;
 
     e = hipMemset(base, 0, sz.total());
     if (e != hipSuccess)
@@ -424,6 +427,8 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
         MAC_HIP(h, hipStreamWaitEvent(st, h->ev_amend, 0));
     if (timing)
         MAC_HIP(h, hipEventRecord(h->tm[0], st));
+    if (h->shape.reuse && h->cfg.ring_size > mac::TILE_W)
+        MAC_HIP(h, mac::launch_match_tiles(h->shape, h->st, v, kv->seq_lens, q_pre_rope, st));
     MAC_HIP(h, mac::launch_match(h->shape, h->st, v, kv->seq_lens, q_pre_rope, override_pos, out,
                                  h->match_waves, st));
     if (timing)

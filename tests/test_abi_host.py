@@ -38,6 +38,7 @@ def test_valid_config_passes():
     mac.mac_config_validate(_cfg())
     mac.mac_config_validate(_cfg(layout=mac.MAC_KV_PAGED, kv_dtype=mac.MAC_FP32, ring_size=64,
                                  num_q_heads=32, num_kv_heads=4, tau=-1.0))
+    mac.mac_config_validate(_cfg(ring_size=2048))     # the pages' largest window (Table 7)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -47,7 +48,7 @@ def test_valid_config_passes():
     (dict(head_dim=0), mac.MAC_EINVAL),
     (dict(num_q_heads=32, num_kv_heads=2), mac.MAC_EUNSUPPORTED),   # 16 q heads per KV head
     (dict(ring_size=0), mac.MAC_EINVAL),
-    (dict(ring_size=65), mac.MAC_EINVAL),
+    (dict(ring_size=2049), mac.MAC_EINVAL),
     (dict(band=0), mac.MAC_EINVAL),
     (dict(tau=float("nan")), mac.MAC_EINVAL),
     (dict(rope_theta=0.0), mac.MAC_EINVAL),

@@ -73,6 +73,16 @@ def test_small_window_and_band(gpu_lib):
     _run(w, w.steps)
 
 
+@pytest.mark.parametrize("W,steps", [(65, 90), (100, 150), (512, 140), (2048, 140)])
+def test_large_windows(gpu_lib, W, steps):
+    """Rings longer than one 64-slot tile (the pages' windows reach 2048
+    entries, Table 7): a ragged last tile, wrap-around eviction (W = 65, 100)
+    and several filled tiles next to empty ones (W = 512, 2048)."""
+    w = scaled(get_config("b16_128k"), B=2, C=600, steps=steps, W=W, rho=("const", 0.96))
+    hits, _ = _run(w, w.steps)
+    assert hits > 0
+
+
 def test_disable_reuse_is_full_attention(gpu_lib):
     import kv_reuse_amd as mac
     import oracle

@@ -225,6 +225,22 @@ def test_nearest_bruteforce_with_ties():
             assert j == -1
 
 
+def test_nearest_bruteforce_large_window():
+    """Windows of the pages' operating point (512-2048 entries, Table 7), with
+    stale and future stamps and planted exact duplicates of the best entry."""
+    d = 128
+    for W in (513, 2048):
+        ring_q = RNG.standard_normal((W, d)).astype(np.float32)
+        ring_pos = RNG.integers(-1, 3000, size=W).astype(np.int32)
+        qt = RNG.standard_normal(d).astype(np.float32)
+        m = 2500
+        j0 = _brute_nearest(qt, ring_q, ring_pos, m)
+        for dup in RNG.choice(W, size=3, replace=False):
+            ring_q[dup] = ring_q[j0]
+        j, _, _ = oracle.nearest(qt, ring_q, ring_pos, m)
+        assert j == _brute_nearest(qt, ring_q, ring_pos, m)
+
+
 def test_nearest_duplicate_prefers_newest():
     d = 4
     ring_q = np.zeros((4, d), np.float32)
