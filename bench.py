@@ -8,9 +8,12 @@ shape (no dataset, no model weights).
 A step is one pass of the whole hot path over the batch: append this token's
 K/V rows, match, complete, reduce/merge (the attention phase) and amend on its
 own stream.  The timed region runs K steps after W warm-up steps; inputs are
-resident in HBM before it starts.  Kernel durations come from the library's
-HIP events on the stream each kernel runs on (MAC_F_TIMING); the attention
-phase is match -> reduce, amend excluded, as the pages split it (Table 5).
+resident in HBM before it starts.  The attention phase (match -> reduce, amend
+excluded, as the pages split it in Table 5) is timed per step by two events on
+the decode stream around the decode call.  A second pass over the same steps,
+from a fresh ring, records the library's HIP events around every kernel
+(MAC_F_TIMING) for the per-kernel durations and the roofline of the complete
+kernel.
 
 Prints one JSON line.  `value` is the attention-phase microseconds per decode
 step (lower is better); the line also carries achieved HBM GB/s, tokens/s, the
@@ -30,18 +33,26 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "complete_kernel_b16_128k_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "kv_reuse_amd", "csrc", "mac_kernels.hip")
+# sources the complete kernel is built from: the counters are void once they change
+KERNEL_SRCS = [os.path.join(ROOT, "kv_reuse_amd", "csrc", f)
+               for f in ("complete.hip", "mac_device.h", "mac_internal.h")]
+
+
+def kernel_sha16():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload):
     """HBM bytes per complete launch from the committed rocprofv3 counter
     summary, valid only while the kernel source is the one it was taken on."""
-    import hashlib
     if workload != "b16_128k" or not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
-    return rec["traffic_bytes_per_launch"] if rec.get("kernel_sha16") == sha else None
+    return rec["traffic_bytes_per_launch"] if rec.get("kernel_sha16") == kernel_sha16() else None
 
 
 def parse():
@@ -76,7 +87,7 @@ class Bench:
             batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, ring_size=w.W, band=w.r, tau=w.tau,
             rope_theta=w.theta, layout=mac.MAC_KV_PAGED if paged else mac.MAC_KV_CONTIGUOUS,
             kv_dtype=mac.MAC_FP32 if w.kv == "fp32" else mac.MAC_BF16, max_seq_len=w.n_cap,
-            flags=flags | mac.MAC_F_TIMING)
+            flags=flags)
         self.stream = torch.cuda.current_stream()
         self.layer = mac.MacLayer(self.cfg, main_stream=self.stream)
         self.view = mac.make_kv_view(self.kc, self.vc, self.seq, self.table,
@@ -84,7 +95,12 @@ class Bench:
         self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
 
     def step(self, t, q, k_new, v_new, scrub=None):
+        """One decode step.  Returns the counters (synchronises) with the last
+        step's kernel times (MAC_F_TIMING) and "span_us": the decode call's work
+        on the main stream (match -> reduce) between two stream events, with
+        nothing recorded between its kernels."""
         w = self.w
+        torch = self.torch
         if scrub is not None:
             # read 1 GiB: evicts the KV cache from L2 and the Infinity Cache
             # without leaving dirty lines for the timed kernels to write back
@@ -92,15 +108,21 @@ class Bench:
         self.pos.fill_(w.C + t)
         self.seq.fill_(w.C + t + 1)
         self.layer.append_kv(self.view, k_new, v_new, self.pos, self.stream)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
         self.layer.decode_step(self.view, q, self.out, None, self.stream)
-        return self.layer.stats()          # synchronises; last step's kernel times
+        e1.record(self.stream)
+        st = self.layer.stats()            # synchronises; last step's kernel times
+        st["span_us"] = e0.elapsed_time(e1) * 1e3
+        return st
 
 
 def speedup_point(name, steps=24, warmup=40):
     """MAC attention phase vs the in-house full-attention kernel on one workload,
     with a 1 GiB scrub read before every step (the KV of small contexts fits in
-    the 256 MB Infinity Cache).  Kernel times are HIP events, so the scrub is not
-    in them."""
+    the 256 MB Infinity Cache).  The attention phase is timed by stream events
+    around the decode call, so the scrub is not in it."""
     import torch
     import kv_reuse_amd as mac
     from workloads import get_config, kv_logical, page_table, queries, to_paged
@@ -122,22 +144,19 @@ def speedup_point(name, steps=24, warmup=40):
     res = {}
     for label, flags in (("mac", 0), ("full", mac.MAC_F_DISABLE_REUSE)):
         bn = Bench(w, flags, kc, vc, paged, table)
-        att, comp, hits = [], [], []
+        att, hits = [], []
         prev = None
         for t in range(total):
             st = bn.step(t, q_dev[t], k_rows[t], v_rows[t], scrub)
             if t >= warmup:
-                att.append(st["last_us_attention"])
-                comp.append(st["last_us_complete"])
+                att.append(st["span_us"])
                 hits.append(st["hits"] - prev["hits"])
             prev = st
         bn.layer.close()
-        res[label] = (float(np.mean(att)), float(np.mean(comp)),
-                      float(np.sum(hits)) / (len(hits) * w.B * w.Hq))
+        res[label] = (float(np.mean(att)), float(np.sum(hits)) / (len(hits) * w.B * w.Hq))
     return {"workload": name, "context": w.C, "batch": w.B,
-            "mac_attention_us": res["mac"][0], "mac_complete_us": res["mac"][1],
-            "full_attention_us": res["full"][0], "full_complete_us": res["full"][1],
-            "head_hit_rate": res["mac"][2], "speedup": res["full"][0] / res["mac"][0],
+            "mac_attention_us": res["mac"][0], "full_attention_us": res["full"][0],
+            "head_hit_rate": res["mac"][1], "speedup": res["full"][0] / res["mac"][0],
             "steps": steps, "warmup": warmup}
 
 
@@ -298,21 +317,19 @@ def main():
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
 
+    # pass 1 (the timed region): the attention phase between two stream events
+    # per step, no events between the kernels
     bench = Bench(w, 0, kc, vc, paged, table)
     for t in range(args.warmup):
         bench.step(t, q_dev[t], k_rows[t], v_rows[t])
     st0 = bench.layer.stats()
     torch.cuda.synchronize()
-    att, comp, match, red, amend, hits, toks = [], [], [], [], [], [], []
+    att, hits, toks = [], [], []
     prev = st0
     wall0 = time.perf_counter()
     for t in range(args.warmup, total):
         st = bench.step(t, q_dev[t], k_rows[t], v_rows[t])
-        att.append(st["last_us_attention"])
-        comp.append(st["last_us_complete"])
-        match.append(st["last_us_match"])
-        red.append(st["last_us_reduce"])
-        amend.append(st["last_us_amend"])
+        att.append(st["span_us"])
         hits.append(st["hits"] - prev["hits"])
         toks.append(st["kv_tokens_critical"] - prev["kv_tokens_critical"])
         prev = st
@@ -320,6 +337,24 @@ def main():
     wall = time.perf_counter() - wall0
     st1 = bench.layer.stats()
     bench.layer.close()
+
+    # pass 2: the same steps from a fresh ring (same decisions, same bytes)
+    # with the library's HIP events around every kernel (MAC_F_TIMING)
+    kb = Bench(w, mac.MAC_F_TIMING, kc, vc, paged, table)
+    comp, match, red, amend, att_ev, toks2 = [], [], [], [], [], []
+    prev = None
+    for t in range(total):
+        st = kb.step(t, q_dev[t], k_rows[t], v_rows[t])
+        if t >= args.warmup:
+            comp.append(st["last_us_complete"])
+            match.append(st["last_us_match"])
+            red.append(st["last_us_reduce"])
+            amend.append(st["last_us_amend"])
+            att_ev.append(st["last_us_attention"])
+            toks2.append(st["kv_tokens_critical"] - prev["kv_tokens_critical"])
+        prev = st
+    kb.layer.close()
+    assert toks2 == toks, "the instrumented pass streamed different bytes"
 
     row_bytes = 2 * w.d * w.kv_elem_bytes                   # one key row + one value row
     kv_bytes = np.array(toks, np.float64) * row_bytes       # per step, per complete launch
@@ -334,18 +369,42 @@ def main():
     # in-house full-attention kernel (every head misses) on the same cache
     base = None
     if not args.no_baseline_kernel:
-        fb = Bench(w, mac.MAC_F_DISABLE_REUSE, kc, vc, paged, table)
         fa, fc = [], []
-        for t in range(min(total, 4 + 16)):
-            st = fb.step(t, q_dev[t], k_rows[t], v_rows[t])
-            if t >= 4:
-                fa.append(st["last_us_attention"])
-                fc.append(st["last_us_complete"])
+        for fl in (mac.MAC_F_DISABLE_REUSE, mac.MAC_F_DISABLE_REUSE | mac.MAC_F_TIMING):
+            fb = Bench(w, fl, kc, vc, paged, table)
+            for t in range(min(total, 4 + 16)):
+                st = fb.step(t, q_dev[t], k_rows[t], v_rows[t])
+                if t >= 4:
+                    if fl & mac.MAC_F_TIMING:
+                        fc.append(st["last_us_complete"])
+                    else:
+                        fa.append(st["span_us"])
+            fb.layer.close()
         full_tok = (w.C + total) * w.B * w.Hkv
         base = {"attention_us": float(np.mean(fa)), "complete_us": float(np.mean(fc)),
                 "hbm_gbps": full_tok * row_bytes / (float(np.mean(fc)) * 1e-6) / 1e9,
                 "speedup_vs_full": float(np.mean(fa)) / att_us}
-        fb.layer.close()
+
+    # the reuse path's own speedup at this context: the same cache, queries
+    # with rho = 0.97 (nearly every head hits its previous step)
+    allhit = None
+    if not args.no_baseline_kernel and args.config == "b16_128k" and not args.set and not args.r:
+        wa = scaled(w, rho=("const", 0.97))
+        qa = torch.as_tensor(queries(wa, steps=total), device="cuda")
+        ab = Bench(wa, 0, kc, vc, paged, table)
+        aa, ah, at, prev = [], [], [], None
+        for t in range(min(total, 4 + 16)):
+            st = ab.step(t, qa[t], k_rows[t], v_rows[t])
+            if t >= 4:
+                aa.append(st["span_us"])
+                ah.append(st["hits"] - prev["hits"])
+                at.append(st["kv_tokens_critical"] - prev["kv_tokens_critical"])
+            prev = st
+        ab.layer.close()
+        allhit = {"rho": 0.97, "attention_us": float(np.mean(aa)),
+                  "head_hit_rate": float(np.sum(ah)) / (heads * len(ah)),
+                  "kv_bytes_per_step": float(np.mean(at)) * row_bytes,
+                  "speedup_vs_full": (base["attention_us"] / float(np.mean(aa))) if base else None}
 
     point_32k = None
     if not args.no_32k and args.config == "b16_128k" and not args.set and not args.r:
@@ -395,12 +454,15 @@ def main():
         "kv_bytes_per_step": float(np.mean(kv_bytes)),
         "head_hit_rate": float(np.sum(hits)) / (heads * len(hits)),
         "kernel_us": {"match": float(np.mean(match)), "complete": comp_us,
-                      "reduce": float(np.mean(red)), "amend": float(np.mean(amend))},
+                      "reduce": float(np.mean(red)), "amend": float(np.mean(amend)),
+                      "attention_with_kernel_events": float(np.mean(att_ev))},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(w.name),
-                     "kernel": "complete_kernel", "bytes_per_launch": float(np.mean(comp_bytes))},
+                     "kernel": "complete_mfma_kernel" if w.kv == "bf16" else "complete_kernel",
+                     "kernel_sha16": kernel_sha16(), "bytes_per_launch": float(np.mean(comp_bytes))},
         "attention_phase_bytes_per_step": att_bytes,
         "full_attention_kernel": base,
+        "allhit_128k": allhit,
         "speedup_32k": point_32k,
         "cpu_baseline": cpu,
         "setup_s": t_setup,

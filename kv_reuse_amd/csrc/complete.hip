@@ -1,0 +1,480 @@
+// complete.hip -- complete step of the MAC-Attention decode (Figure 2 (b)):
+// split-KV flash-decode over each GQA group's union span, equal page shares
+// per wave (the load-balanced plan of Figure 3 (b), built on the device).
+#include "mac_device.h"
+
+namespace mac {
+namespace {
+
+// =============================================================== complete
+// Persistent grid of independent wave workers.  Every block rebuilds the
+// plan (a scan over B*Hkv group spans) in LDS; the step's pages, group after
+// group, are split into equal contiguous shares, one per active wave.  A
+// worker writes one partial summary per group it touches, into slot
+// (worker + group), which is unique along the flattened list.
+template <typename T, int G>
+__global__ __launch_bounds__(BLOCK) void complete_kernel(Shape s, State st, KvView kv)
+{
+    extern __shared__ int s_off[];
+    using K = Kv<T>;
+    const int nG = s.B * s.Hkv;
+    build_plan(s, st, s_off);
+    const int P = s_off[nG];
+    if (P == 0)
+        return;
+    const int nW = active_workers(st.n_workers, P);
+    if (blockIdx.x == 0)
+        publish_plan(s, st, s_off, nW);
+    const int w = blockIdx.x * WAVES + (threadIdx.x >> 6);
+    if (w >= nW)
+        return;
+    long x = (long)w * P / nW;
+    const long x1 = (long)(w + 1) * P / nW;
+    int g = find_group(s_off, nG, x);
+    while (x < x1) {
+        while (s_off[g + 1] <= x)
+            ++g;
+        const long gend = min((long)s_off[g + 1], x1);
+        const int b = g / s.Hkv, kvh = g % s.Hkv;
+        const int m = st.m_buf[b];
+        const int first_page = st.grp_start[g] / PAGE;
+        int hs[G];
+        int hmax = 0;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            hs[h] = st.dec_start[(long)b * s.Hq + kvh * G + h];
+            hmax = max(hmax, hs[h]);
+        }
+        float q[G][K::E];
+        load_group_queries<T, G>(s, st, b, kvh, q);
+        WaveAcc<G, K::E> acc;
+        acc.init();
+
+        PageRegs<T> r0, r1;
+        int page = first_page + (int)(x - s_off[g]);
+        const int last = first_page + (int)(gend - s_off[g]) - 1;
+        load_page<T>(r0, kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page, &st.stats[ST_BAD_INPUT]),
+                     kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page, &st.stats[ST_BAD_INPUT]));
+        while (true) {
+            if (page + 1 <= last)
+                load_page<T>(r1,
+                             kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page + 1, &st.stats[ST_BAD_INPUT]),
+                             kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page + 1, &st.stats[ST_BAD_INPUT]));
+            {
+                const int tok0 = page * PAGE;
+                compute_page<T, G>(r0, tok0, m, hs, tok0 < hmax || tok0 + PAGE - 1 > m, q, acc);
+            }
+            if (++page > last)
+                break;
+            if (page + 1 <= last)
+                load_page<T>(r0,
+                             kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page + 1, &st.stats[ST_BAD_INPUT]),
+                             kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page + 1, &st.stats[ST_BAD_INPUT]));
+            {
+                const int tok0 = page * PAGE;
+                compute_page<T, G>(r1, tok0, m, hs, tok0 < hmax || tok0 + PAGE - 1 > m, q, acc);
+            }
+            if (++page > last)
+                break;
+        }
+        store_wave_summary<T, G>(acc, st.partials + ((long)w + g) * G * SUMM);
+        x = gend;
+    }
+}
+
+// ========================================================== complete (MFMA)
+// bf16 cache, G <= 4 query heads per KV head.  Q.K^T runs on the matrix cores:
+// v_mfma_f32_16x16x32_bf16 with the page's 16 tokens as the 16 columns of B
+// (lane l feeds token l%16, columns 32s + 8(l/16) .. +7 at k-step s, straight
+// from its 16-byte K load) and the group's queries as the rows of A,
+// replicated so that row i holds head i % G: every lane receives the logits of
+// all G heads for token l%16.  A carries the query split into two bf16 parts
+// (hi + lo), so the logits keep ~16 mantissa bits of the fp32 query.
+// P.V stays on the vector units with V loaded as contiguous 1 KB wave loads
+// (lane (r, c) = (l/16, l%16) holds token 4s + r, columns 8c .. 8c+7); each
+// token's probabilities reach the lanes that hold its V row through a
+// 256-byte per-wave LDS exchange.  The softmax reference max is uniform over
+// the wave (one per head) and only moves when a logit exceeds it by more than
+// LAZY_RESCALE (log2 units): exp2(s - M) <= 256 is accumulated as is, and the
+// rescale, when it happens, is exact.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr float LAZY_RESCALE = 8.f;
+
+struct MPage {
+    uint4 k[4], v[4];
+};
+
+// K arrives in the MFMA layout: one wave load covers 64 of the 128 bytes of 16
+// rows, so every cache line is shared by two consecutive loads and is read
+// with the default policy (a streaming hint makes the second half refetch).
+// V arrives as contiguous 1 KB wave loads of whole lines and is streamed.
+__device__ __forceinline__ void load_mpage(MPage &r, const uint16_t *kp, const uint16_t *vp)
+{
+    const int lane = lane_id(), t = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        r.k[s] = *reinterpret_cast<const uint4 *>(kp + t * D + 32 * s + 8 * q);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        r.v[s] = load_stream(vp + (4 * s + q) * D + 8 * t);
+}
+
+// HPL: heads whose logits one lane receives from the MFMA (4 row groups of 4
+// rows; row i holds head i % G).  For G = 8 the lanes of row groups 0 and 2
+// hold heads 0..3 and those of row groups 1 and 3 hold heads 4..7.
+template <int G>
+struct MAcc {
+    static constexpr int HPL = G < 4 ? G : 4;
+    float M[G];           // wave-uniform reference max per head (log2 units)
+    float Ml[HPL];        // M of this lane's own heads (M[v], or M[4 + v] for G = 8)
+    float L[HPL];         // normaliser of this lane's heads over this lane's tokens
+    float acc[G][8];      // P.V over this lane's V rows and 8 columns
+};
+
+// Per-lane choice between two registers by a lane mask.  Written as the
+// instruction itself: a C select between two elements of a register array is
+// folded by the compiler into an indexed access, which moves the array to
+// scratch memory.
+__device__ __forceinline__ float lane_pick(unsigned long long mask, float if_set, float if_clear)
+{
+    float r;
+    asm volatile("v_cndmask_b32_e64 %0, %1, %2, %3"
+                 : "=v"(r)
+                 : "v"(if_clear), "v"(if_set), "s"(mask));
+    return r;
+}
+
+__device__ __forceinline__ int lane_pick(unsigned long long mask, int if_set, int if_clear)
+{
+    return __float_as_int(lane_pick(mask, __int_as_float(if_set), __int_as_float(if_clear)));
+}
+
+// hsl: first key of each of this lane's own heads' spans.  half_mask: lanes
+// holding heads 4..7 (G = 8; zero otherwise).
+template <int G>
+__device__ __forceinline__ void compute_mpage(const MPage &r, const uint4 *qa, float4 *px,
+                                              int tok0, int m, const int (&hsl)[MAcc<G>::HPL],
+                                              bool masked, unsigned long long half_mask,
+                                              MAcc<G> &st)
+{
+    constexpr int HPL = MAcc<G>::HPL;
+    constexpr int NPX = G > 4 ? 2 : 1;   // float4 of probabilities per token
+    const int lane = lane_id(), t = lane & 15, q = lane >> 4;
+    const int half = G > 4 ? (q & 1) : 0;   // which four heads this lane holds
+    floatx4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const bf16x8 kb = __builtin_bit_cast(bf16x8, r.k[s]);
+        const uint4 ahi = qa[(2 * s) * 64 + lane], alo = qa[(2 * s + 1) * 64 + lane];
+        S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ahi), kb, S0, 0,
+                                                     0, 0);
+        S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, alo), kb, S1, 0,
+                                                     0, 0);
+    }
+    float lg[HPL];
+#pragma unroll
+    for (int v = 0; v < HPL; ++v)
+        lg[v] = S0[v] + S1[v];
+    if (masked) {
+        const int tok = tok0 + t;
+#pragma unroll
+        for (int v = 0; v < HPL; ++v)
+            if (tok < hsl[v] || tok > m)
+                lg[v] = NEG_INF;
+    }
+    bool need = false;
+#pragma unroll
+    for (int v = 0; v < HPL; ++v)
+        need |= lg[v] > st.Ml[v] + LAZY_RESCALE;
+    if (__any(need)) {
+        float alpha[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const bool mine = G > 4 ? (h / 4 == half) : true;
+            const float cand = mine ? lg[h % HPL] : NEG_INF;
+            const float mn = fmaxf(st.M[h], wave_max(cand));
+            alpha[h] = mn == st.M[h] ? 1.f : exp2f(st.M[h] - mn);   // 0 from -inf
+            st.M[h] = mn;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                st.acc[h][e] *= alpha[h];
+        }
+#pragma unroll
+        for (int v = 0; v < HPL; ++v) {
+            if constexpr (G > 4) {
+                st.L[v] *= lane_pick(half_mask, alpha[4 + v], alpha[v]);
+                st.Ml[v] = lane_pick(half_mask, st.M[4 + v], st.M[v]);
+            } else {
+                st.L[v] *= alpha[v];
+                st.Ml[v] = st.M[v];
+            }
+        }
+    }
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < HPL; ++v) {
+        p[v] = lg[v] == NEG_INF ? 0.f : exp2f(lg[v] - st.Ml[v]);
+        st.L[v] += p[v];
+    }
+    // token t's probabilities -> the lanes holding V rows of token t
+    if (q < NPX)
+        px[t * NPX + q] = make_float4(p[0], p[1], p[2], p[3]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float pt[4][4 * NPX];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int k = 0; k < NPX; ++k) {
+            const float4 x = px[(4 * s + q) * NPX + k];
+            pt[s][4 * k + 0] = x.x;
+            pt[s][4 * k + 1] = x.y;
+            pt[s][4 * k + 2] = x.z;
+            pt[s][4 * k + 3] = x.w;
+        }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        float vf[8];
+        to_f32(r.v[s], vf);
+        if (masked && tok0 + 4 * s + q > m) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                vf[e] = 0.f;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                st.acc[h][e] = fmaf(pt[s][h], vf[e], st.acc[h][e]);
+    }
+}
+
+// Sum over the four row groups (tokens 4s + r) and, for L, over the 16 token
+// lanes of a row holding the head; the first row stores columns 8c .. 8c+7.
+template <int G>
+__device__ __forceinline__ void store_msummary(MAcc<G> &st, float *dst)
+{
+    constexpr int HPL = MAcc<G>::HPL;
+    const int lane = lane_id(), t = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float a[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a[e] = st.acc[h][e];
+            a[e] += xor_lanes<16>(a[e]);
+            a[e] += xor_lanes<32>(a[e]);
+        }
+        if (q == 0) {
+            float *o = dst + h * SUMM + 8 * t;
+            *reinterpret_cast<float4 *>(o) = make_float4(a[0], a[1], a[2], a[3]);
+            *reinterpret_cast<float4 *>(o + 4) = make_float4(a[4], a[5], a[6], a[7]);
+        }
+        if (lane == 0)
+            dst[h * SUMM + D] = st.M[h];
+    }
+#pragma unroll
+    for (int v = 0; v < HPL; ++v) {
+        const float Lt = row16_sum(st.L[v]);
+        if (lane == 0)
+            dst[v * SUMM + D + 1] = Lt;
+        if (G > 4 && lane == 16)
+            dst[((4 + v) % G) * SUMM + D + 1] = Lt;
+    }
+}
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// A operands of this lane (row l%16 -> head (l%16) % G, k-group l/16) for the
+// 4 k-steps, hi and lo parts interleaved: qa[2s] = hi, qa[2s+1] = lo.  hi
+// keeps the top 16 bits of the scaled fp32 query; lo = bf16(q - hi), where
+// q - hi is exact in fp32.
+template <int G>
+__device__ __forceinline__ void build_qa(const Shape &s, const State &st, int b, int kvh,
+                                         uint4 *qa)
+{
+    const int lane = lane_id(), row = lane & 15, q = lane >> 4;
+    const float *src = st.q_rot + ((long)b * s.Hq + kvh * G + row % G) * D;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = src[32 * k + 8 * q + e] * s.scale_log2;
+            hi[e] = __float_as_uint(x) >> 16;
+            lo[e] = bf16_rne_bits(x - __uint_as_float(hi[e] << 16));
+        }
+        qa[2 * k] = make_uint4(hi[0] | hi[1] << 16, hi[2] | hi[3] << 16, hi[4] | hi[5] << 16,
+                               hi[6] | hi[7] << 16);
+        qa[2 * k + 1] = make_uint4(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16,
+                                   lo[6] | lo[7] << 16);
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Shape s, State st,
+                                                                     KvView kv)
+{
+    extern __shared__ int s_off[];
+    __shared__ uint4 qlds[WAVES][8][64];   // per wave: 8 A-operand registers x 64 lanes
+    __shared__ float4 plds[WAVES][32];     // per wave: probabilities of the page's 16 tokens
+    const int nG = s.B * s.Hkv;
+    build_plan(s, st, s_off);
+    const int P = s_off[nG];
+    if (P == 0)
+        return;
+    const int nW = active_workers(st.n_workers, P);
+    if (blockIdx.x == 0)
+        publish_plan(s, st, s_off, nW);
+    const int wv = threadIdx.x >> 6, lane = lane_id();
+    const int w = blockIdx.x * WAVES + wv;
+    if (w >= nW)
+        return;
+    long x = (long)w * P / nW;
+    const long x1 = (long)(w + 1) * P / nW;
+    int g = find_group(s_off, nG, x);
+    unsigned long long *bad = &st.stats[ST_BAD_INPUT];
+    const uint16_t *kb = reinterpret_cast<const uint16_t *>(kv.k);
+    const uint16_t *vb = reinterpret_cast<const uint16_t *>(kv.v);
+    while (x < x1) {
+        while (s_off[g + 1] <= x)
+            ++g;
+        const long gend = min((long)s_off[g + 1], x1);
+        const int b = g / s.Hkv, kvh = g % s.Hkv;
+        const int m = st.m_buf[b];
+        const int first_page = st.grp_start[g] / PAGE;
+        constexpr int HPL = MAcc<G>::HPL;
+        const unsigned long long half_mask = G > 4 ? __ballot((lane >> 4) & 1) : 0ULL;
+        int hs[G];
+        int hmax = 0;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            hs[h] = st.dec_start[(long)b * s.Hq + kvh * G + h];
+            hmax = max(hmax, hs[h]);
+        }
+        int hsl[HPL];
+#pragma unroll
+        for (int v = 0; v < HPL; ++v) {
+            if constexpr (G > 4)
+                hsl[v] = lane_pick(half_mask, hs[(4 + v) % G], hs[v]);
+            else
+                hsl[v] = hs[v];
+        }
+        {
+            uint4 qa[8];
+            build_qa<G>(s, st, b, kvh, qa);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                qlds[wv][i][lane] = qa[i];
+        }
+        MAcc<G> acc;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            acc.M[h] = NEG_INF;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc.acc[h][e] = 0.f;
+        }
+#pragma unroll
+        for (int v = 0; v < HPL; ++v) {
+            acc.L[v] = 0.f;
+            acc.Ml[v] = NEG_INF;
+        }
+        int page = first_page + (int)(x - s_off[g]);
+        const int last = first_page + (int)(gend - s_off[g]) - 1;
+        // one page in flight per wave: at <= 168 VGPRs (G <= 4) three waves
+        // share each SIMD, which hides the load latency better than double
+        // buffering at two waves per SIMD (measured)
+        MPage r0;
+        while (true) {
+            load_mpage(r0, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad),
+                       kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page, bad));
+            const int tok0 = page * PAGE;
+            compute_mpage<G>(r0, &qlds[wv][0][0], plds[wv], tok0, m, hsl,
+                             tok0 < hmax || tok0 + PAGE - 1 > m, half_mask, acc);
+            if (++page > last)
+                break;
+        }
+        store_msummary<G>(acc, st.partials + ((long)w + g) * G * SUMM);
+        x = gend;
+    }
+}
+
+template <typename T>
+hipError_t launch_complete_t(const Shape &s, const State &st, const KvView &kv, int n_blocks,
+                             hipStream_t stream)
+{
+    const size_t lds = plan_lds_bytes(s);
+    if constexpr (std::is_same<T, uint16_t>::value) {
+        switch (s.G) {
+        case 1: hipLaunchKernelGGL(complete_mfma_kernel<1>, dim3(n_blocks), dim3(BLOCK), lds,
+                                   stream, s, st, kv); break;
+        case 2: hipLaunchKernelGGL(complete_mfma_kernel<2>, dim3(n_blocks), dim3(BLOCK), lds,
+                                   stream, s, st, kv); break;
+        case 4: hipLaunchKernelGGL(complete_mfma_kernel<4>, dim3(n_blocks), dim3(BLOCK), lds,
+                                   stream, s, st, kv); break;
+        default: hipLaunchKernelGGL(complete_mfma_kernel<8>, dim3(n_blocks), dim3(BLOCK), lds,
+                                    stream, s, st, kv); break;
+        }
+        return hipGetLastError();
+    } else {
+        switch (s.G) {
+#define MAC_CASE(GG)                                                                          \
+    case GG:                                                                                  \
+        hipLaunchKernelGGL((complete_kernel<T, GG>), dim3(n_blocks), dim3(BLOCK), lds, stream, \
+                           s, st, kv);                                                        \
+        break;
+            MAC_CASE(1)
+            MAC_CASE(2)
+            MAC_CASE(4)
+            MAC_CASE(8)
+#undef MAC_CASE
+        default:
+            return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+}
+
+}  // namespace
+
+bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
+
+hipError_t launch_complete(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
+                           int n_blocks, hipStream_t stream)
+{
+    return kv_fp32 ? launch_complete_t<float>(s, st, kv, n_blocks, stream)
+                   : launch_complete_t<uint16_t>(s, st, kv, n_blocks, stream);
+}
+
+int complete_blocks_per_cu(bool kv_fp32, int G, size_t lds)
+{
+    int n = 0;
+    hipError_t e = hipErrorInvalidValue;
+#define MAC_OCC(TT, GG)                                                                        \
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_kernel<TT, GG>, BLOCK, lds)
+    if (kv_fp32) {
+        if (G == 1) MAC_OCC(float, 1); else if (G == 2) MAC_OCC(float, 2);
+        else if (G == 4) MAC_OCC(float, 4); else MAC_OCC(float, 8);
+    } else {
+        if (G == 1)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_mfma_kernel<1>, BLOCK, lds);
+        else if (G == 2)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_mfma_kernel<2>, BLOCK, lds);
+        else if (G == 4)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_mfma_kernel<4>, BLOCK, lds);
+        else
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_mfma_kernel<8>, BLOCK, lds);
+    }
+#undef MAC_OCC
+    return (e == hipSuccess && n > 0) ? n : 1;
+}
+
+}  // namespace mac

@@ -1,0 +1,439 @@
+// mac_device.h -- device helpers shared by the gfx950 kernels of the
+// MAC-Attention decode step (match.hip, complete.hip, reduce.hip, amend.hip):
+// wave64 lane exchanges (DPP, ds_swizzle), key/value row loads, the VALU
+// flash-decode wave worker and the device-side work plan.
+//
+// Key/value rows stream as 16-byte loads: for bf16 a row of 128 elements is
+// 16 lanes, a wave load covers 4 tokens and a 16-token page is 4 loads of K
+// and 4 of V; fp32 rows take 32 lanes.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <type_traits>
+
+#include "mac_internal.h"
+
+namespace mac {
+namespace {
+
+constexpr float NEG_INF = -INFINITY;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ------------------------------------------------------------ lane exchange
+// DPP for exchanges inside a quad, ds_swizzle (bit mode) inside 32 lanes,
+// ds_bpermute across the two halves.
+template <int OFF>
+__device__ __forceinline__ int xor_lanes_i(int v)
+{
+    static_assert(OFF > 0 && OFF < 64 && (OFF & (OFF - 1)) == 0, "power of two");
+    if constexpr (OFF == 1)
+        return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+    else if constexpr (OFF == 2)
+        return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+    else if constexpr (OFF < 32)
+        return __builtin_amdgcn_ds_swizzle(v, (OFF << 10) | 0x1F);   // xor mask, and 0x1F
+    else
+        return __shfl_xor(v, 32, 64);
+}
+
+template <int OFF>
+__device__ __forceinline__ float xor_lanes(float v)
+{
+    return __int_as_float(xor_lanes_i<OFF>(__float_as_int(v)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each 16-lane row: after the two quad exchanges every quad is
+// uniform, so the half mirror and the full mirror finish the reduction.
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);   // row_half_mirror
+    v += dpp_f<0x140>(v);   // row_mirror
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = row16_sum(v);
+    v += xor_lanes<16>(v);
+    v += xor_lanes<32>(v);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = fmaxf(v, xor_lanes<1>(v));
+    v = fmaxf(v, xor_lanes<2>(v));
+    v = fmaxf(v, xor_lanes<4>(v));
+    v = fmaxf(v, xor_lanes<8>(v));
+    v = fmaxf(v, xor_lanes<16>(v));
+    v = fmaxf(v, xor_lanes<32>(v));
+    return v;
+}
+
+// ------------------------------------------------------- key/value element
+template <typename T>
+struct Kv;
+template <>
+struct Kv<uint16_t> {           // bf16 bit patterns
+    static constexpr int E = 8;     // elements per 16-byte lane load
+    static constexpr int LPR = 16;  // lanes per 128-element row
+    static constexpr int RPL = 4;   // rows (tokens) per wave load
+    static constexpr int LPP = 4;   // wave loads per 16-token page
+};
+template <>
+struct Kv<float> {
+    static constexpr int E = 4;
+    static constexpr int LPR = 32;
+    static constexpr int RPL = 2;
+    static constexpr int LPP = 8;
+};
+
+__device__ __forceinline__ void to_f32(const uint4 &w, float (&f)[8])
+{
+    f[0] = __uint_as_float(w.x << 16);
+    f[1] = __uint_as_float(w.x & 0xffff0000u);
+    f[2] = __uint_as_float(w.y << 16);
+    f[3] = __uint_as_float(w.y & 0xffff0000u);
+    f[4] = __uint_as_float(w.z << 16);
+    f[5] = __uint_as_float(w.z & 0xffff0000u);
+    f[6] = __uint_as_float(w.w << 16);
+    f[7] = __uint_as_float(w.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ void to_f32(const uint4 &w, float (&f)[4])
+{
+    f[0] = __uint_as_float(w.x);
+    f[1] = __uint_as_float(w.y);
+    f[2] = __uint_as_float(w.z);
+    f[3] = __uint_as_float(w.w);
+}
+
+template <typename T>
+__device__ __forceinline__ float row_sum(float v)
+{
+    v = row16_sum(v);
+    if constexpr (Kv<T>::LPR == 32)
+        v += xor_lanes<16>(v);
+    return v;
+}
+
+// Address of the 16 x D block holding tokens [16*page, 16*page+16) of
+// (request b, KV head kvh).  A page id outside the pool is replaced by page 0
+// and counted, so a corrupt table never reads outside the cache.
+template <typename T>
+__device__ __forceinline__ const T *kv_page(const KvView &kv, const void *base, int b, int kvh,
+                                            int Hkv, int page, unsigned long long *bad)
+{
+    long off;
+    if (kv.paged) {
+        int pid = kv.page_table[(long)b * kv.max_pages + page];
+        if ((unsigned)pid >= (unsigned)kv.num_pages) {
+            atomicAdd(bad, 1ULL);
+            pid = 0;
+        }
+        off = ((long)pid * Hkv + kvh) * (PAGE * D);
+    } else {
+        off = ((long)b * Hkv + kvh) * (long)kv.max_seq_len * D + (long)page * (PAGE * D);
+    }
+    return reinterpret_cast<const T *>(base) + off;
+}
+
+// ------------------------------------------------ flash-decode wave worker
+// One wave keeps, per head of its GQA group and per row group of lanes (the
+// tokens it loads), a running max M (log2 units), normaliser L and
+// unnormalised output acc over its E output columns.
+template <int G, int E>
+struct WaveAcc {
+    float M[G], L[G], acc[G][E];
+    __device__ __forceinline__ void init()
+    {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            M[g] = NEG_INF;
+            L[g] = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                acc[g][e] = 0.f;
+        }
+    }
+};
+
+// Key/value rows are streamed once per step: non-temporal 16-byte loads keep
+// them from displacing reusable lines in L2 and the Infinity Cache (used where
+// a wave load covers whole 128-byte lines).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const void *p)
+{
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
+template <typename T>
+struct PageRegs {
+    uint4 k[Kv<T>::LPP], v[Kv<T>::LPP];
+};
+
+template <typename T>
+__device__ __forceinline__ void load_page(PageRegs<T> &r, const T *kp, const T *vp)
+{
+    using K = Kv<T>;
+    const int lane = lane_id(), row = lane / K::LPR, col = lane % K::LPR;
+#pragma unroll
+    for (int s = 0; s < K::LPP; ++s)
+        r.k[s] = load_stream(kp + (s * K::RPL + row) * D + col * K::E);
+#pragma unroll
+    for (int s = 0; s < K::LPP; ++s)
+        r.v[s] = load_stream(vp + (s * K::RPL + row) * D + col * K::E);
+}
+
+// Fold one page into the wave's state.  Token t of the page is valid for
+// head g iff hs[g] <= t <= m; `masked` is false when every token is valid for
+// every head (the common case), and rows past m are zeroed since a cache slot
+// that was never written may hold any bits.
+template <typename T, int G>
+__device__ __forceinline__ void compute_page(const PageRegs<T> &r, int tok0, int m,
+                                             const int (&hs)[G], bool masked,
+                                             const float (&q)[G][Kv<T>::E],
+                                             WaveAcc<G, Kv<T>::E> &st)
+{
+    using K = Kv<T>;
+    constexpr int E = K::E;
+    const int row = lane_id() / K::LPR;
+    float lg[K::LPP][G];
+#pragma unroll
+    for (int s = 0; s < K::LPP; ++s) {
+        float kf[E];
+        to_f32(r.k[s], kf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float a = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                a = fmaf(q[g][e], kf[e], a);
+            lg[s][g] = row_sum<T>(a);
+        }
+    }
+    if (masked) {
+#pragma unroll
+        for (int s = 0; s < K::LPP; ++s) {
+            const int t = tok0 + s * K::RPL + row;
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                if (t < hs[g] || t > m)
+                    lg[s][g] = NEG_INF;
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float mx = lg[0][g];
+#pragma unroll
+        for (int s = 1; s < K::LPP; ++s)
+            mx = fmaxf(mx, lg[s][g]);
+        const float mn = fmaxf(st.M[g], mx);
+        const float base = mn == NEG_INF ? 0.f : mn;
+        const float alpha = exp2f(st.M[g] - base);
+        st.M[g] = mn;
+        st.L[g] *= alpha;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            st.acc[g][e] *= alpha;
+#pragma unroll
+        for (int s = 0; s < K::LPP; ++s)
+            lg[s][g] = exp2f(lg[s][g] - base);
+    }
+#pragma unroll
+    for (int s = 0; s < K::LPP; ++s) {
+        float vf[E];
+        to_f32(r.v[s], vf);
+        if (masked && tok0 + s * K::RPL + row > m) {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                vf[e] = 0.f;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            st.L[g] += lg[s][g];
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                st.acc[g][e] = fmaf(lg[s][g], vf[e], st.acc[g][e]);
+        }
+    }
+}
+
+// Combine the wave's row groups and store, per head, the unnormalised
+// summary (acc[D], M, L) at dst[g*SUMM ..] (global memory or LDS).
+template <typename T, int G>
+__device__ __forceinline__ void store_wave_summary(WaveAcc<G, Kv<T>::E> &st, float *dst)
+{
+    using K = Kv<T>;
+    constexpr int E = K::E;
+    const int lane = lane_id(), row = lane / K::LPR, col = lane % K::LPR;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float Mt = st.M[g];
+        if constexpr (K::LPR == 16)
+            Mt = fmaxf(Mt, xor_lanes<16>(Mt));
+        Mt = fmaxf(Mt, xor_lanes<32>(Mt));
+        const float base = Mt == NEG_INF ? 0.f : Mt;
+        const float sc = exp2f(st.M[g] - base);
+        float Lr = st.L[g] * sc;
+        float a[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            a[e] = st.acc[g][e] * sc;
+        if constexpr (K::LPR == 16) {
+            Lr += xor_lanes<16>(Lr);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                a[e] += xor_lanes<16>(a[e]);
+        }
+        Lr += xor_lanes<32>(Lr);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            a[e] += xor_lanes<32>(a[e]);
+        if (row == 0) {
+#pragma unroll
+            for (int e = 0; e < E; e += 4)
+                *reinterpret_cast<float4 *>(dst + g * SUMM + col * E + e) =
+                    make_float4(a[e], a[e + 1], a[e + 2], a[e + 3]);
+        }
+        if (lane == 0) {
+            dst[g * SUMM + D] = Mt;
+            dst[g * SUMM + D + 1] = Lr;
+        }
+    }
+}
+
+// Queries of the G heads of (b, kvh), this lane's E columns, scaled so that
+// q.k is the logit in log2 units.
+template <typename T, int G>
+__device__ __forceinline__ void load_group_queries(const Shape &s, const State &st, int b, int kvh,
+                                                   float (&q)[G][Kv<T>::E])
+{
+    using K = Kv<T>;
+    const int col = lane_id() % K::LPR;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float *src = st.q_rot + ((long)b * s.Hq + kvh * G + g) * D + col * K::E;
+#pragma unroll
+        for (int e = 0; e < K::E; e += 4) {
+            float4 x = *reinterpret_cast<const float4 *>(src + e);
+            q[g][e + 0] = x.x * s.scale_log2;
+            q[g][e + 1] = x.y * s.scale_log2;
+            q[g][e + 2] = x.z * s.scale_log2;
+            q[g][e + 3] = x.w * s.scale_log2;
+        }
+    }
+}
+
+// ------------------------------------------------------------------- plan
+// Exclusive prefix sum of a[0..n) in LDS by the whole block (any size up to
+// 1024 threads); a[n] = total.
+constexpr int MAX_BLOCK_WAVES = 16;
+
+__device__ inline void block_exclusive_scan(int *a, int n)
+{
+    __shared__ int wsum[MAX_BLOCK_WAVES];
+    const int nt = blockDim.x, nwv = nt >> 6;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int per = (n + nt - 1) / nt;
+    const int lo = min(n, t * per), hi = min(n, lo + per);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i)
+        sum += a[i];
+    int x = sum;
+    for (int off = 1; off < 64; off <<= 1) {
+        int y = __shfl_up(x, off, 64);
+        if (lane >= off)
+            x += y;
+    }
+    if (lane == 63)
+        wsum[wv] = x;
+    __syncthreads();
+    int pre = 0, tot = 0;
+    for (int i = 0; i < nwv; ++i) {
+        if (i < wv)
+            pre += wsum[i];
+        tot += wsum[i];
+    }
+    int run = pre + x - sum;
+    for (int i = lo; i < hi; ++i) {
+        int v = a[i];
+        a[i] = run;
+        run += v;
+    }
+    if (t == 0)
+        a[n] = tot;
+    __syncthreads();
+}
+
+// Page offsets of every group's union span in the flattened work list:
+// off[g] = pages of groups before g, off[nG] = all pages of the step.
+__device__ inline void build_plan(const Shape &s, const State &st, int *off)
+{
+    const int nG = s.B * s.Hkv;
+    for (int g = threadIdx.x; g < nG; g += blockDim.x) {
+        const int gs = st.grp_start[g];
+        const int m = st.m_buf[g / s.Hkv];
+        off[g] = (gs < 0 || m < 0) ? 0 : (m / PAGE - gs / PAGE + 1);
+    }
+    __syncthreads();
+    block_exclusive_scan(off, nG);
+}
+
+// Waves that take part: every worker gets at least MIN_PAGES_PER_WORKER pages.
+__device__ __forceinline__ int active_workers(int n_workers, int P)
+{
+    return min(n_workers, (P + MIN_PAGES_PER_WORKER - 1) / MIN_PAGES_PER_WORKER);
+}
+
+// Worker w owns flattened pages [w*P/nW, (w+1)*P/nW); owner of page x:
+__device__ __forceinline__ int page_owner(long x, int nW, int P)
+{
+    return (int)(((x + 1) * (long)nW - 1) / P);
+}
+
+// Last group g with off[g] <= x (groups with no pages are skipped by caller).
+__device__ __forceinline__ int find_group(const int *off, int nG, long x)
+{
+    int lo = 0, hi = nG - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= x)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// Block 0 of the complete grid records, per group, the first and last worker
+// whose share touches it (the slots of its partial summaries), so the reduce
+// needs no plan of its own.  Groups without pages get the empty range (0, -1).
+__device__ inline void publish_plan(const Shape &s, const State &st, const int *off, int nW)
+{
+    const int nG = s.B * s.Hkv, P = off[nG];
+    for (int g = threadIdx.x; g < nG; g += blockDim.x) {
+        int2 r = make_int2(0, -1);
+        if (off[g + 1] > off[g])
+            r = make_int2(page_owner(off[g], nW, P), page_owner((long)off[g + 1] - 1, nW, P));
+        reinterpret_cast<int2 *>(st.grp_parts)[g] = r;
+    }
+}
+
+// Bytes of LDS the plan (one int per group, plus the total) occupies.
+inline size_t plan_lds_bytes(const Shape &s) { return (size_t)(s.B * s.Hkv + 1) * sizeof(int); }
+
+}  // namespace
+}  // namespace mac

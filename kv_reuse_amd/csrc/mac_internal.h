@@ -1,5 +1,6 @@
 // mac_internal.h -- state layout and kernel launch interface shared by the
-// host runtime (mac_runtime.cpp) and the gfx950 kernels (mac_kernels.hip).
+// host runtime (mac_runtime.cpp) and the gfx950 kernels (match.hip,
+// complete.hip, reduce.hip, amend.hip).
 //
 // Device memory owned by a handle (fp32 unless noted):
 //   ring_q     [B][Hq][W][D]        pre-RoPE queries of recent steps
@@ -13,6 +14,7 @@
 //   dec_start  [B][Hq] int32        first key of the head's span
 //   dec_rel    [B][Hq]              relative distance of the nearest entry
 //   grp_start  [B][Hkv] int32       first key of the group's union span (-1 idle)
+//   grp_parts  [B][Hkv][2] int32    first and last worker whose partial covers the group
 //   tile_best  [B][Hq][W/64][3]     W > 64: nearest entry of each 64-slot tile
 //   partials   [NW + B*Hkv][G][SUMM] per-(worker, group) unnormalised summaries
 //   as_full    [B][Hq][SUMM]        AS_{1:m} of this step, input of amend
@@ -65,6 +67,7 @@ struct Shape {
 struct State {
     float *ring_q, *ring_s, *q_copy, *q_rot, *partials, *as_full, *dec_rel;
     int32_t *ring_pos, *m_buf, *dec_slot, *dec_p, *dec_start, *grp_start;
+    int32_t *grp_parts;       // [B*Hkv][2] worker range of each group's partials (complete -> reduce)
     unsigned long long *stats;
     const double *inv_freq;   // [D/2] theta^(-2i/D), fp64
     float *tile_best;         // W > TILE_W: [B*Hq][ceil(W/TILE_W)][3] per-tile nearest (D, pos, slot)

@@ -64,12 +64,12 @@ mac_status fail_hip(mac_handle h, const char *what, hipError_t e)
     } while (0)
 
 struct Sizes {
-    size_t ring_q, ring_s, ring_pos, qvec, m_buf, dec_i, dec_f, grp, partials, as_full, stats,
-        inv_freq, tiles;
+    size_t ring_q, ring_s, ring_pos, qvec, m_buf, dec_i, dec_f, grp, grp_parts, partials, as_full,
+        stats, inv_freq, tiles;
     size_t total() const
     {
         return ring_q + ring_s + ring_pos + 2 * qvec + m_buf + 3 * dec_i + dec_f + grp +
-               partials + as_full + stats + inv_freq + tiles;
+               grp_parts + partials + as_full + stats + inv_freq + tiles;
     }
 };
 
@@ -88,6 +88,7 @@ Sizes sizes_for(const mac_config &c, int n_workers)
     s.dec_i = round256(B * Hq * sizeof(int32_t));
     s.dec_f = round256(B * Hq * sizeof(float));
     s.grp = round256(B * Hkv * sizeof(int32_t));
+    s.grp_parts = round256(B * Hkv * 2 * sizeof(int32_t));
     s.partials = round256(((size_t)n_workers + B * Hkv) * G * mac::SUMM * sizeof(float));
     s.as_full = round256(B * Hq * mac::SUMM * sizeof(float));
     s.stats = round256(mac::stats_count((long)B * Hkv) * sizeof(unsigned long long));
@@ -319,6 +320,7 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     h->st.dec_start = (int32_t *)take(sz.dec_i);
     h->st.dec_rel = (float *)take(sz.dec_f);
     h->st.grp_start = (int32_t *)take(sz.grp);
+    h->st.grp_parts = (int32_t *)take(sz.grp_parts);
     h->st.partials = (float *)take(sz.partials);
     h->st.as_full = (float *)take(sz.as_full);
     h->st.stats = (unsigned long long *)take(sz.stats);
