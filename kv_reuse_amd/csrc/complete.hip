@@ -83,10 +83,10 @@ __global__ __launch_bounds__(BLOCK) void complete_kernel(Shape s, State st, KvVi
 }
 
 // ========================================================== complete (MFMA)
-// bf16 cache, G <= 4 query heads per KV head.  Q.K^T runs on the matrix cores:
+// bf16 cache, G <= 8 query heads per KV head.  Q.K^T runs on the matrix cores:
 // v_mfma_f32_16x16x32_bf16 with the page's 16 tokens as the 16 columns of B
-// (lane l feeds token l%16, columns 32s + 8(l/16) .. +7 at k-step s, straight
-// from its 16-byte K load) and the group's queries as the rows of A,
+// (lane l feeds token l%16, columns 32s + 8(l/16) .. +7 at k-step s, read
+// from the wave's swizzled LDS copy of the page) and the group's queries as the rows of A,
 // replicated so that row i holds head i % G: every lane receives the logits of
 // all G heads for token l%16.  A carries the query split into two bf16 parts
 // (hi + lo), so the logits keep ~16 mantissa bits of the fp32 query.
@@ -106,19 +106,40 @@ struct MPage {
     uint4 k[4], v[4];
 };
 
-// K arrives in the MFMA layout: one wave load covers 64 of the 128 bytes of 16
-// rows, so every cache line is shared by two consecutive loads and is read
-// with the default policy (a streaming hint makes the second half refetch).
-// V arrives as contiguous 1 KB wave loads of whole lines and is streamed.
+// K and V both arrive as contiguous 1 KB wave loads of whole 128-byte lines
+// (lane (q, t) = (l/16, l%16) holds token 4s + q, columns 8t .. 8t+7), with a
+// streaming hint: every line is read once, by one instruction.  K then passes
+// through the wave's LDS tile into the MFMA layout (see kswizzle_page).
 __device__ __forceinline__ void load_mpage(MPage &r, const uint16_t *kp, const uint16_t *vp)
 {
     const int lane = lane_id(), t = lane & 15, q = lane >> 4;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        r.k[s] = *reinterpret_cast<const uint4 *>(kp + t * D + 32 * s + 8 * q);
+        r.k[s] = load_stream(kp + (4 * s + q) * D + 8 * t);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
         r.v[s] = load_stream(vp + (4 * s + q) * D + 8 * t);
+}
+
+// The MFMA B operand wants lane l to hold token l%16, columns 32s + 8(l/16) ..
+// +7 at k-step s: read straight from memory, each wave load would cover half
+// of every line it touches.  Instead the page's K rows (16 rows x 16 chunks of
+// 16 bytes) go through a 4 KB per-wave LDS tile, chunk c of row j stored at
+// slot c ^ j: the writes of a wave load fill whole rows, and the reads of the
+// MFMA layout (16 rows, one chunk index each) land on 16 distinct slots, so
+// neither side has bank conflicts.
+__device__ __forceinline__ void kswizzle_page(MPage &r, uint4 *tile)
+{
+    const int lane = lane_id(), t = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        tile[(4 * s + q) * 16 + (t ^ (4 * s + q))] = r.k[s];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        r.k[s] = tile[t * 16 + ((4 * s + q) ^ t)];
 }
 
 // HPL: heads whose logits one lane receives from the MFMA (4 row groups of 4
@@ -325,6 +346,7 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
     extern __shared__ int s_off[];
     __shared__ uint4 qlds[WAVES][8][64];   // per wave: 8 A-operand registers x 64 lanes
     __shared__ float4 plds[WAVES][32];     // per wave: probabilities of the page's 16 tokens
+    __shared__ uint4 klds[WAVES][16 * 16];  // per wave: the page's K rows, swizzled
     const int nG = s.B * s.Hkv;
     build_plan(s, st, s_off);
     const int P = s_off[nG];
@@ -396,6 +418,7 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
         while (true) {
             load_mpage(r0, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad),
                        kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page, bad));
+            kswizzle_page(r0, klds[wv]);
             const int tok0 = page * PAGE;
             compute_mpage<G>(r0, &qlds[wv][0][0], plds[wv], tok0, m, hsl,
                              tok0 < hmax || tok0 + PAGE - 1 > m, half_mask, acc);
