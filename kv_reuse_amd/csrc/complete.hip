@@ -109,7 +109,7 @@ struct MPage {
 // K and V both arrive as contiguous 1 KB wave loads of whole 128-byte lines
 // (lane (q, t) = (l/16, l%16) holds token 4s + q, columns 8t .. 8t+7), with a
 // streaming hint: every line is read once, by one instruction.  K then passes
-// through the wave's LDS tile into the MFMA layout (see kswizzle_page).
+// through the wave's LDS tile into the MFMA layout (see kstore_page).
 __device__ __forceinline__ void load_mpage(MPage &r, const uint16_t *kp, const uint16_t *vp)
 {
     const int lane = lane_id(), t = lane & 15, q = lane >> 4;
@@ -127,8 +127,9 @@ __device__ __forceinline__ void load_mpage(MPage &r, const uint16_t *kp, const u
 // 16 bytes) go through a 4 KB per-wave LDS tile, chunk c of row j stored at
 // slot c ^ j: the writes of a wave load fill whole rows, and the reads of the
 // MFMA layout (16 rows, one chunk index each) land on 16 distinct slots, so
-// neither side has bank conflicts.
-__device__ __forceinline__ void kswizzle_page(MPage &r, uint4 *tile)
+// neither side has bank conflicts.  compute_mpage reads each k-step's operand
+// from the tile just before its MFMA.
+__device__ __forceinline__ void kstore_page(const MPage &r, uint4 *tile)
 {
     const int lane = lane_id(), t = lane & 15, q = lane >> 4;
 #pragma unroll
@@ -137,9 +138,6 @@ __device__ __forceinline__ void kswizzle_page(MPage &r, uint4 *tile)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-        r.k[s] = tile[t * 16 + ((4 * s + q) ^ t)];
 }
 
 // HPL: heads whose logits one lane receives from the MFMA (4 row groups of 4
@@ -175,7 +173,7 @@ __device__ __forceinline__ int lane_pick(unsigned long long mask, int if_set, in
 // hsl: first key of each of this lane's own heads' spans.  half_mask: lanes
 // holding heads 4..7 (G = 8; zero otherwise).
 template <int G>
-__device__ __forceinline__ void compute_mpage(const MPage &r, const uint4 *qa, float4 *px,
+__device__ __forceinline__ void compute_mpage(const uint4 *ktile, const uint4 (&vr)[4], const uint4 *qa, float4 *px,
                                               int tok0, int m, const int (&hsl)[MAcc<G>::HPL],
                                               bool masked, unsigned long long half_mask,
                                               MAcc<G> &st)
@@ -187,7 +185,7 @@ __device__ __forceinline__ void compute_mpage(const MPage &r, const uint4 *qa, f
     floatx4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        const bf16x8 kb = __builtin_bit_cast(bf16x8, r.k[s]);
+        const bf16x8 kb = __builtin_bit_cast(bf16x8, ktile[t * 16 + ((4 * s + q) ^ t)]);
         const uint4 ahi = qa[(2 * s) * 64 + lane], alo = qa[(2 * s + 1) * 64 + lane];
         S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ahi), kb, S0, 0,
                                                      0, 0);
@@ -259,7 +257,7 @@ __device__ __forceinline__ void compute_mpage(const MPage &r, const uint4 *qa, f
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         float vf[8];
-        to_f32(r.v[s], vf);
+        to_f32(vr[s], vf);
         if (masked && tok0 + 4 * s + q > m) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
@@ -411,19 +409,43 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
         }
         int page = first_page + (int)(x - s_off[g]);
         const int last = first_page + (int)(gend - s_off[g]) - 1;
-        // one page in flight per wave: at <= 168 VGPRs (G <= 4) three waves
-        // share each SIMD, which hides the load latency better than double
-        // buffering at two waves per SIMD (measured)
-        MPage r0;
-        while (true) {
-            load_mpage(r0, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad),
+        if constexpr (G > 4) {
+            // two waves per SIMD (G = 8 needs ~220 VGPRs): the next page's
+            // loads are issued before the current page is computed
+            MPage cur, nxt;
+            load_mpage(cur, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad),
                        kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page, bad));
-            kswizzle_page(r0, klds[wv]);
-            const int tok0 = page * PAGE;
-            compute_mpage<G>(r0, &qlds[wv][0][0], plds[wv], tok0, m, hsl,
-                             tok0 < hmax || tok0 + PAGE - 1 > m, half_mask, acc);
-            if (++page > last)
-                break;
+            kstore_page(cur, klds[wv]);
+            while (true) {
+                if (page + 1 <= last)
+                    load_mpage(nxt, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page + 1, bad),
+                               kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page + 1, bad));
+                const int tok0 = page * PAGE;
+                compute_mpage<G>(klds[wv], cur.v, &qlds[wv][0][0], plds[wv], tok0, m, hsl,
+                                 tok0 < hmax || tok0 + PAGE - 1 > m, half_mask, acc);
+                if (++page > last)
+                    break;
+                kstore_page(nxt, klds[wv]);
+                cur.v[0] = nxt.v[0];
+                cur.v[1] = nxt.v[1];
+                cur.v[2] = nxt.v[2];
+                cur.v[3] = nxt.v[3];
+            }
+        } else {
+            // one page in flight per wave: at <= 168 VGPRs three waves share
+            // each SIMD, which hides the load latency better than double
+            // buffering (which needs more registers than that) does (measured)
+            MPage cur;
+            while (true) {
+                load_mpage(cur, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad),
+                           kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page, bad));
+                kstore_page(cur, klds[wv]);
+                const int tok0 = page * PAGE;
+                compute_mpage<G>(klds[wv], cur.v, &qlds[wv][0][0], plds[wv], tok0, m, hsl,
+                                 tok0 < hmax || tok0 + PAGE - 1 > m, half_mask, acc);
+                if (++page > last)
+                    break;
+            }
         }
         store_msummary<G>(acc, st.partials + ((long)w + g) * G * SUMM);
         x = gend;
