@@ -5,8 +5,9 @@ within 1e-4 of tau, or whose two nearest ring entries are within a relative
 1e-5, are forced to the oracle's decision through the override array (both
 decisions are correct there).  The GPU then runs and must reproduce every
 decision bit for bit and every output within max-abs 2e-3 and per-row
-relative 1e-2.  Cache rows that have not been appended yet hold NaN, so a
-kernel that reads past the query position fails loudly.
+relative 1e-2.  Cache rows that have not been appended yet hold NaN (per
+request, for ragged prefill lengths), so a kernel that reads past a request's
+query position fails loudly.
 """
 import numpy as np
 import torch
@@ -25,8 +26,13 @@ def _kv_nan(dtype):
 
 class Lockstep:
     def __init__(self, w, flags=0, track=None, device="cuda", oracle_flags=0, tau=None, r=None,
-                 W=None, sync_amend=False, layer=0, amend_stream=None):
+                 W=None, sync_amend=False, layer=0, amend_stream=None, prefill=None):
         self.w = w
+        # per-request prefill length (ragged batches); request b decodes
+        # position prefill[b] + t at step t
+        self.prefill = (np.full(w.B, w.C, np.int32) if prefill is None
+                        else np.asarray(prefill, np.int32))
+        assert self.prefill.shape == (w.B,) and self.prefill.max() <= w.C
         self.tau = w.tau if tau is None else tau
         self.r = w.r if r is None else r
         self.W = w.W if W is None else W
@@ -50,8 +56,9 @@ class Lockstep:
         # device cache: prefill rows present, the rest NaN until appended
         logical_k = K.clone()
         logical_v = V.clone()
-        logical_k[:, :, w.C:] = _kv_nan(K.dtype)
-        logical_v[:, :, w.C:] = _kv_nan(V.dtype)
+        for b in range(B):
+            logical_k[b, :, int(self.prefill[b]):] = _kv_nan(K.dtype)
+            logical_v[b, :, int(self.prefill[b]):] = _kv_nan(V.dtype)
         if self.paged:
             self.table_np = page_table(w)
             self.kc = to_paged(logical_k, self.table_np)
@@ -87,12 +94,12 @@ class Lockstep:
         """Append, run the oracle, enqueue the GPU decode step (no synchronisation)."""
         w = self.w
         B = w.B
-        seq_h = np.full(B, w.C + t + 1, np.int32) if seq_lens is None else np.asarray(seq_lens,
-                                                                                       np.int32)
+        seq_h = (self.prefill + t + 1).astype(np.int32) if seq_lens is None else np.asarray(
+            seq_lens, np.int32)
         q_h = self.q[t] if q is None else q
-        # KV manager: row C+t of the workload enters the cache at step t for
-        # every request, whether or not the request decodes this step
-        pos_h = np.full(B, w.C + t, np.int32)
+        # KV manager: row prefill[b]+t of the workload enters request b's cache
+        # at step t, whether or not the request decodes this step
+        pos_h = (self.prefill + t).astype(np.int32)
         self.pos.copy_(torch.as_tensor(pos_h))
         m_idx = torch.as_tensor(pos_h, device=self.dev, dtype=torch.long)
         bi = torch.arange(B, device=self.dev)

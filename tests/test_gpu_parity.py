@@ -73,6 +73,37 @@ def test_small_window_and_band(gpu_lib):
     _run(w, w.steps)
 
 
+def test_ragged_contexts(gpu_lib):
+    """Requests of different lengths in one batch: positions at every offset
+    within a page, one request shorter than the band (its stored prefixes are
+    EMPTY), rows past each request's position NaN."""
+    w = scaled(get_config("b16_128k"), B=6, C=1200, steps=40, rho=("const", 0.96))
+    hits, _ = _run(w, w.steps, prefill=[1200, 1199, 1185, 1024, 777, 17])
+    assert hits > 0
+
+
+def test_context_shorter_than_band(gpu_lib):
+    """m grows from 3 past r = 64: hits before m = r merge an EMPTY prefix."""
+    w = scaled(get_config("b16_128k"), B=2, C=3, steps=100, W=16, r=64, rho=("const", 0.96))
+    hits, _ = _run(w, w.steps)
+    assert hits > 0
+
+
+@pytest.mark.parametrize("W", [24, 48])
+def test_windows_not_power_of_two(gpu_lib, W):
+    w = scaled(get_config("b16_128k"), B=2, C=500, steps=70, W=W, rho=("const", 0.96))
+    _run(w, w.steps)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8)])
+def test_maximum_group_count(gpu_lib, Hq, Hkv):
+    """B * Hkv = 4096 GQA groups, the most a handle takes: the plan of every
+    complete block covers all of them."""
+    w = scaled(get_config("b16_128k"), B=4096 // Hkv, Hq=Hq, Hkv=Hkv, C=40, steps=6, W=4, r=16,
+               rho=("const", 0.96))
+    _run(w, w.steps)
+
+
 @pytest.mark.parametrize("W,steps", [(65, 90), (100, 150), (512, 140), (2048, 140)])
 def test_large_windows(gpu_lib, W, steps):
     """Rings longer than one 64-slot tile (the pages' windows reach 2048
