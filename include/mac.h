@@ -12,7 +12,9 @@
  * full attention over the whole context.
  *
  * Conventions for every call:
- *  - Pointers are device pointers unless marked "host".
+ *  - Pointers are device pointers unless marked "host".  The key/value
+ *    caches, k_new, v_new, q_pre_rope and out must be 16-byte aligned (the
+ *    kernels move rows as 16-byte vectors); a misaligned one is MAC_EINVAL.
  *  - Positions are 0-based.  For request b the query position is
  *    m = seq_lens[b] - 1; its own K/V row must already be in the cache.
  *  - A summary (o, M, l) is the normalised attention output o[d], a reference

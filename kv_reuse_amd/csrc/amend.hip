@@ -83,8 +83,13 @@ __global__ __launch_bounds__(64 * AMEND_WAVES) void amend_kernel(Shape s, State 
         const float2 qv = *reinterpret_cast<const float2 *>(st.q_copy + idx * D + 2 * lane);
         *reinterpret_cast<float2 *>(st.ring_q + (idx * s.W + slot_new) * D + 2 * lane) = qv;
     }
-    if (kvh == 0 && threadIdx.x == 0)
-        st.ring_pos[(long)b * s.W + slot_new] = m;
+    if (threadIdx.x == 0) {
+        if (kvh == 0)
+            st.ring_pos[(long)b * s.W + slot_new] = m;
+        if (has_prefix)   // this block owns the group's amend counter
+            st.grp_stats[((long)b * s.Hkv + kvh) * GRP_NSTAT + GS_TOK_AMEND] +=
+                (unsigned long long)s.r;
+    }
 }
 
 // ================================================================= append
@@ -187,7 +192,7 @@ hipError_t launch_append(const Shape &s, const State &st, const KvView &kv, bool
 hipError_t launch_reset(const Shape &s, const State &st, hipStream_t stream)
 {
     const long n = (long)s.B * s.W;
-    const long ns = stats_count(s.B * s.Hkv);
+    const long ns = stats_count((long)s.B * s.Hq, (long)s.B * s.Hkv);
     const long tot = n > ns ? n : ns;
     hipLaunchKernelGGL(reset_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream,
                        st.ring_pos, n, st.stats, ns);

@@ -37,14 +37,15 @@ __global__ __launch_bounds__(BLOCK) void complete_kernel(Shape s, State st, KvVi
         const long gend = min((long)s_off[g + 1], x1);
         const int b = g / s.Hkv, kvh = g % s.Hkv;
         const int m = st.m_buf[b];
-        const int first_page = st.grp_start[g] / PAGE;
         int hs[G];
-        int hmax = 0;
+        int hmax = 0, hmin = INT_MAX;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             hs[h] = st.dec_start[(long)b * s.Hq + kvh * G + h];
             hmax = max(hmax, hs[h]);
+            hmin = min(hmin, hs[h]);
         }
+        const int first_page = hmin / PAGE;   // the group's union span starts at hmin
         float q[G][K::E];
         load_group_queries<T, G>(s, st, b, kvh, q);
         WaveAcc<G, K::E> acc;
@@ -369,16 +370,17 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
         const long gend = min((long)s_off[g + 1], x1);
         const int b = g / s.Hkv, kvh = g % s.Hkv;
         const int m = st.m_buf[b];
-        const int first_page = st.grp_start[g] / PAGE;
         constexpr int HPL = MAcc<G>::HPL;
         const unsigned long long half_mask = G > 4 ? __ballot((lane >> 4) & 1) : 0ULL;
         int hs[G];
-        int hmax = 0;
+        int hmax = 0, hmin = INT_MAX;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             hs[h] = st.dec_start[(long)b * s.Hq + kvh * G + h];
             hmax = max(hmax, hs[h]);
+            hmin = min(hmin, hs[h]);
         }
+        const int first_page = hmin / PAGE;   // the group's union span starts at hmin
         int hsl[HPL];
 #pragma unroll
         for (int v = 0; v < HPL; ++v) {

@@ -378,15 +378,26 @@ __device__ inline void block_exclusive_scan(int *a, int n)
     __syncthreads();
 }
 
+// First key of group g's union span: the smallest first key of its heads'
+// spans (every span ends at the query position m).
+__device__ __forceinline__ int group_start(const Shape &s, const State &st, int g)
+{
+    const int b = g / s.Hkv, kvh = g % s.Hkv;
+    const int32_t *ds = st.dec_start + (long)b * s.Hq + kvh * s.G;
+    int gs = ds[0];
+    for (int h = 1; h < s.G; ++h)
+        gs = min(gs, ds[h]);
+    return gs;
+}
+
 // Page offsets of every group's union span in the flattened work list:
 // off[g] = pages of groups before g, off[nG] = all pages of the step.
 __device__ inline void build_plan(const Shape &s, const State &st, int *off)
 {
     const int nG = s.B * s.Hkv;
     for (int g = threadIdx.x; g < nG; g += blockDim.x) {
-        const int gs = st.grp_start[g];
         const int m = st.m_buf[g / s.Hkv];
-        off[g] = (gs < 0 || m < 0) ? 0 : (m / PAGE - gs / PAGE + 1);
+        off[g] = m < 0 ? 0 : (m / PAGE - group_start(s, st, g) / PAGE + 1);
     }
     __syncthreads();
     block_exclusive_scan(off, nG);
@@ -420,14 +431,20 @@ __device__ __forceinline__ int find_group(const int *off, int nG, long x)
 
 // Block 0 of the complete grid records, per group, the first and last worker
 // whose share touches it (the slots of its partial summaries), so the reduce
-// needs no plan of its own.  Groups without pages get the empty range (0, -1).
+// needs no plan of its own, and adds the keys the group streams this step
+// (m - start + 1) to the group's counter, which only this block writes.
+// Groups without pages get the empty range (0, -1).
 __device__ inline void publish_plan(const Shape &s, const State &st, const int *off, int nW)
 {
     const int nG = s.B * s.Hkv, P = off[nG];
     for (int g = threadIdx.x; g < nG; g += blockDim.x) {
         int2 r = make_int2(0, -1);
-        if (off[g + 1] > off[g])
+        if (off[g + 1] > off[g]) {
             r = make_int2(page_owner(off[g], nW, P), page_owner((long)off[g + 1] - 1, nW, P));
+            const int m = st.m_buf[g / s.Hkv];
+            st.grp_stats[(long)g * GRP_NSTAT + GS_TOK_CRIT] +=
+                (unsigned long long)(m - group_start(s, st, g) + 1);
+        }
         reinterpret_cast<int2 *>(st.grp_parts)[g] = r;
     }
 }

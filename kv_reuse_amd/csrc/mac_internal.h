@@ -13,12 +13,13 @@
 //   dec_p      [B][Hq] int32        matched position (-1 miss)
 //   dec_start  [B][Hq] int32        first key of the head's span
 //   dec_rel    [B][Hq]              relative distance of the nearest entry
-//   grp_start  [B][Hkv] int32       first key of the group's union span (-1 idle)
 //   grp_parts  [B][Hkv][2] int32    first and last worker whose partial covers the group
 //   tile_best  [B][Hq][W/64][3]     W > 64: nearest entry of each 64-slot tile
 //   partials   [NW + B*Hkv][G][SUMM] per-(worker, group) unnormalised summaries
 //   as_full    [B][Hq][SUMM]        AS_{1:m} of this step, input of amend
-//   stats      [MAC_NSTAT + B*Hkv*GRP_NSTAT] uint64
+//   stats      [MAC_NSTAT] + [B*Hq][HEAD_NSTAT] + [B*Hkv][GRP_NSTAT] uint64 counters
+// A group's union span (the keys complete streams for it) starts at the
+// smallest first key of its heads' spans; the plan derives it from dec_start.
 // M values inside the library are in log2 units of the scaled logit
 // (s * log2 e); every summary the library stores uses the same units.
 #pragma once
@@ -37,16 +38,19 @@ constexpr int TILE_W = 64;      // ring slots a wave scans at once (LDS tile or 
 constexpr int MAX_GROUPS = 4096;  // B * Hkv
 constexpr int MIN_PAGES_PER_WORKER = 2;
 
-// Counters: stats[0 .. MAC_NSTAT) are device-wide (only ST_BAD_INPUT is used
-// there, by atomics on error paths); each GQA group g then owns
-// stats[MAC_NSTAT + g*GRP_NSTAT ..], updated without atomics by the one match
-// block that handles g in a step.  The host sums the groups.
-enum Stat {
-    ST_DECISIONS = 0, ST_HITS, ST_MISSES, ST_NEAR_TAU, ST_OVR_INVALID, ST_TOK_CRIT, ST_TOK_AMEND,
-    ST_BAD_INPUT, MAC_NSTAT = 16
-};
-constexpr int GRP_NSTAT = 8;
-inline long stats_count(long n_groups) { return MAC_NSTAT + n_groups * GRP_NSTAT; }
+// Counters, one uint64 block: MAC_NSTAT device-wide ones (only ST_BAD_INPUT,
+// by atomics on error paths), then HEAD_NSTAT per (request, query head),
+// written without atomics by the match wave that owns the head, then
+// GRP_NSTAT per (request, KV group): keys streamed by complete (written by
+// block 0 of the complete grid) and re-read by amend (written by the amend
+// block of the group).  The host sums them.
+enum GlobalStat { ST_BAD_INPUT = 0, MAC_NSTAT = 8 };
+enum HeadStat { HS_HITS = 0, HS_MISSES, HS_NEAR_TAU, HS_OVR_INVALID, HEAD_NSTAT };
+enum GroupStat { GS_TOK_CRIT = 0, GS_TOK_AMEND, GRP_NSTAT };
+inline long stats_count(long n_heads, long n_groups)
+{
+    return MAC_NSTAT + n_heads * HEAD_NSTAT + n_groups * GRP_NSTAT;
+}
 
 struct KvView {
     void *k;
@@ -66,9 +70,11 @@ struct Shape {
 
 struct State {
     float *ring_q, *ring_s, *q_copy, *q_rot, *partials, *as_full, *dec_rel;
-    int32_t *ring_pos, *m_buf, *dec_slot, *dec_p, *dec_start, *grp_start;
+    int32_t *ring_pos, *m_buf, *dec_slot, *dec_p, *dec_start;
     int32_t *grp_parts;       // [B*Hkv][2] worker range of each group's partials (complete -> reduce)
-    unsigned long long *stats;
+    unsigned long long *stats;        // [MAC_NSTAT], then the two blocks below
+    unsigned long long *head_stats;   // [B*Hq][HEAD_NSTAT]
+    unsigned long long *grp_stats;    // [B*Hkv][GRP_NSTAT]
     const double *inv_freq;   // [D/2] theta^(-2i/D), fp64
     float *tile_best;         // W > TILE_W: [B*Hq][ceil(W/TILE_W)][3] per-tile nearest (D, pos, slot)
     int32_t n_workers;        // waves in the complete grid
@@ -79,10 +85,8 @@ struct State {
 hipError_t launch_match_tiles(const Shape &s, const State &st, const KvView &kv,
                               const int32_t *seq_lens, const float *q_pre, hipStream_t stream);
 hipError_t launch_match(const Shape &s, const State &st, const KvView &kv, const int32_t *seq_lens,
-                        const float *q_pre, const int32_t *override_pos, float *out, int waves,
+                        const float *q_pre, const int32_t *override_pos, float *out,
                         hipStream_t stream);
-// Waves per match block whose ring tiles fit in max_lds bytes of LDS.
-int match_waves(const Shape &s, size_t max_lds);
 hipError_t launch_complete(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
                            int n_blocks, hipStream_t stream);
 hipError_t launch_reduce(const Shape &s, const State &st, float *out, hipStream_t stream);

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -22,7 +23,6 @@ struct mac_ctx {
     mac::State st{};
     int device = 0;
     int n_blocks = 0;
-    int match_waves = 1;
     bool kv_fp32 = false;
     hipStream_t main_stream = nullptr;
     hipStream_t amend_stream = nullptr;
@@ -64,12 +64,12 @@ mac_status fail_hip(mac_handle h, const char *what, hipError_t e)
     } while (0)
 
 struct Sizes {
-    size_t ring_q, ring_s, ring_pos, qvec, m_buf, dec_i, dec_f, grp, grp_parts, partials, as_full,
+    size_t ring_q, ring_s, ring_pos, qvec, m_buf, dec_i, dec_f, grp_parts, partials, as_full,
         stats, inv_freq, tiles;
     size_t total() const
     {
-        return ring_q + ring_s + ring_pos + 2 * qvec + m_buf + 3 * dec_i + dec_f + grp +
-               grp_parts + partials + as_full + stats + inv_freq + tiles;
+        return ring_q + ring_s + ring_pos + 2 * qvec + m_buf + 3 * dec_i + dec_f + grp_parts +
+               partials + as_full + stats + inv_freq + tiles;
     }
 };
 
@@ -87,11 +87,11 @@ Sizes sizes_for(const mac_config &c, int n_workers)
     s.m_buf = round256(B * sizeof(int32_t));
     s.dec_i = round256(B * Hq * sizeof(int32_t));
     s.dec_f = round256(B * Hq * sizeof(float));
-    s.grp = round256(B * Hkv * sizeof(int32_t));
     s.grp_parts = round256(B * Hkv * 2 * sizeof(int32_t));
     s.partials = round256(((size_t)n_workers + B * Hkv) * G * mac::SUMM * sizeof(float));
     s.as_full = round256(B * Hq * mac::SUMM * sizeof(float));
-    s.stats = round256(mac::stats_count((long)B * Hkv) * sizeof(unsigned long long));
+    s.stats = round256(mac::stats_count((long)(B * Hq), (long)(B * Hkv)) *
+                       sizeof(unsigned long long));
     s.inv_freq = round256(mac::D / 2 * sizeof(double));
     const size_t ntiles = (W + mac::TILE_W - 1) / mac::TILE_W;
     s.tiles = W > (size_t)mac::TILE_W ? round256(B * Hq * ntiles * 3 * sizeof(float)) : 0;
@@ -169,12 +169,17 @@ mac_status validate(const mac_config *c, std::string &why)
     return MAC_OK;
 }
 
+// Kernels move key/value rows, queries and outputs as 16-byte vectors.
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
 mac_status check_view(mac_handle h, const mac_kv_view *kv)
 {
     if (!kv)
         return fail(h, MAC_EINVAL, "kv view is NULL");
     if (!kv->k || !kv->v)
         return fail(h, MAC_EINVAL, "kv view has a NULL key or value pointer");
+    if (!aligned16(kv->k) || !aligned16(kv->v))
+        return fail(h, MAC_EINVAL, "kv view key and value pointers must be 16-byte aligned");
     if (!kv->seq_lens)
         return fail(h, MAC_EINVAL, "kv view has NULL seq_lens");
     if (h->cfg.layout == MAC_KV_PAGED &&
@@ -282,10 +287,6 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     if (e != hipSuccess || n_cu < 1)
         return bail(MAC_EHIP, "cannot query the compute-unit count");
 
-    int max_lds = 0;
-    e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, h->device);
-    if (e != hipSuccess || max_lds < 1)
-        return bail(MAC_EHIP, "cannot query the LDS size per block");
     const int G = cfg->num_q_heads / cfg->num_kv_heads;
     const size_t plan_lds = (size_t)(cfg->batch * cfg->num_kv_heads + 1) * sizeof(int);
     h->n_blocks = n_cu * mac::complete_blocks_per_cu(h->kv_fp32, G, plan_lds);
@@ -319,11 +320,12 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     h->st.dec_p = (int32_t *)take(sz.dec_i);
     h->st.dec_start = (int32_t *)take(sz.dec_i);
     h->st.dec_rel = (float *)take(sz.dec_f);
-    h->st.grp_start = (int32_t *)take(sz.grp);
     h->st.grp_parts = (int32_t *)take(sz.grp_parts);
     h->st.partials = (float *)take(sz.partials);
     h->st.as_full = (float *)take(sz.as_full);
     h->st.stats = (unsigned long long *)take(sz.stats);
+    h->st.head_stats = h->st.stats + mac::MAC_NSTAT;
+    h->st.grp_stats = h->st.head_stats + (long)cfg->batch * cfg->num_q_heads * mac::HEAD_NSTAT;
     h->st.inv_freq = (const double *)take(sz.inv_freq);
     h->st.tile_best = sz.tiles ? (float *)take(sz.tiles) : nullptr;
 
@@ -347,7 +349,6 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     const double scale = cfg->sm_scale > 0.f ? (double)cfg->sm_scale : 1.0 / std::sqrt((double)mac::D);
     h->shape.scale_log2 = (float)(scale * 1.4426950408889634);
     h->shape.reuse = !(cfg->flags & MAC_F_DISABLE_REUSE) && cfg->tau >= 0.f;
-    h->match_waves = mac::match_waves(h->shape, (size_t)max_lds);
 
     if (amend_stream) {
         h->amend_stream = (hipStream_t)amend_stream;
@@ -404,6 +405,8 @@ mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv, const void *k_new,
         return s;
     if (!k_new || !v_new || !positions)
         return fail(h, MAC_EINVAL, "k_new, v_new and positions must be non-NULL");
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return fail(h, MAC_EINVAL, "k_new and v_new must be 16-byte aligned");
     hipStream_t st = stream ? (hipStream_t)stream : h->main_stream;
     MAC_HIP(h, mac::launch_append(h->shape, h->st, to_view(h, kv), h->kv_fp32, k_new, v_new,
                                   positions, st));
@@ -420,6 +423,8 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
         return s;
     if (!q_pre_rope || !out)
         return fail(h, MAC_EINVAL, "q_pre_rope and out must be non-NULL");
+    if (!aligned16(q_pre_rope) || !aligned16(out))
+        return fail(h, MAC_EINVAL, "q_pre_rope and out must be 16-byte aligned");
     hipStream_t st = stream ? (hipStream_t)stream : h->main_stream;
     const mac::KvView v = to_view(h, kv);
     const bool timing = h->cfg.flags & MAC_F_TIMING;
@@ -432,7 +437,7 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
     if (h->shape.reuse && h->cfg.ring_size > mac::TILE_W)
         MAC_HIP(h, mac::launch_match_tiles(h->shape, h->st, v, kv->seq_lens, q_pre_rope, st));
     MAC_HIP(h, mac::launch_match(h->shape, h->st, v, kv->seq_lens, q_pre_rope, override_pos, out,
-                                 h->match_waves, st));
+                                 st));
     if (timing)
         MAC_HIP(h, hipEventRecord(h->tm[1], st));
     MAC_HIP(h, mac::launch_complete(h->shape, h->st, v, h->kv_fp32, h->n_blocks, st));
@@ -470,31 +475,34 @@ mac_status mac_stats(mac_handle h, mac_stats_t *out)
     if (h->amend_stream)
         MAC_HIP(h, hipStreamSynchronize(h->amend_stream));
     MAC_HIP(h, hipDeviceSynchronize());
+    const long n_heads = (long)h->cfg.batch * h->cfg.num_q_heads;
     const long n_groups = (long)h->cfg.batch * h->cfg.num_kv_heads;
-    std::vector<unsigned long long> raw(mac::stats_count(n_groups));
+    std::vector<unsigned long long> raw(mac::stats_count(n_heads, n_groups));
     MAC_HIP(h, hipMemcpy(raw.data(), h->st.stats, raw.size() * sizeof(unsigned long long),
                          hipMemcpyDeviceToHost));
-    unsigned long long c[mac::MAC_NSTAT];
-    for (int k = 0; k < mac::MAC_NSTAT; ++k)
-        c[k] = raw[k];
+    unsigned long long hs[mac::HEAD_NSTAT] = {}, gs[mac::GRP_NSTAT] = {};
+    const unsigned long long *hp = raw.data() + mac::MAC_NSTAT;
+    const unsigned long long *gp = hp + n_heads * mac::HEAD_NSTAT;
+    for (long i = 0; i < n_heads; ++i)
+        for (int k = 0; k < mac::HEAD_NSTAT; ++k)
+            hs[k] += hp[i * mac::HEAD_NSTAT + k];
     for (long g = 0; g < n_groups; ++g)
         for (int k = 0; k < mac::GRP_NSTAT; ++k)
-            if (k != mac::ST_BAD_INPUT)
-                c[k] += raw[mac::MAC_NSTAT + g * mac::GRP_NSTAT + k];
+            gs[k] += gp[g * mac::GRP_NSTAT + k];
     std::memset(out, 0, sizeof *out);
     const uint64_t row = 2ull * mac::D * (h->kv_fp32 ? 4 : 2);   // one key row + one value row
     out->steps = (uint64_t)h->calls;
-    out->decisions = c[mac::ST_DECISIONS];
-    out->hits = c[mac::ST_HITS];
-    out->misses = c[mac::ST_MISSES];
-    out->near_tau = c[mac::ST_NEAR_TAU];
-    out->override_invalid = c[mac::ST_OVR_INVALID];
-    out->kv_tokens_critical = c[mac::ST_TOK_CRIT];
-    out->kv_tokens_amend = c[mac::ST_TOK_AMEND];
-    out->kv_bytes_critical = c[mac::ST_TOK_CRIT] * row;
-    out->kv_bytes_amend = c[mac::ST_TOK_AMEND] * row;
+    out->hits = hs[mac::HS_HITS];
+    out->misses = hs[mac::HS_MISSES];
+    out->decisions = out->hits + out->misses;
+    out->near_tau = hs[mac::HS_NEAR_TAU];
+    out->override_invalid = hs[mac::HS_OVR_INVALID];
+    out->kv_tokens_critical = gs[mac::GS_TOK_CRIT];
+    out->kv_tokens_amend = gs[mac::GS_TOK_AMEND];
+    out->kv_bytes_critical = gs[mac::GS_TOK_CRIT] * row;
+    out->kv_bytes_amend = gs[mac::GS_TOK_AMEND] * row;
     out->aux_bytes = h->aux_bytes;
-    out->bad_input = c[mac::ST_BAD_INPUT];
+    out->bad_input = raw[mac::ST_BAD_INPUT];
     if (h->timed_step) {
         float t = 0.f;
         if (hipEventElapsedTime(&t, h->tm[0], h->tm[1]) == hipSuccess) out->last_us_match = t * 1e3f;

@@ -8,7 +8,8 @@
   attention; an override naming no stored position is a counted miss;
 - mac_reset empties the rings; idle requests produce zeros and store nothing;
 - sequence lengths and page ids out of range are caught on the device;
-- the counters agree with the oracle's decisions and key counts.
+- the counters agree with the oracle's decisions and key counts;
+- misaligned device pointers are refused on the host.
 """
 import numpy as np
 import pytest
@@ -204,3 +205,27 @@ def test_timing_flag_reports_kernel_times():
     st = pl.layer.stats()
     assert st["last_us_attention"] > 0 and st["last_us_complete"] > 0
     assert st["last_us_amend"] > 0
+
+
+def test_misaligned_pointers_rejected_on_host():
+    """Queries, outputs and cache rows move as 16-byte vectors: a pointer off
+    by one float is refused before any launch, and the handle stays usable."""
+    w = _case(B=2, steps=2)
+    pl = Plain(w, paged=True)
+    qs = queries(w)
+    q = torch.as_tensor(qs[0], device="cuda")
+    qbuf = torch.zeros(q.numel() + 4, dtype=torch.float32, device="cuda")
+    qbuf[1:1 + q.numel()].copy_(q.reshape(-1))
+    q_bad = qbuf[1:1 + q.numel()].view_as(q)
+    pl.seq.fill_(w.C + 1)
+    with pytest.raises(mac.MacError) as ei:
+        pl.layer.decode_step(pl.view, q_bad, pl.out)
+    assert ei.value.status == mac.MAC_EINVAL
+    obuf = torch.zeros(pl.out.numel() + 4, dtype=torch.float32, device="cuda")
+    with pytest.raises(mac.MacError) as ei:
+        pl.layer.decode_step(pl.view, q, obuf[2:2 + pl.out.numel()].view_as(pl.out))
+    assert ei.value.status == mac.MAC_EINVAL
+    out = pl.step(np.full(w.B, w.C + 1), qs[0])
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and out.abs().sum() > 0
+    assert pl.layer.stats()["steps"] == 1
