@@ -153,7 +153,10 @@ mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv /* host */, const v
  * on the ring entry stored at position p (a counted miss when absent).
  * Waits on the previous step's amend; enqueues match, complete and the
  * reduce/merge on `stream`, then amend on the amend stream (or on `stream`
- * with MAC_F_SYNC_AMEND).  The library copies what amend needs, so the caller
+ * with MAC_F_SYNC_AMEND).  The complete kernel also waits for all work queued
+ * on the amend stream before it (another layer's amend when layers share the
+ * stream): complete runs one wave per SIMD slot with equal shares, and a
+ * kernel still resident when it starts would delay some of its waves.  The library copies what amend needs, so the caller
  * may reuse q_pre_rope, out and seq_lens as soon as the step's work on
  * `stream` has run. */
 mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv /* host */,

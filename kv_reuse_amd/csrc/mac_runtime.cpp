@@ -27,7 +27,7 @@ struct mac_ctx {
     hipStream_t main_stream = nullptr;
     hipStream_t amend_stream = nullptr;
     bool own_amend = false;
-    hipEvent_t ev_attn = nullptr, ev_amend = nullptr;
+    hipEvent_t ev_attn = nullptr, ev_amend = nullptr, ev_drain = nullptr;
     bool amend_pending = false;
     hipEvent_t tm[6] = {};
     bool timed_step = false;
@@ -213,6 +213,7 @@ void release(mac_ctx *h)
     h->n_alloc = 0;
     if (h->ev_attn) (void)hipEventDestroy(h->ev_attn);
     if (h->ev_amend) (void)hipEventDestroy(h->ev_amend);
+    if (h->ev_drain) (void)hipEventDestroy(h->ev_drain);
     for (auto &e : h->tm)
         if (e) (void)hipEventDestroy(e);
     if (h->own_amend && h->amend_stream)
@@ -359,7 +360,8 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
         h->own_amend = true;
     }
     if (hipEventCreateWithFlags(&h->ev_attn, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_amend, hipEventDisableTiming) != hipSuccess)
+        hipEventCreateWithFlags(&h->ev_amend, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_drain, hipEventDisableTiming) != hipSuccess)
         return bail(MAC_EHIP, "hipEventCreate failed");
     for (auto &ev : h->tm)
         if (hipEventCreate(&ev) != hipSuccess)
@@ -438,6 +440,16 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
         MAC_HIP(h, mac::launch_match_tiles(h->shape, h->st, v, kv->seq_lens, q_pre_rope, st));
     MAC_HIP(h, mac::launch_match(h->shape, h->st, v, kv->seq_lens, q_pre_rope, override_pos, out,
                                  st));
+    // The complete kernel is a persistent grid with equal static shares per
+    // wave: a kernel still holding CU slots when it launches delays some of
+    // its waves and with them the whole launch (measured: +35 % when an amend
+    // of another layer overlapped its first microsecond).  So complete waits
+    // for every amend already queued on the amend stream (this handle's or
+    // another layer's sharing it); amend still overlaps append and match.
+    if (h->amend_stream != st && !(h->cfg.flags & MAC_F_SYNC_AMEND) && h->shape.reuse) {
+        MAC_HIP(h, hipEventRecord(h->ev_drain, h->amend_stream));
+        MAC_HIP(h, hipStreamWaitEvent(st, h->ev_drain, 0));
+    }
     if (timing)
         MAC_HIP(h, hipEventRecord(h->tm[1], st));
     MAC_HIP(h, mac::launch_complete(h->shape, h->st, v, h->kv_fp32, h->n_blocks, st));
