@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline-kernel", action="store_true")
     ap.add_argument("--no-32k", action="store_true", help="skip the 32K speedup point")
+    ap.add_argument("--fused-amend", action="store_true",
+                    help="MAC passes with MAC_F_FUSED_AMEND (the reduce updates the ring)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 2 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -116,6 +118,36 @@ class Bench:
         st = self.layer.stats()            # synchronises; last step's kernel times
         st["span_us"] = e0.elapsed_time(e1) * 1e3
         return st
+
+    def enqueue(self, t, q, k_new, v_new):
+        """One decode step enqueued without any host synchronisation."""
+        w = self.w
+        self.pos.fill_(w.C + t)
+        self.seq.fill_(w.C + t + 1)
+        self.layer.append_kv(self.view, k_new, v_new, self.pos, self.stream)
+        self.layer.decode_step(self.view, q, self.out, None, self.stream)
+
+
+def loop_us(w, flags, cache, q_dev, k_rows, v_rows, warmup, steps):
+    """Microseconds per step of a decode loop run back to back (append and
+    decode enqueued with no host synchronisation, as a serving loop runs):
+    each step's match waits for the previous step's amend, so this is the
+    step's whole cost, amend included.  Events on the decode stream around the
+    timed steps; a fresh ring, then `warmup` synchronised steps first."""
+    import torch
+    bn = Bench(w, flags, *cache)
+    for t in range(warmup):
+        bn.step(t, q_dev[t], k_rows[t], v_rows[t])
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(bn.stream)
+    for t in range(warmup, warmup + steps):
+        bn.enqueue(t, q_dev[t], k_rows[t], v_rows[t])
+    e1.record(bn.stream)
+    bn.layer.stats()                       # synchronises every stream of the handle
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    bn.layer.close()
+    return us
 
 
 def speedup_point(name, steps=24, warmup=40):
@@ -196,7 +228,8 @@ def contgen(args):
     main = torch.cuda.current_stream()
     amend = torch.cuda.Stream()
     res = {}
-    for label, flags in (("mac", 0), ("full", mac.MAC_F_DISABLE_REUSE)):
+    for label, flags in (("mac", 0), ("mac_fused_amend", mac.MAC_F_FUSED_AMEND),
+                         ("full", mac.MAC_F_DISABLE_REUSE)):
         cfg = mac.make_config(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, ring_size=w.W,
                               band=w.r, tau=w.tau, rope_theta=w.theta, layout=mac.MAC_KV_PAGED,
                               kv_dtype=mac.MAC_BF16, max_seq_len=w.n_cap, flags=flags)
@@ -238,9 +271,13 @@ def contgen(args):
         "config": {"workload": "contgen", "batch": w.B, "layers": L, "context_at_window": ctx0,
                    "q_heads": w.Hq, "kv_heads": w.Hkv, "ring": w.W, "band": w.r, "tau": w.tau,
                    "rho": list(base.rho), "jump_every": base.jump_every,
-                   "note": "attention path only (append, match, complete, reduce, async amend); no FFN"},
-        "mac": res["mac"], "full_attention_kernel": res["full"],
+                   "note": "attention path only (append, match, complete, reduce, amend on a "
+                           "second stream shared by the layers); no FFN"},
+        "mac": res["mac"], "mac_fused_amend": res["mac_fused_amend"],
+        "full_attention_kernel": res["full"],
         "speedup_vs_full": res["mac"]["tokens_per_s"] / res["full"]["tokens_per_s"],
+        "speedup_vs_full_fused_amend": (res["mac_fused_amend"]["tokens_per_s"] /
+                                        res["full"]["tokens_per_s"]),
         "setup_s": setup,
     }
     print(json.dumps(line), flush=True)
@@ -319,7 +356,8 @@ def main():
 
     # pass 1 (the timed region): the attention phase between two stream events
     # per step, no events between the kernels
-    bench = Bench(w, 0, kc, vc, paged, table)
+    mac_flags = mac.MAC_F_FUSED_AMEND if args.fused_amend else 0
+    bench = Bench(w, mac_flags, kc, vc, paged, table)
     for t in range(args.warmup):
         bench.step(t, q_dev[t], k_rows[t], v_rows[t])
     st0 = bench.layer.stats()
@@ -340,7 +378,7 @@ def main():
 
     # pass 2: the same steps from a fresh ring (same decisions, same bytes)
     # with the library's HIP events around every kernel (MAC_F_TIMING)
-    kb = Bench(w, mac.MAC_F_TIMING, kc, vc, paged, table)
+    kb = Bench(w, mac_flags | mac.MAC_F_TIMING, kc, vc, paged, table)
     comp, match, red, amend, att_ev, toks2 = [], [], [], [], [], []
     prev = None
     for t in range(total):
@@ -387,11 +425,11 @@ def main():
 
     # the reuse path's own speedup at this context: the same cache, queries
     # with rho = 0.97 (nearly every head hits its previous step)
-    allhit = None
+    allhit = loops = None
     if not args.no_baseline_kernel and args.config == "b16_128k" and not args.set and not args.r:
         wa = scaled(w, rho=("const", 0.97))
         qa = torch.as_tensor(queries(wa, steps=total), device="cuda")
-        ab = Bench(wa, 0, kc, vc, paged, table)
+        ab = Bench(wa, mac_flags, kc, vc, paged, table)
         aa, ah, at, prev = [], [], [], None
         for t in range(min(total, 4 + 16)):
             st = ab.step(t, qa[t], k_rows[t], v_rows[t])
@@ -401,10 +439,21 @@ def main():
                 at.append(st["kv_tokens_critical"] - prev["kv_tokens_critical"])
             prev = st
         ab.layer.close()
+        cache = (kc, vc, paged, table)
         allhit = {"rho": 0.97, "attention_us": float(np.mean(aa)),
                   "head_hit_rate": float(np.sum(ah)) / (heads * len(ah)),
                   "kv_bytes_per_step": float(np.mean(at)) * row_bytes,
-                  "speedup_vs_full": (base["attention_us"] / float(np.mean(aa))) if base else None}
+                  "speedup_vs_full": (base["attention_us"] / float(np.mean(aa))) if base else None,
+                  "loop_us_per_step": {
+                      "mac": loop_us(wa, 0, cache, qa, k_rows, v_rows, 4, 16),
+                      "mac_fused_amend": loop_us(wa, mac.MAC_F_FUSED_AMEND, cache, qa, k_rows,
+                                                 v_rows, 4, 16)}}
+        # the mixed workload's decode loop, amend included, for both amend forms
+        loops = {"mac": loop_us(w, 0, cache, q_dev, k_rows, v_rows, 4, 16),
+                 "mac_fused_amend": loop_us(w, mac.MAC_F_FUSED_AMEND, cache, q_dev, k_rows,
+                                            v_rows, 4, 16),
+                 "full_attention": loop_us(w, mac.MAC_F_DISABLE_REUSE, cache, q_dev, k_rows,
+                                           v_rows, 4, 16)}
 
     point_32k = None
     if not args.no_32k and args.config == "b16_128k" and not args.set and not args.r:
@@ -448,7 +497,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "context": w.C, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.d, "kv_layout": w.layout,
-                   "ring": w.W, "band": w.r, "tau": w.tau, "rho": list(w.rho)},
+                   "ring": w.W, "band": w.r, "tau": w.tau, "rho": list(w.rho),
+                   "amend": "fused" if args.fused_amend else "async"},
         "hbm_gbps": float(np.mean(kv_bytes)) / (att_us * 1e-6) / 1e9,
         "tokens_per_s": w.B / (att_us * 1e-6),
         "kv_bytes_per_step": float(np.mean(kv_bytes)),
@@ -462,6 +512,7 @@ def main():
                      "kernel_sha16": kernel_sha16(), "bytes_per_launch": float(np.mean(comp_bytes))},
         "attention_phase_bytes_per_step": att_bytes,
         "full_attention_kernel": base,
+        "loop_us_per_step": loops,
         "allhit_128k": allhit,
         "speedup_32k": point_32k,
         "cpu_baseline": cpu,

@@ -59,7 +59,13 @@ enum {
     MAC_F_DISABLE_REUSE = 1u,  /* every head misses: plain full attention, no ring upkeep */
     MAC_F_SYNC_AMEND = 2u,     /* run amend on the decode stream instead of the amend stream */
     MAC_F_TIMING = 4u,         /* time each kernel with HIP events (read via mac_stats) */
-    MAC_F_RECORD_DEBUG = 8u    /* keep per-head decisions for mac_debug_last */
+    MAC_F_RECORD_DEBUG = 8u,   /* keep per-head decisions for mac_debug_last */
+    /* Fused amend (a variant of Figure 2 (c)): complete cuts every span before
+     * the band [m-r+1, m], and the reduce forms AS_{1:m-r} as the stored
+     * prefix merged with the part before the band and writes the ring entry
+     * itself: no band re-read, no log-domain removal, no amend stream work.
+     * Same results up to rounding. */
+    MAC_F_FUSED_AMEND = 16u
 };
 
 /* Layer configuration (host struct).  head_dim must be 128; Hq % Hkv == 0;
@@ -153,10 +159,12 @@ mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv /* host */, const v
  * on the ring entry stored at position p (a counted miss when absent).
  * Waits on the previous step's amend; enqueues match, complete and the
  * reduce/merge on `stream`, then amend on the amend stream (or on `stream`
- * with MAC_F_SYNC_AMEND).  The complete kernel also waits for all work queued
- * on the amend stream before it (another layer's amend when layers share the
- * stream): complete runs one wave per SIMD slot with equal shares, and a
- * kernel still resident when it starts would delay some of its waves.  The library copies what amend needs, so the caller
+ * with MAC_F_SYNC_AMEND; with MAC_F_FUSED_AMEND the reduce does the ring
+ * update and no amend is enqueued).  When the amend stream was supplied to
+ * mac_init (layers may share it), the complete kernel also waits for all work
+ * queued on it before it: complete gives every wave of a full-occupancy grid
+ * an equal share, and a kernel still resident when it starts would delay some
+ * of its waves.  The library copies what amend needs, so the caller
  * may reuse q_pre_rope, out and seq_lens as soon as the step's work on
  * `stream` has run. */
 mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv /* host */,

@@ -8,18 +8,19 @@ namespace {
 
 // =============================================================== complete
 // Persistent grid of independent wave workers.  Every block rebuilds the
-// plan (a scan over B*Hkv group spans) in LDS; the step's pages, group after
-// group, are split into equal contiguous shares, one per active wave.  A
-// worker writes one partial summary per group it touches, into slot
-// (worker + group), which is unique along the flattened list.
+// plan (a scan over the work list's segments: each group's union span, cut
+// before the band when amend is fused) in LDS; the step's pages, segment
+// after segment, are split into equal contiguous shares, one per active wave.
+// A worker writes one partial summary per segment it touches, into slot
+// (worker + segment), which is unique along the flattened list.
 template <typename T, int G>
 __global__ __launch_bounds__(BLOCK) void complete_kernel(Shape s, State st, KvView kv)
 {
     extern __shared__ int s_off[];
     using K = Kv<T>;
-    const int nG = s.B * s.Hkv;
+    const int nS = s.B * s.Hkv * s.nseg;
     build_plan(s, st, s_off);
-    const int P = s_off[nG];
+    const int P = s_off[nS];
     if (P == 0)
         return;
     const int nW = active_workers(st.n_workers, P);
@@ -30,56 +31,55 @@ __global__ __launch_bounds__(BLOCK) void complete_kernel(Shape s, State st, KvVi
         return;
     long x = (long)w * P / nW;
     const long x1 = (long)(w + 1) * P / nW;
-    int g = find_group(s_off, nG, x);
+    int sg = find_segment(s_off, nS, x);
+    unsigned long long *bad = &st.stats[ST_BAD_INPUT];
     while (x < x1) {
-        while (s_off[g + 1] <= x)
-            ++g;
-        const long gend = min((long)s_off[g + 1], x1);
-        const int b = g / s.Hkv, kvh = g % s.Hkv;
-        const int m = st.m_buf[b];
+        while (s_off[sg + 1] <= x)
+            ++sg;
+        const long send = min((long)s_off[sg + 1], x1);
+        const Seg sd = segment(s, st, sg);
+        const int b = sd.b, kvh = sd.kvh, hi = sd.hi;
+        // head h attends keys [max(start_h, lo), hi] of this segment
         int hs[G];
-        int hmax = 0, hmin = INT_MAX;
+        int hmax = 0;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            hs[h] = st.dec_start[(long)b * s.Hq + kvh * G + h];
+            hs[h] = max(st.dec_start[(long)b * s.Hq + kvh * G + h], sd.lo);
             hmax = max(hmax, hs[h]);
-            hmin = min(hmin, hs[h]);
         }
-        const int first_page = hmin / PAGE;   // the group's union span starts at hmin
+        const int first_page = sd.lo / PAGE;
         float q[G][K::E];
         load_group_queries<T, G>(s, st, b, kvh, q);
         WaveAcc<G, K::E> acc;
         acc.init();
 
         PageRegs<T> r0, r1;
-        int page = first_page + (int)(x - s_off[g]);
-        const int last = first_page + (int)(gend - s_off[g]) - 1;
-        load_page<T>(r0, kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page, &st.stats[ST_BAD_INPUT]),
-                     kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page, &st.stats[ST_BAD_INPUT]));
+        int page = first_page + (int)(x - s_off[sg]);
+        const int last = first_page + (int)(send - s_off[sg]) - 1;
+        load_page<T>(r0, kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page, bad),
+                     kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page, bad));
         while (true) {
             if (page + 1 <= last)
-                load_page<T>(r1,
-                             kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page + 1, &st.stats[ST_BAD_INPUT]),
-                             kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page + 1, &st.stats[ST_BAD_INPUT]));
+                load_page<T>(r1, kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page + 1, bad),
+                             kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page + 1, bad));
             {
                 const int tok0 = page * PAGE;
-                compute_page<T, G>(r0, tok0, m, hs, tok0 < hmax || tok0 + PAGE - 1 > m, q, acc);
+                compute_page<T, G>(r0, tok0, hi, hs, tok0 < hmax || tok0 + PAGE - 1 > hi, q, acc);
             }
             if (++page > last)
                 break;
             if (page + 1 <= last)
-                load_page<T>(r0,
-                             kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page + 1, &st.stats[ST_BAD_INPUT]),
-                             kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page + 1, &st.stats[ST_BAD_INPUT]));
+                load_page<T>(r0, kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page + 1, bad),
+                             kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page + 1, bad));
             {
                 const int tok0 = page * PAGE;
-                compute_page<T, G>(r1, tok0, m, hs, tok0 < hmax || tok0 + PAGE - 1 > m, q, acc);
+                compute_page<T, G>(r1, tok0, hi, hs, tok0 < hmax || tok0 + PAGE - 1 > hi, q, acc);
             }
             if (++page > last)
                 break;
         }
-        store_wave_summary<T, G>(acc, st.partials + ((long)w + g) * G * SUMM);
-        x = gend;
+        store_wave_summary<T, G>(acc, st.partials + ((long)w + sg) * G * SUMM);
+        x = send;
     }
 }
 
@@ -171,11 +171,12 @@ __device__ __forceinline__ int lane_pick(unsigned long long mask, int if_set, in
     return __float_as_int(lane_pick(mask, __int_as_float(if_set), __int_as_float(if_clear)));
 }
 
-// hsl: first key of each of this lane's own heads' spans.  half_mask: lanes
-// holding heads 4..7 (G = 8; zero otherwise).
+// Fold one page (tokens tok0 .. tok0+15) into the wave's state.  hsl: first
+// key of each of this lane's own heads' spans; hi: the segment's last key.
+// half_mask: lanes holding heads 4..7 (G = 8; zero otherwise).
 template <int G>
 __device__ __forceinline__ void compute_mpage(const uint4 *ktile, const uint4 (&vr)[4], const uint4 *qa, float4 *px,
-                                              int tok0, int m, const int (&hsl)[MAcc<G>::HPL],
+                                              int tok0, int hi, const int (&hsl)[MAcc<G>::HPL],
                                               bool masked, unsigned long long half_mask,
                                               MAcc<G> &st)
 {
@@ -201,7 +202,7 @@ __device__ __forceinline__ void compute_mpage(const uint4 *ktile, const uint4 (&
         const int tok = tok0 + t;
 #pragma unroll
         for (int v = 0; v < HPL; ++v)
-            if (tok < hsl[v] || tok > m)
+            if (tok < hsl[v] || tok > hi)
                 lg[v] = NEG_INF;
     }
     bool need = false;
@@ -259,7 +260,7 @@ __device__ __forceinline__ void compute_mpage(const uint4 *ktile, const uint4 (&
     for (int s = 0; s < 4; ++s) {
         float vf[8];
         to_f32(vr[s], vf);
-        if (masked && tok0 + 4 * s + q > m) {
+        if (masked && tok0 + 4 * s + q > hi) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 vf[e] = 0.f;
@@ -346,9 +347,9 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
     __shared__ uint4 qlds[WAVES][8][64];   // per wave: 8 A-operand registers x 64 lanes
     __shared__ float4 plds[WAVES][32];     // per wave: probabilities of the page's 16 tokens
     __shared__ uint4 klds[WAVES][16 * 16];  // per wave: the page's K rows, swizzled
-    const int nG = s.B * s.Hkv;
+    const int nS = s.B * s.Hkv * s.nseg;
     build_plan(s, st, s_off);
-    const int P = s_off[nG];
+    const int P = s_off[nS];
     if (P == 0)
         return;
     const int nW = active_workers(st.n_workers, P);
@@ -360,27 +361,27 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
         return;
     long x = (long)w * P / nW;
     const long x1 = (long)(w + 1) * P / nW;
-    int g = find_group(s_off, nG, x);
+    int sg = find_segment(s_off, nS, x);
     unsigned long long *bad = &st.stats[ST_BAD_INPUT];
     const uint16_t *kb = reinterpret_cast<const uint16_t *>(kv.k);
     const uint16_t *vb = reinterpret_cast<const uint16_t *>(kv.v);
     while (x < x1) {
-        while (s_off[g + 1] <= x)
-            ++g;
-        const long gend = min((long)s_off[g + 1], x1);
-        const int b = g / s.Hkv, kvh = g % s.Hkv;
-        const int m = st.m_buf[b];
+        while (s_off[sg + 1] <= x)
+            ++sg;
+        const long send = min((long)s_off[sg + 1], x1);
+        const Seg sd = segment(s, st, sg);
+        const int b = sd.b, kvh = sd.kvh, hi = sd.hi;
         constexpr int HPL = MAcc<G>::HPL;
         const unsigned long long half_mask = G > 4 ? __ballot((lane >> 4) & 1) : 0ULL;
+        // head h attends keys [max(start_h, lo), hi] of this segment
         int hs[G];
-        int hmax = 0, hmin = INT_MAX;
+        int hmax = 0;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            hs[h] = st.dec_start[(long)b * s.Hq + kvh * G + h];
+            hs[h] = max(st.dec_start[(long)b * s.Hq + kvh * G + h], sd.lo);
             hmax = max(hmax, hs[h]);
-            hmin = min(hmin, hs[h]);
         }
-        const int first_page = hmin / PAGE;   // the group's union span starts at hmin
+        const int first_page = sd.lo / PAGE;
         int hsl[HPL];
 #pragma unroll
         for (int v = 0; v < HPL; ++v) {
@@ -409,8 +410,8 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
             acc.L[v] = 0.f;
             acc.Ml[v] = NEG_INF;
         }
-        int page = first_page + (int)(x - s_off[g]);
-        const int last = first_page + (int)(gend - s_off[g]) - 1;
+        int page = first_page + (int)(x - s_off[sg]);
+        const int last = first_page + (int)(send - s_off[sg]) - 1;
         if constexpr (G > 4) {
             // two waves per SIMD (G = 8 needs ~220 VGPRs): the next page's
             // loads are issued before the current page is computed
@@ -423,8 +424,8 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
                     load_mpage(nxt, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page + 1, bad),
                                kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page + 1, bad));
                 const int tok0 = page * PAGE;
-                compute_mpage<G>(klds[wv], cur.v, &qlds[wv][0][0], plds[wv], tok0, m, hsl,
-                                 tok0 < hmax || tok0 + PAGE - 1 > m, half_mask, acc);
+                compute_mpage<G>(klds[wv], cur.v, &qlds[wv][0][0], plds[wv], tok0, hi, hsl,
+                                 tok0 < hmax || tok0 + PAGE - 1 > hi, half_mask, acc);
                 if (++page > last)
                     break;
                 kstore_page(nxt, klds[wv]);
@@ -443,14 +444,14 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
                            kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page, bad));
                 kstore_page(cur, klds[wv]);
                 const int tok0 = page * PAGE;
-                compute_mpage<G>(klds[wv], cur.v, &qlds[wv][0][0], plds[wv], tok0, m, hsl,
-                                 tok0 < hmax || tok0 + PAGE - 1 > m, half_mask, acc);
+                compute_mpage<G>(klds[wv], cur.v, &qlds[wv][0][0], plds[wv], tok0, hi, hsl,
+                                 tok0 < hmax || tok0 + PAGE - 1 > hi, half_mask, acc);
                 if (++page > last)
                     break;
             }
         }
-        store_msummary<G>(acc, st.partials + ((long)w + g) * G * SUMM);
-        x = gend;
+        store_msummary<G>(acc, st.partials + ((long)w + sg) * G * SUMM);
+        x = send;
     }
 }
 

@@ -390,17 +390,53 @@ __device__ __forceinline__ int group_start(const Shape &s, const State &st, int 
     return gs;
 }
 
-// Page offsets of every group's union span in the flattened work list:
-// off[g] = pages of groups before g, off[nG] = all pages of the step.
+// One segment of the work list: request b, KV head kvh, query position m,
+// keys [lo, hi] (empty when lo > hi).  Without fused amend a group's segment
+// is its whole union span [start, m]; with it, part 0 is [start, m - r] and
+// part 1 the band [m - r + 1, m] (every head's span reaches back past m - r,
+// since a hit's p is at most m - 1), so the reduce can form AS_{1:m-r} from
+// part 0 and the stored prefix alone.  seg = group * nseg + part.
+struct Seg {
+    int b, kvh, m, lo, hi;
+};
+
+__device__ __forceinline__ Seg segment(const Shape &s, const State &st, int seg)
+{
+    const int g = seg / s.nseg, part = seg % s.nseg;
+    Seg r;
+    r.b = g / s.Hkv;
+    r.kvh = g % s.Hkv;
+    r.m = st.m_buf[r.b];
+    r.lo = 0;
+    r.hi = -1;
+    if (r.m < 0)
+        return r;
+    const int gs = group_start(s, st, g);
+    if (s.nseg == 1) {
+        r.lo = gs;
+        r.hi = r.m;
+    } else {
+        const int cut = max(gs, r.m - s.r + 1);   // first key of the band part
+        r.lo = part == 0 ? gs : cut;
+        r.hi = part == 0 ? cut - 1 : r.m;
+    }
+    return r;
+}
+
+__device__ __forceinline__ int segment_pages(const Seg &sg)
+{
+    return sg.lo > sg.hi ? 0 : sg.hi / PAGE - sg.lo / PAGE + 1;
+}
+
+// Page offsets of every segment in the flattened work list: off[i] = pages
+// of the segments before i, off[nS] = all pages of the step.
 __device__ inline void build_plan(const Shape &s, const State &st, int *off)
 {
-    const int nG = s.B * s.Hkv;
-    for (int g = threadIdx.x; g < nG; g += blockDim.x) {
-        const int m = st.m_buf[g / s.Hkv];
-        off[g] = m < 0 ? 0 : (m / PAGE - group_start(s, st, g) / PAGE + 1);
-    }
+    const int nS = s.B * s.Hkv * s.nseg;
+    for (int i = threadIdx.x; i < nS; i += blockDim.x)
+        off[i] = segment_pages(segment(s, st, i));
     __syncthreads();
-    block_exclusive_scan(off, nG);
+    block_exclusive_scan(off, nS);
 }
 
 // Waves that take part: every worker gets at least MIN_PAGES_PER_WORKER pages.
@@ -415,10 +451,11 @@ __device__ __forceinline__ int page_owner(long x, int nW, int P)
     return (int)(((x + 1) * (long)nW - 1) / P);
 }
 
-// Last group g with off[g] <= x (groups with no pages are skipped by caller).
-__device__ __forceinline__ int find_group(const int *off, int nG, long x)
+// Last segment i with off[i] <= x (segments with no pages are skipped by the
+// caller).
+__device__ __forceinline__ int find_segment(const int *off, int nS, long x)
 {
-    int lo = 0, hi = nG - 1;
+    int lo = 0, hi = nS - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
         if (off[mid] <= x)
@@ -429,28 +466,30 @@ __device__ __forceinline__ int find_group(const int *off, int nG, long x)
     return lo;
 }
 
-// Block 0 of the complete grid records, per group, the first and last worker
-// whose share touches it (the slots of its partial summaries), so the reduce
-// needs no plan of its own, and adds the keys the group streams this step
-// (m - start + 1) to the group's counter, which only this block writes.
-// Groups without pages get the empty range (0, -1).
+// Block 0 of the complete grid records, per segment, the first and last
+// worker whose share touches it (the slots of its partial summaries), so the
+// reduce needs no plan of its own, and adds the keys each group streams this
+// step (m - start + 1, its segments together) to the group's counter, which
+// only this block writes.  Empty segments get the range (0, -1).
 __device__ inline void publish_plan(const Shape &s, const State &st, const int *off, int nW)
 {
-    const int nG = s.B * s.Hkv, P = off[nG];
-    for (int g = threadIdx.x; g < nG; g += blockDim.x) {
+    const int nG = s.B * s.Hkv, nS = nG * s.nseg, P = off[nS];
+    for (int i = threadIdx.x; i < nS; i += blockDim.x) {
         int2 r = make_int2(0, -1);
-        if (off[g + 1] > off[g]) {
-            r = make_int2(page_owner(off[g], nW, P), page_owner((long)off[g + 1] - 1, nW, P));
-            const int m = st.m_buf[g / s.Hkv];
+        if (off[i + 1] > off[i])
+            r = make_int2(page_owner(off[i], nW, P), page_owner((long)off[i + 1] - 1, nW, P));
+        reinterpret_cast<int2 *>(st.grp_parts)[i] = r;
+    }
+    for (int g = threadIdx.x; g < nG; g += blockDim.x) {
+        const int m = st.m_buf[g / s.Hkv];
+        if (m >= 0)
             st.grp_stats[(long)g * GRP_NSTAT + GS_TOK_CRIT] +=
                 (unsigned long long)(m - group_start(s, st, g) + 1);
-        }
-        reinterpret_cast<int2 *>(st.grp_parts)[g] = r;
     }
 }
 
-// Bytes of LDS the plan (one int per group, plus the total) occupies.
-inline size_t plan_lds_bytes(const Shape &s) { return (size_t)(s.B * s.Hkv + 1) * sizeof(int); }
+// Bytes of LDS the plan (one int per segment, plus the total) occupies.
+inline size_t plan_lds_bytes(const Shape &s) { return (size_t)(s.B * s.Hkv * s.nseg + 1) * sizeof(int); }
 
 }  // namespace
 }  // namespace mac

@@ -13,13 +13,15 @@
 //   dec_p      [B][Hq] int32        matched position (-1 miss)
 //   dec_start  [B][Hq] int32        first key of the head's span
 //   dec_rel    [B][Hq]              relative distance of the nearest entry
-//   grp_parts  [B][Hkv][2] int32    first and last worker whose partial covers the group
+//   grp_parts  [B][Hkv][nseg][2] int32  first and last worker whose partial covers a segment
 //   tile_best  [B][Hq][W/64][3]     W > 64: nearest entry of each 64-slot tile
-//   partials   [NW + B*Hkv][G][SUMM] per-(worker, group) unnormalised summaries
+//   partials   [NW + B*Hkv*nseg][G][SUMM] per-(worker, segment) unnormalised summaries
 //   as_full    [B][Hq][SUMM]        AS_{1:m} of this step, input of amend
 //   stats      [MAC_NSTAT] + [B*Hq][HEAD_NSTAT] + [B*Hkv][GRP_NSTAT] uint64 counters
 // A group's union span (the keys complete streams for it) starts at the
 // smallest first key of its heads' spans; the plan derives it from dec_start.
+// The work list is cut into segments: one per group, or with fused amend two
+// (the span up to m - r, then the band [m - r + 1, m]).
 // M values inside the library are in log2 units of the scaled logit
 // (s * log2 e); every summary the library stores uses the same units.
 #pragma once
@@ -66,12 +68,13 @@ struct Shape {
     int32_t B, Hq, Hkv, G, W, r;
     float tau, scale_log2;  // scale_log2 = sm_scale * log2(e)
     int32_t reuse;          // 0: every head misses
+    int32_t nseg;           // work-list segments per group: 1, or 2 when amend is fused
 };
 
 struct State {
     float *ring_q, *ring_s, *q_copy, *q_rot, *partials, *as_full, *dec_rel;
     int32_t *ring_pos, *m_buf, *dec_slot, *dec_p, *dec_start;
-    int32_t *grp_parts;       // [B*Hkv][2] worker range of each group's partials (complete -> reduce)
+    int32_t *grp_parts;       // [B*Hkv*nseg][2] worker range of each segment's partials (complete -> reduce)
     unsigned long long *stats;        // [MAC_NSTAT], then the two blocks below
     unsigned long long *head_stats;   // [B*Hq][HEAD_NSTAT]
     unsigned long long *grp_stats;    // [B*Hkv][GRP_NSTAT]
@@ -89,7 +92,9 @@ hipError_t launch_match(const Shape &s, const State &st, const KvView &kv, const
                         hipStream_t stream);
 hipError_t launch_complete(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
                            int n_blocks, hipStream_t stream);
-hipError_t launch_reduce(const Shape &s, const State &st, float *out, hipStream_t stream);
+// slot_new: the ring slot a fused amend writes (ignored when nseg == 1).
+hipError_t launch_reduce(const Shape &s, const State &st, float *out, int slot_new,
+                         hipStream_t stream);
 hipError_t launch_amend(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
                         int slot_new, hipStream_t stream);
 hipError_t launch_append(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,

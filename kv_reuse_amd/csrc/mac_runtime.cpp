@@ -75,10 +75,17 @@ struct Sizes {
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Work-list segments per group (two when amend is fused into the step).
+int segments_per_group(const mac_config &c)
+{
+    const bool reuse = !(c.flags & MAC_F_DISABLE_REUSE) && c.tau >= 0.f;
+    return (reuse && (c.flags & MAC_F_FUSED_AMEND)) ? 2 : 1;
+}
+
 Sizes sizes_for(const mac_config &c, int n_workers)
 {
     const size_t B = c.batch, Hq = c.num_q_heads, Hkv = c.num_kv_heads, W = c.ring_size;
-    const size_t G = Hq / Hkv;
+    const size_t G = Hq / Hkv, nseg = segments_per_group(c);
     Sizes s;
     s.ring_q = round256(B * Hq * W * mac::D * sizeof(float));
     s.ring_s = round256(B * Hq * W * mac::SUMM * sizeof(float));
@@ -87,8 +94,8 @@ Sizes sizes_for(const mac_config &c, int n_workers)
     s.m_buf = round256(B * sizeof(int32_t));
     s.dec_i = round256(B * Hq * sizeof(int32_t));
     s.dec_f = round256(B * Hq * sizeof(float));
-    s.grp_parts = round256(B * Hkv * 2 * sizeof(int32_t));
-    s.partials = round256(((size_t)n_workers + B * Hkv) * G * mac::SUMM * sizeof(float));
+    s.grp_parts = round256(B * Hkv * nseg * 2 * sizeof(int32_t));
+    s.partials = round256(((size_t)n_workers + B * Hkv * nseg) * G * mac::SUMM * sizeof(float));
     s.as_full = round256(B * Hq * mac::SUMM * sizeof(float));
     s.stats = round256(mac::stats_count((long)(B * Hq), (long)(B * Hkv)) *
                        sizeof(unsigned long long));
@@ -161,7 +168,7 @@ mac_status validate(const mac_config *c, std::string &why)
         return MAC_EUNSUPPORTED;
     }
     const uint32_t known = MAC_F_DISABLE_REUSE | MAC_F_SYNC_AMEND | MAC_F_TIMING |
-                           MAC_F_RECORD_DEBUG;
+                           MAC_F_RECORD_DEBUG | MAC_F_FUSED_AMEND;
     if (c->flags & ~known) {
         why = "unknown flag bits";
         return MAC_EINVAL;
@@ -289,7 +296,8 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
         return bail(MAC_EHIP, "cannot query the compute-unit count");
 
     const int G = cfg->num_q_heads / cfg->num_kv_heads;
-    const size_t plan_lds = (size_t)(cfg->batch * cfg->num_kv_heads + 1) * sizeof(int);
+    const size_t plan_lds =
+        (size_t)(cfg->batch * cfg->num_kv_heads * segments_per_group(*cfg) + 1) * sizeof(int);
     h->n_blocks = n_cu * mac::complete_blocks_per_cu(h->kv_fp32, G, plan_lds);
     h->st.n_workers = h->n_blocks * mac::WAVES;
 
@@ -350,6 +358,7 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     const double scale = cfg->sm_scale > 0.f ? (double)cfg->sm_scale : 1.0 / std::sqrt((double)mac::D);
     h->shape.scale_log2 = (float)(scale * 1.4426950408889634);
     h->shape.reuse = !(cfg->flags & MAC_F_DISABLE_REUSE) && cfg->tau >= 0.f;
+    h->shape.nseg = segments_per_group(*cfg);
 
     if (amend_stream) {
         h->amend_stream = (hipStream_t)amend_stream;
@@ -443,10 +452,14 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
     // The complete kernel is a persistent grid with equal static shares per
     // wave: a kernel still holding CU slots when it launches delays some of
     // its waves and with them the whole launch (measured: +35 % when an amend
-    // of another layer overlapped its first microsecond).  So complete waits
-    // for every amend already queued on the amend stream (this handle's or
-    // another layer's sharing it); amend still overlaps append and match.
-    if (h->amend_stream != st && !(h->cfg.flags & MAC_F_SYNC_AMEND) && h->shape.reuse) {
+    // of another layer overlapped its first microsecond).  So on an amend
+    // stream the caller supplied (which other layers may share), complete
+    // waits for every amend already queued there; amend still overlaps append
+    // and match.  A stream the handle owns holds only this handle's amend,
+    // which match already waited for (the extra cross-queue wait costs ~10 us).
+    const bool fused = h->shape.nseg == 2;
+    if (!h->own_amend && h->amend_stream != st && !(h->cfg.flags & MAC_F_SYNC_AMEND) &&
+        h->shape.reuse && !fused) {
         MAC_HIP(h, hipEventRecord(h->ev_drain, h->amend_stream));
         MAC_HIP(h, hipStreamWaitEvent(st, h->ev_drain, 0));
     }
@@ -455,12 +468,12 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
     MAC_HIP(h, mac::launch_complete(h->shape, h->st, v, h->kv_fp32, h->n_blocks, st));
     if (timing)
         MAC_HIP(h, hipEventRecord(h->tm[2], st));
-    MAC_HIP(h, mac::launch_reduce(h->shape, h->st, out, st));
+    const int slot_new = (int)(h->calls % h->cfg.ring_size);
+    MAC_HIP(h, mac::launch_reduce(h->shape, h->st, out, slot_new, st));
     if (timing)
         MAC_HIP(h, hipEventRecord(h->tm[3], st));
 
-    if (h->shape.reuse) {
-        const int slot_new = (int)(h->calls % h->cfg.ring_size);
+    if (h->shape.reuse && !fused) {
         hipStream_t as = (h->cfg.flags & MAC_F_SYNC_AMEND) ? st : h->amend_stream;
         if (as != st) {
             MAC_HIP(h, hipEventRecord(h->ev_attn, st));
@@ -521,7 +534,8 @@ mac_status mac_stats(mac_handle h, mac_stats_t *out)
         if (hipEventElapsedTime(&t, h->tm[1], h->tm[2]) == hipSuccess) out->last_us_complete = t * 1e3f;
         if (hipEventElapsedTime(&t, h->tm[2], h->tm[3]) == hipSuccess) out->last_us_reduce = t * 1e3f;
         if (hipEventElapsedTime(&t, h->tm[0], h->tm[3]) == hipSuccess) out->last_us_attention = t * 1e3f;
-        if (h->shape.reuse && hipEventElapsedTime(&t, h->tm[4], h->tm[5]) == hipSuccess)
+        if (h->shape.reuse && h->shape.nseg == 1 &&
+            hipEventElapsedTime(&t, h->tm[4], h->tm[5]) == hipSuccess)
             out->last_us_amend = t * 1e3f;
     }
     return MAC_OK;

@@ -7,21 +7,54 @@ namespace mac {
 namespace {
 
 // ================================================================== reduce
-// Grid (Hq, B), 1024 threads: one block per (request, query head).  The
-// head's group has n partial summaries (slots w + g for the worker range the
-// complete kernel published); n is a few dozen when most groups stream their
-// whole context and reaches the thousands when one long span shares the
-// workers with short ones.  The block is laid out as RLANES partials x RCH
-// float4 column chunks: thread (k, c) folds chunk c of partials k, k + RLANES,
-// ... into an online-softmax state (running max, rescaled sums), RUNROLL
-// partials per round with all their loads in flight; the RLANES states are
-// then combined in LDS.  The head is merged (+) with the matched entry's
-// stored AS_{1:p-r}; out receives the normalised output and AS_{1:m} is kept
-// for amend.
+// Grid (Hq, B), 1024 threads: one block per (request, query head).  Each
+// segment of the head's group has n partial summaries (slots w + segment for
+// the worker range the complete kernel published); n is a few dozen when
+// most groups stream their whole context and reaches the thousands when one
+// long span shares the workers with short ones.  The block is laid out as
+// RLANES partials x RCH float4 column chunks: thread (k, c) folds chunk c of
+// partials k, k + RLANES, ... into an online-softmax state (running max,
+// rescaled sums), RUNROLL partials per round with all their loads in flight;
+// the RLANES states are then combined in LDS.
+//
+// Then, per head, with the matched entry's stored prefix S = AS_{1:p-r}
+// (EMPTY on a miss) and (+) the log-domain merge:
+//   one segment:  O = S (+) span; AS_{1:m} = O is kept for amend;
+//   fused amend:  X = S (+) part 0 is AS_{1:m-r} and goes into the ring slot
+//                 of this step together with the pre-RoPE query and m;
+//                 O = X (+) band.
+// out receives O's normalised output.
 constexpr int REDUCE_THREADS = 1024;
 constexpr int RCH = D / 4;                       // float4 chunks of a row
 constexpr int RLANES = REDUCE_THREADS / RCH;     // partials combined side by side
 constexpr int RUNROLL = 4;                       // partials per round of loads
+
+// A summary as threads 0..RCH-1 hold it: normalised output chunk c (o), the
+// reference max M (log2 units) and the normaliser L; EMPTY is (0, -inf, 0).
+struct Sum4 {
+    float4 o;
+    float M, L;
+};
+
+// X (+) Y for the chunk this thread holds.
+__device__ __forceinline__ Sum4 merge(const Sum4 &x, const Sum4 &y)
+{
+    if (!(y.L > 0.f))
+        return x;
+    if (!(x.L > 0.f))
+        return y;
+    const float Mn = fmaxf(x.M, y.M);
+    const float ca = x.L * exp2f(x.M - Mn), cb = y.L * exp2f(y.M - Mn);
+    const float Ln = ca + cb;
+    Sum4 r;
+    r.o.x = (ca * x.o.x + cb * y.o.x) / Ln;
+    r.o.y = (ca * x.o.y + cb * y.o.y) / Ln;
+    r.o.z = (ca * x.o.z + cb * y.o.z) / Ln;
+    r.o.w = (ca * x.o.w + cb * y.o.w) / Ln;
+    r.M = Mn;
+    r.L = Ln;
+    return r;
+}
 
 __device__ __forceinline__ void fold(float4 &a, float &L, float &M, const float4 (&ov)[RUNROLL],
                                      const float (&mv)[RUNROLL], const float (&lv)[RUNROLL], int cnt)
@@ -53,35 +86,19 @@ __device__ __forceinline__ void fold(float4 &a, float &L, float &M, const float4
     }
 }
 
-__global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(Shape s, State st,
-                                                                float *__restrict__ out)
-{
-    __shared__ float4 red_o[RLANES][RCH];
-    __shared__ float red_l[RLANES], red_m[RLANES];
-    const int b = blockIdx.y, h = blockIdx.x, kvh = h / s.G, hh = h % s.G;
-    const int g = b * s.Hkv + kvh;
-    const int t = threadIdx.x;
-    const int c = t % RCH, k = t / RCH;
-    const long idx = (long)b * s.Hq + h;
-    // the stored summary to merge with (threads 0..RCH-1)
-    float4 so = make_float4(0.f, 0.f, 0.f, 0.f);
-    float Ms = NEG_INF, Ls = 0.f;
-    if (t < RCH) {
-        const int slot = st.dec_slot[idx];
-        if (slot >= 0) {
-            const float *rs = st.ring_s + (idx * s.W + slot) * SUMM;
-            so = *reinterpret_cast<const float4 *>(rs + 4 * c);
-            Ms = rs[D];
-            Ls = rs[D + 1];
-        }
-    }
-    const int2 range = reinterpret_cast<const int2 *>(st.grp_parts)[g];
-    if (st.m_buf[b] < 0 || range.y < range.x)
-        return;   // idle request: match wrote its zero output
-    const int n = range.y - range.x + 1;
-    const long pstride = (long)s.G * SUMM;   // one slot
-    const float *part = st.partials + ((long)range.x + g) * pstride + hh * SUMM;
+struct ReduceLds {
+    float4 o[RLANES][RCH];
+    float l[RLANES], m[RLANES];
+};
 
+// Combine the n partials at part, part + pstride, ... (this head's rows) into
+// a normalised summary, valid in threads 0..RCH-1; EMPTY when n = 0.  Every
+// thread of the block calls it; reuse: another call follows, so the LDS is
+// released by a second barrier.
+__device__ __forceinline__ Sum4 combine_partials(const float *part, int n, long pstride, ReduceLds &lds,
+                                 bool reuse)
+{
+    const int t = threadIdx.x, c = t % RCH, k = t / RCH;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     float L = 0.f, M = NEG_INF;
     for (int i = k; i < n; i += RUNROLL * RLANES) {
@@ -90,9 +107,8 @@ __global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(Shape s, State s
         const int cnt = min(RUNROLL, (n - i + RLANES - 1) / RLANES);
 #pragma unroll
         for (int u = 0; u < RUNROLL; ++u) {
-            const int iu = i + u * RLANES;
             if (u < cnt) {
-                const float *pi = part + (long)iu * pstride;
+                const float *pi = part + (long)(i + u * RLANES) * pstride;
                 ov[u] = *reinterpret_cast<const float4 *>(pi + 4 * c);
                 mv[u] = pi[D];
                 lv[u] = pi[D + 1];
@@ -100,64 +116,120 @@ __global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(Shape s, State s
         }
         fold(a, L, M, ov, mv, lv, cnt);
     }
-    red_o[k][c] = a;
+    lds.o[k][c] = a;
     if (c == 0) {
-        red_l[k] = L;
-        red_m[k] = M;
+        lds.l[k] = L;
+        lds.m[k] = M;
     }
     __syncthreads();
+    Sum4 r;
+    r.o = make_float4(0.f, 0.f, 0.f, 0.f);
+    r.M = NEG_INF;
+    r.L = 0.f;
+    if (t < RCH) {
+        float Mx = lds.m[0];
+#pragma unroll
+        for (int q = 1; q < RLANES; ++q)
+            Mx = fmaxf(Mx, lds.m[q]);
+        const float base = Mx == NEG_INF ? 0.f : Mx;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        float Lt = 0.f;
+#pragma unroll
+        for (int q = 0; q < RLANES; ++q) {
+            const float sc = exp2f(lds.m[q] - base);   // 0 for a lane that saw no partial
+            const float4 x = lds.o[q][c];
+            o.x = fmaf(x.x, sc, o.x);
+            o.y = fmaf(x.y, sc, o.y);
+            o.z = fmaf(x.z, sc, o.z);
+            o.w = fmaf(x.w, sc, o.w);
+            Lt = fmaf(lds.l[q], sc, Lt);
+        }
+        if (Lt > 0.f) {
+            r.o = make_float4(o.x / Lt, o.y / Lt, o.z / Lt, o.w / Lt);
+            r.M = Mx;
+            r.L = Lt;
+        }
+    }
+    if (reuse)
+        __syncthreads();
+    return r;
+}
+
+__global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(Shape s, State st,
+                                                                float *__restrict__ out,
+                                                                int slot_new)
+{
+    __shared__ ReduceLds lds;
+    const int b = blockIdx.y, h = blockIdx.x, kvh = h / s.G, hh = h % s.G;
+    const int g = b * s.Hkv + kvh;
+    const int t = threadIdx.x, c = t % RCH;
+    const long idx = (long)b * s.Hq + h;
+    // the stored summary to merge with (threads 0..RCH-1)
+    Sum4 S;
+    S.o = make_float4(0.f, 0.f, 0.f, 0.f);
+    S.M = NEG_INF;
+    S.L = 0.f;
+    if (t < RCH) {
+        const int slot = st.dec_slot[idx];
+        if (slot >= 0) {
+            const float *rs = st.ring_s + (idx * s.W + slot) * SUMM;
+            S.o = *reinterpret_cast<const float4 *>(rs + 4 * c);
+            S.M = rs[D];
+            S.L = rs[D + 1];
+        }
+    }
+    // loaded together with the position (independent loads, one round trip)
+    const int2 *ranges = reinterpret_cast<const int2 *>(st.grp_parts);
+    const int seg0 = g * s.nseg;
+    const int2 rg0 = ranges[seg0];
+    const int2 rg1 = s.nseg == 2 ? ranges[seg0 + 1] : make_int2(0, -1);
+    const int m = st.m_buf[b];
+    if (m < 0)
+        return;   // idle request: match wrote its zero output, nothing is stored
+    const long pstride = (long)s.G * SUMM;   // one slot
+    const Sum4 part0 = combine_partials(st.partials + ((long)rg0.x + seg0) * pstride + hh * SUMM,
+                                        rg0.y - rg0.x + 1, pstride, lds, s.nseg == 2);
+    Sum4 part1 = part0;
+    if (s.nseg == 2)
+        part1 = combine_partials(st.partials + ((long)rg1.x + seg0 + 1) * pstride + hh * SUMM,
+                                 rg1.y - rg1.x + 1, pstride, lds, false);
     if (t >= RCH)
         return;
-    float Mx = red_m[0];
-#pragma unroll
-    for (int r = 1; r < RLANES; ++r)
-        Mx = fmaxf(Mx, red_m[r]);
-    const float base = Mx == NEG_INF ? 0.f : Mx;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    float Lt = 0.f;
-#pragma unroll
-    for (int r = 0; r < RLANES; ++r) {
-        const float sc = exp2f(red_m[r] - base);   // 0 for a lane that saw no partial
-        const float4 x = red_o[r][c];
-        o.x = fmaf(x.x, sc, o.x);
-        o.y = fmaf(x.y, sc, o.y);
-        o.z = fmaf(x.z, sc, o.z);
-        o.w = fmaf(x.w, sc, o.w);
-        Lt = fmaf(red_l[r], sc, Lt);
+    Sum4 O;
+    if (s.nseg == 1) {
+        O = merge(S, part0);
+        float *asf = st.as_full + idx * SUMM;
+        *reinterpret_cast<float4 *>(asf + 4 * c) = O.o;
+        if (t == 0) {
+            asf[D] = O.M;
+            asf[D + 1] = O.L;
+        }
+    } else {
+        const Sum4 X = merge(S, part0);   // AS_{1:m-r}
+        O = merge(X, part1);
+        float *dst = st.ring_s + (idx * s.W + slot_new) * SUMM;
+        *reinterpret_cast<float4 *>(dst + 4 * c) = X.o;
+        *reinterpret_cast<float4 *>(st.ring_q + (idx * s.W + slot_new) * D + 4 * c) =
+            *reinterpret_cast<const float4 *>(st.q_copy + idx * D + 4 * c);
+        if (t == 0) {
+            dst[D] = X.M;
+            dst[D + 1] = X.L;
+            if (h == 0)
+                st.ring_pos[(long)b * s.W + slot_new] = m;
+        }
     }
-    o.x /= Lt;
-    o.y /= Lt;
-    o.z /= Lt;
-    o.w /= Lt;
-    float Mo = Mx, Lo = Lt;
-    if (Ls > 0.f) {
-        const float Mn = fmaxf(Ms, Mx);
-        const float ca = Ls * exp2f(Ms - Mn), cb = Lt * exp2f(Mx - Mn);
-        const float Ln = ca + cb;
-        o.x = (ca * so.x + cb * o.x) / Ln;
-        o.y = (ca * so.y + cb * o.y) / Ln;
-        o.z = (ca * so.z + cb * o.z) / Ln;
-        o.w = (ca * so.w + cb * o.w) / Ln;
-        Mo = Mn;
-        Lo = Ln;
-    }
-    *reinterpret_cast<float4 *>(out + idx * D + 4 * c) = o;
-    float *asf = st.as_full + idx * SUMM;
-    *reinterpret_cast<float4 *>(asf + 4 * c) = o;
-    if (t == 0) {
-        asf[D] = Mo;
-        asf[D + 1] = Lo;
-    }
+    *reinterpret_cast<float4 *>(out + idx * D + 4 * c) = O.o;
 }
 
 }  // namespace
 
-hipError_t launch_reduce(const Shape &s, const State &st, float *out, hipStream_t stream)
+hipError_t launch_reduce(const Shape &s, const State &st, float *out, int slot_new,
+                         hipStream_t stream)
 {
-    if (!supported_group(s.G))
+    if (!supported_group(s.G) || s.nseg < 1 || s.nseg > 2)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(reduce_kernel, dim3(s.Hq, s.B), dim3(REDUCE_THREADS), 0, stream, s, st,
-                       out);
+                       out, slot_new);
     return hipGetLastError();
 }
 

@@ -114,6 +114,31 @@ def test_large_windows(gpu_lib, W, steps):
     assert hits > 0
 
 
+_FUSED_CASES = {
+    "cpu4k_fp32": (lambda: scaled(get_config("cpu4k"), steps=120), {}),
+    "paged_mixed": (lambda: scaled(get_config("b16_128k"), B=4, C=3000, steps=48), {}),
+    "moe_g8": (lambda: scaled(get_config("moe_122k"), B=2, C=2500, steps=40), {"r": 1024}),
+    "ragged": (lambda: scaled(get_config("b16_128k"), B=6, C=1200, steps=40, rho=("const", 0.96)),
+               {"prefill": [1200, 1199, 1185, 1024, 777, 17]}),
+    "shorter_than_band": (lambda: scaled(get_config("b16_128k"), B=2, C=3, steps=100, W=16, r=64,
+                                         rho=("const", 0.96)), {}),
+    "window_100": (lambda: scaled(get_config("b16_128k"), B=2, C=600, steps=150, W=100,
+                                  rho=("const", 0.96)), {}),
+    "band_of_one": (lambda: scaled(get_config("cpu4k"), C=300, steps=40, W=1, r=1, kv="bf16"), {}),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_FUSED_CASES))
+def test_fused_amend_matches_oracle(gpu_lib, case):
+    """MAC_F_FUSED_AMEND: the reduce stores AS_{1:m-r} as the stored prefix
+    merged with the part of the span before the band; the oracle amends with
+    the log-domain removal.  Same decisions, outputs within tolerance."""
+    import kv_reuse_amd as mac
+    make, kw = _FUSED_CASES[case]
+    w = make()
+    _run(w, w.steps, flags=mac.MAC_F_FUSED_AMEND, **kw)
+
+
 def test_disable_reuse_is_full_attention(gpu_lib):
     import kv_reuse_amd as mac
     import oracle
