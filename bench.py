@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline-kernel", action="store_true")
     ap.add_argument("--no-32k", action="store_true", help="skip the 32K speedup point")
+    ap.add_argument("--figures", action="store_true",
+                    help="synthetic analogs of the pages' Figures 4, 5 and 8 (one JSON line)")
     ap.add_argument("--fused-amend", action="store_true",
                     help="MAC passes with MAC_F_FUSED_AMEND (the reduce updates the ring)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -96,7 +98,7 @@ class Bench:
                                      num_pages=self.kc.shape[0] if paged else 0)
         self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
 
-    def step(self, t, q, k_new, v_new, scrub=None):
+    def step(self, t, q, k_new, v_new, scrub=None, override=None):
         """One decode step.  Returns the counters (synchronises) with the last
         step's kernel times (MAC_F_TIMING) and "span_us": the decode call's work
         on the main stream (match -> reduce) between two stream events, with
@@ -113,7 +115,7 @@ class Bench:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(self.stream)
-        self.layer.decode_step(self.view, q, self.out, None, self.stream)
+        self.layer.decode_step(self.view, q, self.out, override, self.stream)
         e1.record(self.stream)
         st = self.layer.stats()            # synchronises; last step's kernel times
         st["span_us"] = e0.elapsed_time(e1) * 1e3
@@ -283,6 +285,135 @@ def contgen(args):
     print(json.dumps(line), flush=True)
 
 
+def figures(args):
+    """Synthetic analogs of the pages' Figures 5, 4 and 8 (no datasets, no
+    model queries; the AR(1) recipes of the workloads):
+      fig5: head hit rate and skipped-key share vs tau and window W, and vs the
+            query correlation rho (128K x 16 paged cache);
+      fig4: MAC-vs-full relative output error vs the reuse gap m - p (hits
+            forced through the override input) and the band r;
+      fig8: match latency vs query heads per KV head G and window W.
+    Prints one JSON line."""
+    import torch
+    import kv_reuse_amd as mac
+    from workloads import get_config, kv_logical, page_table, queries, scaled, to_paged
+    base = scaled(get_config("b16_128k"), steps=40)
+    total = base.steps
+    K, V = kv_logical(base, "cuda")
+    idx = torch.arange(base.C, base.C + total, device="cuda")
+    k_rows = K[:, :, idx].permute(2, 0, 1, 3).contiguous()
+    v_rows = V[:, :, idx].permute(2, 0, 1, 3).contiguous()
+    tab = page_table(base)
+    cache = (to_paged(K, tab), to_paged(V, tab), True, torch.as_tensor(tab, device="cuda"))
+    del K, V
+    B, Hq, Hkv = base.B, base.Hq, base.Hkv
+
+    def rates(w, warm=4, steps=8):
+        qd = torch.as_tensor(queries(w, steps=warm + steps), device="cuda")
+        bn = Bench(w, 0, *cache)
+        hits = toks = full = 0
+        att, prev = [], None
+        for t in range(warm + steps):
+            st = bn.step(t, qd[t], k_rows[t], v_rows[t])
+            if t >= warm:
+                hits += st["hits"] - prev["hits"]
+                toks += st["kv_tokens_critical"] - prev["kv_tokens_critical"]
+                full += (w.C + t + 1) * B * Hkv
+                att.append(st["span_us"])
+            prev = st
+        bn.layer.close()
+        return {"head_hit_rate": hits / (steps * B * Hq), "skipped_keys": 1.0 - toks / full,
+                "attention_us": float(np.mean(att))}
+
+    fig5 = []
+    for tau in (0.1, 0.2, 0.3, 0.45, 0.6):
+        for W in (16, 32, 256, 1024):
+            r = rates(scaled(base, tau=tau, W=W))
+            r.update({"tau": tau, "W": W})
+            fig5.append(r)
+    full_us = rates(scaled(base, tau=-1.0))["attention_us"]
+    fig5_rho = []
+    for rho in (0.9, 0.95, 0.96, 0.97, 0.98, 0.99):
+        r = rates(scaled(base, rho=("const", rho)))
+        r.update({"rho": rho, "speedup_vs_full": full_us / r["attention_us"]})
+        fig5_rho.append(r)
+
+    # fig4: every head forced to reuse the entry from gap steps back.  With
+    # fresh summaries the warm-up steps are forced misses, so each stored
+    # AS_{1:p-r} is exact attention of q_p; with natural decisions hits chain
+    # (a hit's stored summary inherits the prefix it reused), so the prefix a
+    # late step reuses was computed for a query many steps older.
+    wq = scaled(base, rho=("const", 0.97))
+    qd = torch.as_tensor(queries(wq, steps=total), device="cuda")
+    warm, steps = 33, 4
+
+    def outputs(w, flags, gap=0, fresh=False):
+        bn = Bench(w, flags, *cache)
+        res = []
+        for t in range(warm + steps):
+            ov = None
+            if gap and t >= warm:
+                ov = torch.full((B, Hq), w.C + t - gap, dtype=torch.int32, device="cuda")
+            elif fresh and t < warm:
+                ov = torch.full((B, Hq), -1, dtype=torch.int32, device="cuda")
+            st = bn.step(t, qd[t], k_rows[t], v_rows[t], override=ov)
+            if t >= warm:
+                res.append(bn.out.clone())
+                if gap:
+                    assert st["override_invalid"] == 0, "forced position not in the ring"
+        bn.layer.close()
+        return res
+
+    def rel_err(got, ref):
+        e = torch.stack([(g - f).norm(dim=-1) / f.norm(dim=-1) for g, f in zip(got, ref)])
+        return float(e.mean()), float(e.max())
+
+    ref = outputs(wq, mac.MAC_F_DISABLE_REUSE)
+    fig4 = []
+    for r in (64, 256, 1024):
+        for gap in (1, 2, 4, 8, 16, 32):
+            mean_e, max_e = rel_err(outputs(scaled(wq, r=r), 0, gap, fresh=True), ref)
+            fig4.append({"r": r, "gap": gap, "summaries": "fresh", "mean_rel_err": mean_e,
+                         "max_rel_err": max_e})
+        mean_e, max_e = rel_err(outputs(scaled(wq, r=r), 0), ref)
+        fig4.append({"r": r, "gap": None, "summaries": "natural chains (33 steps)",
+                     "mean_rel_err": mean_e, "max_rel_err": max_e})
+    del cache, k_rows, v_rows
+    torch.cuda.empty_cache()
+
+    # fig8: match latency (library HIP events) vs G and W at a short context
+    fig8 = []
+    for G in (1, 2, 4, 8):
+        w8 = scaled(base, Hkv=Hq // G, C=4096, steps=12, rho=("const", 0.97))
+        K, V = kv_logical(w8, "cuda")
+        idx = torch.arange(w8.C, w8.C + 12, device="cuda")
+        kr = K[:, :, idx].permute(2, 0, 1, 3).contiguous()
+        vr = V[:, :, idx].permute(2, 0, 1, 3).contiguous()
+        t8 = page_table(w8)
+        c8 = (to_paged(K, t8), to_paged(V, t8), True, torch.as_tensor(t8, device="cuda"))
+        del K, V
+        q8 = torch.as_tensor(queries(w8, steps=12), device="cuda")
+        for W in (16, 32, 64, 256, 1024, 2048):
+            bn = Bench(scaled(w8, W=W), mac.MAC_F_TIMING, *c8)
+            us = []
+            for t in range(12):
+                st = bn.step(t, q8[t], kr[t], vr[t])
+                if t >= 4:
+                    us.append(st["last_us_match"])
+            bn.layer.close()
+            fig8.append({"G": G, "W": W, "match_us": float(np.mean(us)),
+                         "ring_bytes": B * Hq * W * w8.d * 4})
+        del c8, kr, vr
+        torch.cuda.empty_cache()
+
+    print(json.dumps({"figures": {"fig5_tau_window": fig5, "fig5_rho": fig5_rho,
+                                  "full_attention_us": full_us, "fig4_gap_band": fig4,
+                                  "fig8_match": fig8},
+                      "config": {"workload": "b16_128k", "batch": B, "context": base.C,
+                                 "q_heads": Hq, "kv_heads": Hkv, "data": "synthetic"}}),
+          flush=True)
+
+
 def oracle_baseline(w, K, V, qs, n_req, n_steps):
     """fp64 oracle, as it stands, on the first n_req requests for n_steps steps."""
     import oracle
@@ -315,6 +446,9 @@ def main():
     torch.cuda.set_device(0)
     if args.config == "contgen":
         contgen(args)
+        return
+    if args.figures:
+        figures(args)
         return
     w = get_config(args.config)
     if args.r:
