@@ -14,13 +14,19 @@ from workloads import get_config, scaled
 pytestmark = pytest.mark.gpu
 
 
-def test_layers_share_amend_stream_and_match_oracle(gpu_lib):
+@pytest.mark.parametrize("fused", [False, True])
+def test_layers_share_amend_stream_and_match_oracle(gpu_lib, fused):
+    """Default: amend of every layer on one shared stream.  Fused amend: no
+    amend stream work at all, the layers' reduce kernels update their rings."""
     import torch
+    import kv_reuse_amd as mac
     from gpu_harness import Lockstep
     w = scaled(get_config("contgen"), B=4, C=1500, steps=40, layers=3, jump_every=16)
-    print("case contgen layers", w.layers, "B", w.B, "C", w.C, flush=True)
+    print("case contgen layers", w.layers, "B", w.B, "C", w.C, "fused", fused, flush=True)
     amend = torch.cuda.Stream()
-    runs = [Lockstep(w, layer=layer, amend_stream=amend) for layer in range(w.layers)]
+    flags = mac.MAC_F_FUSED_AMEND if fused else 0
+    runs = [Lockstep(w, layer=layer, amend_stream=amend, flags=flags)
+            for layer in range(w.layers)]
     hits = np.zeros(w.layers, int)
     try:
         for t in range(w.steps):

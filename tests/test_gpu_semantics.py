@@ -154,10 +154,13 @@ def test_idle_request_outputs_zero_and_stores_nothing():
         ls.close()
 
 
-def test_stats_match_oracle_counts():
+@pytest.mark.parametrize("fused", [False, True])
+def test_stats_match_oracle_counts(fused):
+    """Counters against the oracle's decisions and key counts; amend re-reads
+    r keys per active group and step (none when it is fused into the reduce)."""
     from gpu_harness import Lockstep
     w = _case(steps=20)
-    ls = Lockstep(w)
+    ls = Lockstep(w, flags=mac.MAC_F_FUSED_AMEND if fused else 0)
     try:
         hits = toks = 0
         for t in range(20):
@@ -169,6 +172,8 @@ def test_stats_match_oracle_counts():
         assert st["hits"] == hits and st["misses"] == 20 * w.B * w.Hq - hits
         assert st["kv_tokens_critical"] == toks
         assert st["kv_bytes_critical"] == toks * 2 * w.d * 2
+        amend_toks = 0 if fused else 20 * w.B * w.Hkv * w.r   # every step has m >= r here
+        assert st["kv_tokens_amend"] == amend_toks
         assert st["bad_input"] == 0 and st["aux_bytes"] > 0
     finally:
         ls.close()
