@@ -11,6 +11,7 @@ What each function follows (MAC-Attention, arXiv 2604.00235, paper card):
   merge ....... log-domain merge (+) (Figure 2 (b))
   remove ...... log-domain removal (-) (Figure 2 (c))
   nearest ..... pre-RoPE L2 nearest neighbour over the ring (Figure 2 (a))
+  round_bf16 .. ring queries kept in bfloat16 (F_RING_BF16; Table 7's memory)
   Oracle.step . match -> complete -> amend, one decode call (Figure 2, Figure 3 (c))
 
 Parity pins live in tests/test_oracle_pins.py; every function here has one.
@@ -25,6 +26,7 @@ _LIB_PATH = os.path.join(_HERE, "libmac_oracle.so")
 _lib = None
 
 F_DISABLE_REUSE = 1
+F_RING_BF16 = 2          # the ring keeps pre-RoPE queries rounded to bfloat16
 
 _dp = ctypes.POINTER(ctypes.c_double)
 _fp = ctypes.POINTER(ctypes.c_float)
@@ -51,6 +53,8 @@ def _load():
     lib.orc_nearest.argtypes = [_fp, _fp, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                                 _dp, _dp]
     lib.orc_nearest.restype = ctypes.c_int
+    lib.orc_round_bf16.argtypes = [ctypes.c_float]
+    lib.orc_round_bf16.restype = ctypes.c_float
     lib.orc_create.argtypes = [ctypes.c_int] * 6 + [ctypes.c_double] * 3 + [ctypes.c_int,
                                                                           ctypes.c_uint]
     lib.orc_create.restype = _vp
@@ -119,6 +123,13 @@ def remove(z, y):
     x = np.empty_like(z)
     _load().orc_remove(_ptr(z, _dp), _ptr(y, _dp), z.shape[0] - 2, _ptr(x, _dp))
     return x
+
+
+def round_bf16(x):
+    """x (float32 array) rounded to the nearest bfloat16, ties to even, as float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    f = _load().orc_round_bf16
+    return np.array([f(float(v)) for v in x.reshape(-1)], np.float32).reshape(x.shape)
 
 
 def nearest(qt, ring_q, ring_pos, m):

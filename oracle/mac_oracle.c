@@ -32,8 +32,28 @@
 #include <string.h>
 
 #define ORC_F_DISABLE_REUSE 1u
+#define ORC_F_RING_BF16 2u      /* ring keeps pre-RoPE queries rounded to bfloat16 */
 
 /* ---------------------------------------------------------------- values */
+
+/* x rounded to the nearest bfloat16 (ties to even), returned as a float:
+ * bfloat16 is the top 16 bits of an IEEE-754 single, so rounding adds half of
+ * the dropped 16-bit unit (less one when the kept part is even) and clears
+ * the low half.  NaN stays NaN; overflow rounds to infinity.  The ring keeps
+ * its queries in this form when ORC_F_RING_BF16 is set (the pages' Table 7
+ * puts the auxiliary memory at ~6x a token's KV per ring entry, which fits a
+ * 16-bit query plus an fp32 summary per head). */
+float orc_round_bf16(float x)
+{
+    if (isnan(x))
+        return x;
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+    float y;
+    memcpy(&y, &u, sizeof y);
+    return y;
+}
 
 /* bfloat16 bit pattern -> double; exact (bf16 is the top half of a float). */
 static double bf16_bits_to_double(uint16_t b)
@@ -408,7 +428,9 @@ int orc_step(orc_ctx *c, const void *const *k_grp, const void *const *v_grp,
         }
         if (reuse) {
             pos[slot_new] = (int32_t)m;
-            memcpy(rq + (size_t)slot_new * d, qt, (size_t)d * sizeof(float));
+            float *dst = rq + (size_t)slot_new * d;
+            for (int i = 0; i < d; i++)
+                dst[i] = (c->flags & ORC_F_RING_BF16) ? orc_round_bf16(qt[i]) : qt[i];
             memcpy(rs + (size_t)slot_new * (d + 2), Sm, (size_t)(d + 2) * sizeof(double));
         }
         free(q); free(O); free(tmp); free(Sm);

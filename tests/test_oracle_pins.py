@@ -249,3 +249,61 @@ def test_nearest_duplicate_prefers_newest():
     assert j == 1
     j, _, _ = oracle.nearest(np.zeros(d, np.float32), ring_q, ring_pos, 8)   # pos 9 > m
     assert j == 2
+
+
+# ------------------------------------------------------ bfloat16 ring queries
+
+def test_round_bf16_matches_torch_conversion():
+    """The oracle's bfloat16 rounding against torch's float32 -> bfloat16
+    conversion (round to nearest, ties to even), with planted exact ties."""
+    import torch
+    x = RNG.standard_normal(4000).astype(np.float32) * np.float32(3.0)
+    bits = x.view(np.uint32)
+    ties = (bits[:1000] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)    # exactly half an ulp
+    x[:1000] = ties.view(np.float32)
+    x[1000:1010] = [0.0, -0.0, 1.0, -1.0, 65504.0, 1e-38, -1e-38, 3.3895314e38, 1e30, 7.0]
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    got = oracle.round_bf16(x)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_ring_bf16_stores_rounded_queries_and_matches_on_them():
+    """With F_RING_BF16 the ring holds bfloat16-rounded pre-RoPE queries and
+    the decision is the brute-force nearest over those stored values."""
+    import torch
+    B, Hq, Hkv, d, W, r = 1, 2, 1, 128, 8, 4
+    n = 40
+    K, V = _rand_kv(n, d)
+    Kg, Vg = [K], [V]
+    orc = oracle.Oracle(B, Hq, Hkv, d, W, r, 0.3, 5e5, flags=oracle.F_RING_BF16)
+    plain = oracle.Oracle(B, Hq, Hkv, d, W, r, 0.3, 5e5)
+    q = RNG.standard_normal((Hq, d))
+    for t in range(20):
+        q = 0.97 * q + math.sqrt(1 - 0.97 ** 2) * RNG.standard_normal((Hq, d))
+        qf = q.astype(np.float32)[None]
+        m = 10 + t
+        # expected decisions from the stored entries, read before the step inserts
+        expect = []
+        for h in range(Hq):
+            entries = [orc.ring_entry(0, h, j) for j in range(W)]
+            ring_q = np.stack([e[1] for e in entries])
+            ring_pos = np.array([e[0] for e in entries], np.int32)
+            for e in entries:
+                if e[0] >= 0:
+                    assert np.array_equal(e[1], torch.from_numpy(e[1]).to(torch.bfloat16)
+                                          .to(torch.float32).numpy())
+            j = _brute_nearest(qf[0, h], ring_q, ring_pos, m)
+            qd = qf[0, h].astype(np.float64)
+            hit = j >= 0 and float(np.sum((qd - ring_q[j]) ** 2)) <= 0.09 * float(np.sum(qd * qd))
+            expect.append((hit, int(ring_pos[j]) if hit else -1))
+        res = orc.step(Kg, Vg, np.array([m + 1]), qf)
+        for h, (hit, p) in enumerate(expect):
+            assert bool(res["hit"][0, h]) == hit
+            if hit:
+                assert res["p"][0, h] == p
+        plain.step(Kg, Vg, np.array([m + 1]), qf)
+    # the plain oracle keeps the exact fp32 queries
+    pos, qp, _ = plain.ring_entry(0, 0, (20 - 1) % W)
+    pos_b, qb, _ = orc.ring_entry(0, 0, (20 - 1) % W)
+    assert pos == pos_b and not np.array_equal(qp, qb)
+    assert np.array_equal(qb, oracle.round_bf16(qp))
