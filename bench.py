@@ -71,6 +71,8 @@ def parse():
                     help="synthetic analogs of the pages' Figures 4, 5 and 8 (one JSON line)")
     ap.add_argument("--fused-amend", action="store_true",
                     help="MAC passes with MAC_F_FUSED_AMEND (the reduce updates the ring)")
+    ap.add_argument("--ring-bf16", action="store_true",
+                    help="MAC passes with MAC_F_RING_BF16 (ring queries kept as bfloat16)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 2 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -394,15 +396,16 @@ def figures(args):
         del K, V
         q8 = torch.as_tensor(queries(w8, steps=12), device="cuda")
         for W in (16, 32, 64, 256, 1024, 2048):
-            bn = Bench(scaled(w8, W=W), mac.MAC_F_TIMING, *c8)
-            us = []
-            for t in range(12):
-                st = bn.step(t, q8[t], kr[t], vr[t])
-                if t >= 4:
-                    us.append(st["last_us_match"])
-            bn.layer.close()
-            fig8.append({"G": G, "W": W, "match_us": float(np.mean(us)),
-                         "ring_bytes": B * Hq * W * w8.d * 4})
+            for ring, rflag, qbytes in (("fp32", 0, 4), ("bf16", mac.MAC_F_RING_BF16, 2)):
+                bn = Bench(scaled(w8, W=W), mac.MAC_F_TIMING | rflag, *c8)
+                us = []
+                for t in range(12):
+                    st = bn.step(t, q8[t], kr[t], vr[t])
+                    if t >= 4:
+                        us.append(st["last_us_match"])
+                bn.layer.close()
+                fig8.append({"G": G, "W": W, "ring": ring, "match_us": float(np.mean(us)),
+                             "ring_bytes": B * Hq * W * w8.d * qbytes})
         del c8, kr, vr
         torch.cuda.empty_cache()
 
@@ -490,7 +493,8 @@ def main():
 
     # pass 1 (the timed region): the attention phase between two stream events
     # per step, no events between the kernels
-    mac_flags = mac.MAC_F_FUSED_AMEND if args.fused_amend else 0
+    mac_flags = ((mac.MAC_F_FUSED_AMEND if args.fused_amend else 0) |
+                 (mac.MAC_F_RING_BF16 if args.ring_bf16 else 0))
     bench = Bench(w, mac_flags, kc, vc, paged, table)
     for t in range(args.warmup):
         bench.step(t, q_dev[t], k_rows[t], v_rows[t])
@@ -632,7 +636,8 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "context": w.C, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.d, "kv_layout": w.layout,
                    "ring": w.W, "band": w.r, "tau": w.tau, "rho": list(w.rho),
-                   "amend": "fused" if args.fused_amend else "async"},
+                   "amend": "fused" if args.fused_amend else "async",
+                   "ring_queries": "bf16" if args.ring_bf16 else "fp32"},
         "hbm_gbps": float(np.mean(kv_bytes)) / (att_us * 1e-6) / 1e9,
         "tokens_per_s": w.B / (att_us * 1e-6),
         "kv_bytes_per_step": float(np.mean(kv_bytes)),

@@ -65,7 +65,12 @@ enum {
      * prefix merged with the part before the band and writes the ring entry
      * itself: no band re-read, no log-domain removal, no amend stream work.
      * Same results up to rounding. */
-    MAC_F_FUSED_AMEND = 16u
+    MAC_F_FUSED_AMEND = 16u,
+    /* Keep the ring's pre-RoPE queries as bfloat16 (rounded to nearest, ties
+     * to even) and match against those: half the match traffic, ~6x a token's
+     * K/V bytes per ring entry as in the pages' Table 7.  Decisions can differ
+     * from the fp32 ring where the nearest entries are within rounding. */
+    MAC_F_RING_BF16 = 32u
 };
 
 /* Layer configuration (host struct).  head_dim must be 128; Hq % Hkv == 0;

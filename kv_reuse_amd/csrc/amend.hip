@@ -81,7 +81,12 @@ __global__ __launch_bounds__(64 * AMEND_WAVES) void amend_kernel(Shape s, State 
             dst[D + 1] = sL;
         }
         const float2 qv = *reinterpret_cast<const float2 *>(st.q_copy + idx * D + 2 * lane);
-        *reinterpret_cast<float2 *>(st.ring_q + (idx * s.W + slot_new) * D + 2 * lane) = qv;
+        const long row = (idx * s.W + slot_new) * D;
+        if (s.ring_bf16)
+            reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(st.ring_q) + row)[lane] =
+                bf16_rne_bits(qv.x) | bf16_rne_bits(qv.y) << 16;
+        else
+            reinterpret_cast<float2 *>(static_cast<float *>(st.ring_q) + row)[lane] = qv;
     }
     if (threadIdx.x == 0) {
         if (kvh == 0)

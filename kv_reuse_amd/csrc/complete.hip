@@ -307,12 +307,6 @@ __device__ __forceinline__ void store_msummary(MAcc<G> &st, float *dst)
     }
 }
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x)
-{
-    const uint32_t u = __float_as_uint(x);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // A operands of this lane (row l%16 -> head (l%16) % G, k-group l/16) for the
 // 4 k-steps, hi and lo parts interleaved: qa[2s] = hi, qa[2s+1] = lo.  hi
 // keeps the top 16 bits of the scaled fp32 query; lo = bf16(q - hi), where

@@ -119,6 +119,14 @@ __device__ __forceinline__ void to_f32(const uint4 &w, float (&f)[4])
     f[3] = __uint_as_float(w.w);
 }
 
+// bf16 bit pattern of x rounded to nearest, ties to even (finite inputs; an
+// overflow rounds to infinity).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 template <typename T>
 __device__ __forceinline__ float row_sum(float v)
 {

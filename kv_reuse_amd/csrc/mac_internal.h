@@ -3,7 +3,8 @@
 // complete.hip, reduce.hip, amend.hip).
 //
 // Device memory owned by a handle (fp32 unless noted):
-//   ring_q     [B][Hq][W][D]        pre-RoPE queries of recent steps
+//   ring_q     [B][Hq][W][D]        pre-RoPE queries of recent steps (fp32, or
+//                                   bf16 bit patterns with MAC_F_RING_BF16)
 //   ring_s     [B][Hq][W][SUMM]     summaries AS_{1:pos-r}: o[D], M, l, pad
 //   ring_pos   [B][W]  int32        position stored in each slot (-1 empty)
 //   q_copy     [B][Hq][D]           this step's pre-RoPE queries (for amend)
@@ -69,10 +70,12 @@ struct Shape {
     float tau, scale_log2;  // scale_log2 = sm_scale * log2(e)
     int32_t reuse;          // 0: every head misses
     int32_t nseg;           // work-list segments per group: 1, or 2 when amend is fused
+    int32_t ring_bf16;      // ring queries stored as bf16 (rounded to nearest, ties to even)
 };
 
 struct State {
-    float *ring_q, *ring_s, *q_copy, *q_rot, *partials, *as_full, *dec_rel;
+    void *ring_q;             // float, or uint16_t (bf16) when Shape::ring_bf16
+    float *ring_s, *q_copy, *q_rot, *partials, *as_full, *dec_rel;
     int32_t *ring_pos, *m_buf, *dec_slot, *dec_p, *dec_start;
     int32_t *grp_parts;       // [B*Hkv*nseg][2] worker range of each segment's partials (complete -> reduce)
     unsigned long long *stats;        // [MAC_NSTAT], then the two blocks below

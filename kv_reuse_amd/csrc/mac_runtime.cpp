@@ -87,7 +87,7 @@ Sizes sizes_for(const mac_config &c, int n_workers)
     const size_t B = c.batch, Hq = c.num_q_heads, Hkv = c.num_kv_heads, W = c.ring_size;
     const size_t G = Hq / Hkv, nseg = segments_per_group(c);
     Sizes s;
-    s.ring_q = round256(B * Hq * W * mac::D * sizeof(float));
+    s.ring_q = round256(B * Hq * W * mac::D * ((c.flags & MAC_F_RING_BF16) ? 2 : 4));
     s.ring_s = round256(B * Hq * W * mac::SUMM * sizeof(float));
     s.ring_pos = round256(B * W * sizeof(int32_t));
     s.qvec = round256(B * Hq * mac::D * sizeof(float));
@@ -168,7 +168,7 @@ mac_status validate(const mac_config *c, std::string &why)
         return MAC_EUNSUPPORTED;
     }
     const uint32_t known = MAC_F_DISABLE_REUSE | MAC_F_SYNC_AMEND | MAC_F_TIMING |
-                           MAC_F_RECORD_DEBUG | MAC_F_FUSED_AMEND;
+                           MAC_F_RECORD_DEBUG | MAC_F_FUSED_AMEND | MAC_F_RING_BF16;
     if (c->flags & ~known) {
         why = "unknown flag bits";
         return MAC_EINVAL;
@@ -319,7 +319,7 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
         p += bytes;
         return r;
     };
-    h->st.ring_q = (float *)take(sz.ring_q);
+    h->st.ring_q = take(sz.ring_q);
     h->st.ring_s = (float *)take(sz.ring_s);
     h->st.ring_pos = (int32_t *)take(sz.ring_pos);
     h->st.q_copy = (float *)take(sz.qvec);
@@ -359,6 +359,7 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     h->shape.scale_log2 = (float)(scale * 1.4426950408889634);
     h->shape.reuse = !(cfg->flags & MAC_F_DISABLE_REUSE) && cfg->tau >= 0.f;
     h->shape.nseg = segments_per_group(*cfg);
+    h->shape.ring_bf16 = (cfg->flags & MAC_F_RING_BF16) ? 1 : 0;
 
     if (amend_stream) {
         h->amend_stream = (hipStream_t)amend_stream;

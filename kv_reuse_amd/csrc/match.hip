@@ -82,6 +82,82 @@ __device__ __forceinline__ void scan_tile(const float4 *rq, int base, int nslot,
     }
 }
 
+// The same scan over a ring of bf16 queries: a slot is 256 bytes, so one
+// 1 KB wave load covers four slots (lanes 16j .. 16j+15 hold slot 4u + j,
+// eight columns each) and the squared differences are summed over each
+// 16-lane row with DPP.  q8 holds columns 8c .. 8c+7 of the query
+// (c = lane % 16).
+__device__ __forceinline__ void scan_tile_bf16(const uint4 *rq, int base, int nslot,
+                                               const float (&q8)[8], int pos_l, int m, float &kd,
+                                               int &kp, int &kj)
+{
+    const int lane = lane_id(), sub = lane >> 4, c = lane & 15;
+    kd = INFINITY;
+    kp = INT_MIN;
+    kj = -1;
+    for (int i = 0; i < nslot; i += 32) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int sl = min(i + 4 * u + sub, nslot - 1);
+            v[u] = rq[(long)sl * (D / 8) + c];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int sl = i + 4 * u + sub;
+            float f[8];
+            to_f32(v[u], f);
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float t = q8[e] - f[e];
+                d = fmaf(t, t, d);
+            }
+            d = row16_sum(d);
+            const int pos = __shfl(pos_l, sl & 63, 64);
+            const bool valid = sl < nslot && pos >= 0 && pos <= m;
+            if (valid && nearer(d, pos, base + sl, kd, kp, kj)) {
+                kd = d;
+                kp = pos;
+                kj = base + sl;
+            }
+        }
+    }
+    // the four rows saw different slots
+#pragma unroll
+    for (int off = 16; off <= 32; off *= 2) {
+        const float d2 = off == 16 ? xor_lanes<16>(kd) : xor_lanes<32>(kd);
+        const int p2 = off == 16 ? xor_lanes_i<16>(kp) : xor_lanes_i<32>(kp);
+        const int j2 = off == 16 ? xor_lanes_i<16>(kj) : xor_lanes_i<32>(kj);
+        if (nearer(d2, p2, j2, kd, kp, kj)) {
+            kd = d2;
+            kp = p2;
+            kj = j2;
+        }
+    }
+}
+
+// Nearest valid entry among ring slots [base, base + nslot) of head idx, in
+// whichever form the ring stores its queries.  qsrc: the head's pre-RoPE query.
+__device__ __forceinline__ void scan_ring_tile(const Shape &s, const State &st, long idx, int base,
+                                               int nslot, const float *qsrc, int pos_l, int m,
+                                               float &kd, int &kp, int &kj)
+{
+    const int lane = lane_id();
+    const long row = (idx * s.W + base) * D;
+    if (s.ring_bf16) {
+        const float4 a = reinterpret_cast<const float4 *>(qsrc)[2 * (lane & 15)];
+        const float4 b = reinterpret_cast<const float4 *>(qsrc)[2 * (lane & 15) + 1];
+        const float q8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        scan_tile_bf16(reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(st.ring_q) + row),
+                       base, nslot, q8, pos_l, m, kd, kp, kj);
+    } else {
+        const float4 qv = reinterpret_cast<const float4 *>(qsrc)[lane & 31];
+        scan_tile(reinterpret_cast<const float4 *>(static_cast<const float *>(st.ring_q) + row),
+                  base, nslot, qv, pos_l, m, kd, kp, kj);
+    }
+}
+
 // =========================================================== match tiles
 // Rings longer than one 64-slot tile (the pages' windows of 512-2048 entries,
 // Figure 6, Tables 5 and 7).  Grid (tiles, Hq, B), one wave per tile: the
@@ -100,11 +176,9 @@ __global__ __launch_bounds__(64) void match_tiles_kernel(Shape s, State st, KvVi
     bool bad;
     const int m = query_position(kv, seq_lens[b], bad);
     const int pos_l = lane < nslot ? st.ring_pos[(long)b * s.W + base + lane] : -1;
-    const float4 qv = reinterpret_cast<const float4 *>(q_pre + idx * D)[lane & 31];
     float kd;
     int kp, kj;
-    scan_tile(reinterpret_cast<const float4 *>(st.ring_q + (idx * s.W + base) * D), base, nslot,
-              qv, pos_l, m, kd, kp, kj);
+    scan_ring_tile(s, st, idx, base, nslot, q_pre + idx * D, pos_l, m, kd, kp, kj);
     if (lane == 0) {
         float *o = st.tile_best + (idx * ntiles + tile) * 3;
         o[0] = kd;
@@ -140,7 +214,6 @@ __global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
     // ---- loads independent of the position
     const int seq = seq_lens[b];
     const float qa = q_pre[idx * D + lane], qb = q_pre[idx * D + lane + 64];
-    const float4 qv = reinterpret_cast<const float4 *>(q_pre + idx * D)[lane & 31];
     const double inv = st.inv_freq[lane];
     const int ov = ovr ? ovr[idx] : -2;
     const int pos_l = (s.reuse && lane < s.W) ? st.ring_pos[(long)b * s.W + lane] : -1;
@@ -188,8 +261,7 @@ __global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
         float kd;
         int kp, kj;
         if (!tiled) {
-            scan_tile(reinterpret_cast<const float4 *>(st.ring_q + idx * s.W * D), 0, s.W, qv,
-                      pos_l, m, kd, kp, kj);
+            scan_ring_tile(s, st, idx, 0, s.W, q_pre + idx * D, pos_l, m, kd, kp, kj);
         } else {
             // nearest entry over the head's tiles
             kd = td;

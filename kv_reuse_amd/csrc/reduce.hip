@@ -209,8 +209,14 @@ __global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(Shape s, State s
         O = merge(X, part1);
         float *dst = st.ring_s + (idx * s.W + slot_new) * SUMM;
         *reinterpret_cast<float4 *>(dst + 4 * c) = X.o;
-        *reinterpret_cast<float4 *>(st.ring_q + (idx * s.W + slot_new) * D + 4 * c) =
-            *reinterpret_cast<const float4 *>(st.q_copy + idx * D + 4 * c);
+        const float4 qv = *reinterpret_cast<const float4 *>(st.q_copy + idx * D + 4 * c);
+        const long row = (idx * s.W + slot_new) * D;
+        if (s.ring_bf16)
+            reinterpret_cast<uint2 *>(static_cast<uint16_t *>(st.ring_q) + row)[c] =
+                make_uint2(bf16_rne_bits(qv.x) | bf16_rne_bits(qv.y) << 16,
+                           bf16_rne_bits(qv.z) | bf16_rne_bits(qv.w) << 16);
+        else
+            reinterpret_cast<float4 *>(static_cast<float *>(st.ring_q) + row)[c] = qv;
         if (t == 0) {
             dst[D] = X.M;
             dst[D + 1] = X.L;

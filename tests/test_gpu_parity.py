@@ -139,6 +139,29 @@ def test_fused_amend_matches_oracle(gpu_lib, case):
     _run(w, w.steps, flags=mac.MAC_F_FUSED_AMEND, **kw)
 
 
+_RING_BF16_CASES = {
+    "paged_mixed_w32": (lambda: scaled(get_config("b16_128k"), B=4, C=3000, steps=48), {}),
+    "window_100": (lambda: scaled(get_config("b16_128k"), B=2, C=600, steps=150, W=100,
+                                  rho=("const", 0.96)), {}),
+    "window_2048": (lambda: scaled(get_config("b16_128k"), B=2, C=600, steps=140, W=2048,
+                                   rho=("const", 0.96)), {}),
+    "window_24_g8": (lambda: scaled(get_config("moe_122k"), B=2, C=2500, steps=40, W=24), {}),
+    "cpu4k_fp32_fused": (lambda: scaled(get_config("cpu4k"), steps=120), {"fused": True}),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_RING_BF16_CASES))
+def test_ring_bf16_matches_oracle(gpu_lib, case):
+    """MAC_F_RING_BF16: ring queries stored as bfloat16, against the oracle
+    with the same rounding (F_RING_BF16); decisions bit-exact."""
+    import kv_reuse_amd as mac
+    import oracle
+    make, kw = _RING_BF16_CASES[case]
+    w = make()
+    flags = mac.MAC_F_RING_BF16 | (mac.MAC_F_FUSED_AMEND if kw.get("fused") else 0)
+    _run(w, w.steps, flags=flags, oracle_flags=oracle.F_RING_BF16)
+
+
 def test_disable_reuse_is_full_attention(gpu_lib):
     import kv_reuse_amd as mac
     import oracle
