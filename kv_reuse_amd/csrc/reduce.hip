@@ -91,24 +91,31 @@ struct ReduceLds {
     float l[RLANES], m[RLANES];
 };
 
-// Combine the n partials at part, part + pstride, ... (this head's rows) into
-// a normalised summary, valid in threads 0..RCH-1; EMPTY when n = 0.  Every
-// thread of the block calls it; reuse: another call follows, so the LDS is
-// released by a second barrier.
-__device__ __forceinline__ Sum4 combine_partials(const float *part, int n, long pstride, ReduceLds &lds,
-                                 bool reuse)
+// Combine NSETS (1 or 2) sets of partials -- set j: n_j rows at part_j,
+// part_j + pstride, ... (this head's rows) -- into normalised summaries r0,
+// r1, valid in threads 0..RCH-1 (EMPTY for a set with no rows).  The block's
+// RLANES partial lanes are split evenly between the sets, so both are read in
+// the same rounds.  Every thread of the block calls it (one barrier).
+template <int NSETS>
+__device__ __forceinline__ void combine_partials(const float *part0, int n0, const float *part1,
+                                                 int n1, long pstride, ReduceLds &lds, Sum4 &r0,
+                                                 Sum4 &r1)
 {
+    constexpr int PER = RLANES / NSETS;   // partial lanes per set
     const int t = threadIdx.x, c = t % RCH, k = t / RCH;
+    const int set = k / PER, kk = k % PER;
+    const float *part = set == 0 ? part0 : part1;
+    const int n = set == 0 ? n0 : n1;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     float L = 0.f, M = NEG_INF;
-    for (int i = k; i < n; i += RUNROLL * RLANES) {
+    for (int i = kk; i < n; i += RUNROLL * PER) {
         float4 ov[RUNROLL];
         float mv[RUNROLL], lv[RUNROLL];
-        const int cnt = min(RUNROLL, (n - i + RLANES - 1) / RLANES);
+        const int cnt = min(RUNROLL, (n - i + PER - 1) / PER);
 #pragma unroll
         for (int u = 0; u < RUNROLL; ++u) {
             if (u < cnt) {
-                const float *pi = part + (long)(i + u * RLANES) * pstride;
+                const float *pi = part + (long)(i + u * PER) * pstride;
                 ov[u] = *reinterpret_cast<const float4 *>(pi + 4 * c);
                 mv[u] = pi[D];
                 lv[u] = pi[D + 1];
@@ -122,27 +129,32 @@ __device__ __forceinline__ Sum4 combine_partials(const float *part, int n, long 
         lds.m[k] = M;
     }
     __syncthreads();
+    if (t >= 64)
+        return;
+    // wave 0: lanes 32j .. 32j+31 finish set j (set 0 only when NSETS == 1)
     Sum4 r;
     r.o = make_float4(0.f, 0.f, 0.f, 0.f);
     r.M = NEG_INF;
     r.L = 0.f;
-    if (t < RCH) {
-        float Mx = lds.m[0];
+    const int mine = t / RCH;
+    if (mine < NSETS) {
+        const int q0 = mine * PER;
+        float Mx = lds.m[q0];
 #pragma unroll
-        for (int q = 1; q < RLANES; ++q)
-            Mx = fmaxf(Mx, lds.m[q]);
+        for (int q = 1; q < PER; ++q)
+            Mx = fmaxf(Mx, lds.m[q0 + q]);
         const float base = Mx == NEG_INF ? 0.f : Mx;
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
         float Lt = 0.f;
 #pragma unroll
-        for (int q = 0; q < RLANES; ++q) {
-            const float sc = exp2f(lds.m[q] - base);   // 0 for a lane that saw no partial
-            const float4 x = lds.o[q][c];
+        for (int q = 0; q < PER; ++q) {
+            const float sc = exp2f(lds.m[q0 + q] - base);   // 0 for a lane that saw no partial
+            const float4 x = lds.o[q0 + q][c];
             o.x = fmaf(x.x, sc, o.x);
             o.y = fmaf(x.y, sc, o.y);
             o.z = fmaf(x.z, sc, o.z);
             o.w = fmaf(x.w, sc, o.w);
-            Lt = fmaf(lds.l[q], sc, Lt);
+            Lt = fmaf(lds.l[q0 + q], sc, Lt);
         }
         if (Lt > 0.f) {
             r.o = make_float4(o.x / Lt, o.y / Lt, o.z / Lt, o.w / Lt);
@@ -150,9 +162,17 @@ __device__ __forceinline__ Sum4 combine_partials(const float *part, int n, long 
             r.L = Lt;
         }
     }
-    if (reuse)
-        __syncthreads();
-    return r;
+    r0 = r;
+    if constexpr (NSETS == 2) {
+        r1.o.x = __shfl(r.o.x, t + 32, 64);
+        r1.o.y = __shfl(r.o.y, t + 32, 64);
+        r1.o.z = __shfl(r.o.z, t + 32, 64);
+        r1.o.w = __shfl(r.o.w, t + 32, 64);
+        r1.M = __shfl(r.M, t + 32, 64);
+        r1.L = __shfl(r.L, t + 32, 64);
+    } else {
+        r1 = r;
+    }
 }
 
 __global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(Shape s, State st,
@@ -187,12 +207,14 @@ __global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(Shape s, State s
     if (m < 0)
         return;   // idle request: match wrote its zero output, nothing is stored
     const long pstride = (long)s.G * SUMM;   // one slot
-    const Sum4 part0 = combine_partials(st.partials + ((long)rg0.x + seg0) * pstride + hh * SUMM,
-                                        rg0.y - rg0.x + 1, pstride, lds, s.nseg == 2);
-    Sum4 part1 = part0;
+    const float *p0 = st.partials + ((long)rg0.x + seg0) * pstride + hh * SUMM;
+    Sum4 part0, part1;
     if (s.nseg == 2)
-        part1 = combine_partials(st.partials + ((long)rg1.x + seg0 + 1) * pstride + hh * SUMM,
-                                 rg1.y - rg1.x + 1, pstride, lds, false);
+        combine_partials<2>(p0, rg0.y - rg0.x + 1,
+                            st.partials + ((long)rg1.x + seg0 + 1) * pstride + hh * SUMM,
+                            rg1.y - rg1.x + 1, pstride, lds, part0, part1);
+    else
+        combine_partials<1>(p0, rg0.y - rg0.x + 1, nullptr, 0, pstride, lds, part0, part1);
     if (t >= RCH)
         return;
     Sum4 O;
