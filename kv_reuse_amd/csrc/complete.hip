@@ -333,6 +333,47 @@ __device__ __forceinline__ void build_qa(const Shape &s, const State &st, int b,
     }
 }
 
+// Element offsets of the (page, KV head) blocks a wave walks in one segment.
+// Paged caches: the page ids are fetched 64 at a time, one per lane, and each
+// page reads its id from that lane, so a page's K/V loads wait on no table
+// lookup of their own.  An id outside the pool is replaced by page 0
+// and counted (once per wave and page).
+struct PageWalker {
+    const int32_t *row;   // paged: the request's page-table row
+    long base;            // contiguous: offset of (request, KV head)
+    int kvh, Hkv, num_pages, chunk0, pid_l, last;
+    bool paged;
+
+    __device__ __forceinline__ PageWalker(const KvView &kv, int b, int kvh_, int Hkv_, int first,
+                                          int last_)
+        : kvh(kvh_), Hkv(Hkv_), num_pages(kv.num_pages), chunk0(first - 64), pid_l(0),
+          last(last_), paged(kv.paged != 0)
+    {
+        row = kv.page_table + (long)b * kv.max_pages;
+        base = ((long)b * Hkv + kvh) * (long)kv.max_seq_len * D;
+    }
+
+    __device__ __forceinline__ long offset(int page, unsigned long long *bad)
+    {
+        if (!paged)
+            return base + (long)page * (PAGE * D);
+        if (page >= chunk0 + 64) {
+            chunk0 = page;
+            const int tp = page + lane_id();
+            pid_l = tp <= last ? row[tp] : 0;
+        }
+        // the lane index is wave-uniform: v_readlane into a scalar register,
+        // no LDS round trip (a ds_bpermute would queue behind the page's LDS work)
+        int pid = __builtin_amdgcn_readlane(pid_l, page - chunk0);
+        if ((unsigned)pid >= (unsigned)num_pages) {
+            if (lane_id() == 0)
+                atomicAdd(bad, 1ULL);
+            pid = 0;
+        }
+        return ((long)pid * Hkv + kvh) * (PAGE * D);
+    }
+};
+
 template <int G>
 __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Shape s, State st,
                                                                      KvView kv)
@@ -407,16 +448,20 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
         int page = first_page + (int)(x - s_off[sg]);
         const int last = first_page + (int)(send - s_off[sg]) - 1;
         if constexpr (G > 4) {
+            PageWalker pw(kv, b, kvh, s.Hkv, page, last);
             // two waves per SIMD (G = 8 needs ~220 VGPRs): the next page's
             // loads are issued before the current page is computed
             MPage cur, nxt;
-            load_mpage(cur, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad),
-                       kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page, bad));
+            {
+                const long off = pw.offset(page, bad);
+                load_mpage(cur, kb + off, vb + off);
+            }
             kstore_page(cur, klds[wv]);
             while (true) {
-                if (page + 1 <= last)
-                    load_mpage(nxt, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page + 1, bad),
-                               kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page + 1, bad));
+                if (page + 1 <= last) {
+                    const long off = pw.offset(page + 1, bad);
+                    load_mpage(nxt, kb + off, vb + off);
+                }
                 const int tok0 = page * PAGE;
                 compute_mpage<G>(klds[wv], cur.v, &qlds[wv][0][0], plds[wv], tok0, hi, hsl,
                                  tok0 < hmax || tok0 + PAGE - 1 > hi, half_mask, acc);
@@ -432,6 +477,8 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
             // one page in flight per wave: at <= 168 VGPRs three waves share
             // each SIMD, which hides the load latency better than double
             // buffering (which needs more registers than that) does (measured)
+            // (the page id comes from a wave-uniform scalar load here: with one
+            // page in flight the lane-fetched ids of PageWalker measured slower)
             MPage cur;
             while (true) {
                 load_mpage(cur, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad),
