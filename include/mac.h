@@ -26,10 +26,12 @@
  *    mac_last_error() gives the handle's last message.  Shape and pointer
  *    errors are caught on the host before any launch.  Device faults surface
  *    as MAC_EHIP at the next synchronising call.  Data values are not
- *    validated (NaN propagates); indices read from device memory (sequence
- *    lengths, page ids, positions) are bounds-checked on the device, and an
- *    out-of-range entry idles that request or row and is counted in
- *    mac_stats_t.bad_input instead of being dereferenced.
+ *    validated (NaN propagates); indices read from device memory are
+ *    bounds-checked on the device and never dereferenced out of range: a
+ *    sequence length past the cache idles its request, an append position
+ *    past it skips its row, and a page id outside the pool is read as page 0
+ *    (that request's output is then meaningless).  Each is counted in
+ *    mac_stats_t.bad_input.
  */
 #ifndef MAC_H
 #define MAC_H

@@ -8,15 +8,19 @@ namespace mac {
 namespace {
 
 // ================================================================== amend
-// Grid (Hkv, B), 8 waves: the waves share the band [m-r+1, m] page by page
-// (two or three pages each at r = 256), combine in LDS, then per head
-// AS_{1:m-r} = AS_{1:m} (-) band and the ring slot receives (q~_m, AS_{1:m-r}, m).
-constexpr int AMEND_WAVES = 8;
+// Grid (Hkv, B), 8 waves (4 for 8 query heads per KV head, whose VALU worker
+// needs more than the 256 VGPRs two waves per SIMD allow): the waves share the
+// band [m-r+1, m] page by page (two to five pages each at r = 256), combine in
+// LDS, then per head AS_{1:m-r} = AS_{1:m} (-) band and the ring slot receives
+// (q~_m, AS_{1:m-r}, m).
+template <int G>
+constexpr int amend_waves() { return G > 4 ? 4 : 8; }
 
 template <typename T, int G>
-__global__ __launch_bounds__(64 * AMEND_WAVES) void amend_kernel(Shape s, State st, KvView kv,
-                                                                 int slot_new)
+__global__ __launch_bounds__(64 * amend_waves<G>()) void amend_kernel(Shape s, State st, KvView kv,
+                                                                      int slot_new)
 {
+    constexpr int AMEND_WAVES = amend_waves<G>();
     __shared__ float red[AMEND_WAVES][G][SUMM];
     using K = Kv<T>;
     const int b = blockIdx.y, kvh = blockIdx.x;
@@ -157,8 +161,8 @@ hipError_t launch_amend_t(const Shape &s, const State &st, const KvView &kv, int
     switch (s.G) {
 #define MAC_CASE(GG)                                                                          \
     case GG:                                                                                  \
-        hipLaunchKernelGGL((amend_kernel<T, GG>), grid, dim3(64 * AMEND_WAVES), 0, stream, s,  \
-                           st, kv, slot_new);                                                 \
+        hipLaunchKernelGGL((amend_kernel<T, GG>), grid, dim3(64 * amend_waves<GG>()), 0, stream, \
+                           s, st, kv, slot_new);                                              \
         break;
         MAC_CASE(1)
         MAC_CASE(2)

@@ -147,7 +147,8 @@ __device__ __forceinline__ const T *kv_page(const KvView &kv, const void *base, 
     if (kv.paged) {
         int pid = kv.page_table[(long)b * kv.max_pages + page];
         if ((unsigned)pid >= (unsigned)kv.num_pages) {
-            atomicAdd(bad, 1ULL);
+            if (lane_id() == 0)
+                atomicAdd(bad, 1ULL);   // once per wave and page
             pid = 0;
         }
         off = ((long)pid * Hkv + kvh) * (PAGE * D);
