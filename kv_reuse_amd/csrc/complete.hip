@@ -307,22 +307,37 @@ __device__ __forceinline__ void store_msummary(MAcc<G> &st, float *dst)
     }
 }
 
-// A operands of this lane (row l%16 -> head (l%16) % G, k-group l/16) for the
-// 4 k-steps, hi and lo parts interleaved: qa[2s] = hi, qa[2s+1] = lo.  hi
-// keeps the top 16 bits of the scaled fp32 query; lo = bf16(q - hi), where
-// q - hi is exact in fp32.
+// This lane's query values for the MFMA A operand (row l%16 -> head
+// (l%16) % G, k-group l/16): columns 32k + 8(l/16) .. +7 for the 4 k-steps,
+// two float4 each.  Loaded on their own so they can be in flight while the
+// segment's bounds are read.
 template <int G>
-__device__ __forceinline__ void build_qa(const Shape &s, const State &st, int b, int kvh,
-                                         uint4 *qa)
+__device__ __forceinline__ void load_qa_rows(const Shape &s, const State &st, int b, int kvh,
+                                             float4 (&qf)[8])
 {
     const int lane = lane_id(), row = lane & 15, q = lane >> 4;
-    const float *src = st.q_rot + ((long)b * s.Hq + kvh * G + row % G) * D;
+    const float4 *src = reinterpret_cast<const float4 *>(
+        st.q_rot + ((long)b * s.Hq + kvh * G + row % G) * D);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
+        qf[2 * k] = src[(32 * k + 8 * q) / 4];
+        qf[2 * k + 1] = src[(32 * k + 8 * q) / 4 + 1];
+    }
+}
+
+// The A operands for the 4 k-steps, hi and lo parts interleaved: qa[2s] = hi,
+// qa[2s+1] = lo.  hi keeps the top 16 bits of the scaled fp32 query; lo =
+// bf16(q - hi), where q - hi is exact in fp32.
+__device__ __forceinline__ void build_qa(const float4 (&qf)[8], float scale, uint4 *qa)
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float v[8] = {qf[2 * k].x, qf[2 * k].y, qf[2 * k].z, qf[2 * k].w,
+                            qf[2 * k + 1].x, qf[2 * k + 1].y, qf[2 * k + 1].z, qf[2 * k + 1].w};
         uint32_t hi[8], lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float x = src[32 * k + 8 * q + e] * s.scale_log2;
+            const float x = v[e] * scale;
             hi[e] = __float_as_uint(x) >> 16;
             lo[e] = bf16_rne_bits(x - __uint_as_float(hi[e] << 16));
         }
@@ -404,6 +419,8 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
         while (s_off[sg + 1] <= x)
             ++sg;
         const long send = min((long)s_off[sg + 1], x1);
+        float4 qf[8];   // issued before the segment's bounds are read
+        load_qa_rows<G>(s, st, (sg / s.nseg) / s.Hkv, (sg / s.nseg) % s.Hkv, qf);
         const Seg sd = segment(s, st, sg);
         const int b = sd.b, kvh = sd.kvh, hi = sd.hi;
         constexpr int HPL = MAcc<G>::HPL;
@@ -427,7 +444,7 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
         }
         {
             uint4 qa[8];
-            build_qa<G>(s, st, b, kvh, qa);
+            build_qa(qf, s.scale_log2, qa);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 qlds[wv][i][lane] = qa[i];

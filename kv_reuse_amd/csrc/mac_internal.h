@@ -39,7 +39,7 @@ constexpr int WAVES = BLOCK / 64;
 constexpr int MAX_W = 2048;     // ring slots per (request, head)
 constexpr int TILE_W = 64;      // ring slots a wave scans at once (LDS tile or one tile wave)
 constexpr int MAX_GROUPS = 4096;  // B * Hkv
-constexpr int MIN_PAGES_PER_WORKER = 2;
+constexpr int MIN_PAGES_PER_WORKER = 1;
 
 // Counters, one uint64 block: MAC_NSTAT device-wide ones (only ST_BAD_INPUT,
 // by atomics on error paths), then HEAD_NSTAT per (request, query head),
