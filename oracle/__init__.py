@@ -12,6 +12,8 @@ What each function follows (MAC-Attention, arXiv 2604.00235, paper card):
   remove ...... log-domain removal (-) (Figure 2 (c))
   nearest ..... pre-RoPE L2 nearest neighbour over the ring (Figure 2 (a))
   round_bf16 .. ring queries kept in bfloat16 (F_RING_BF16; Table 7's memory)
+  F_STALE_RING  asynchronous cache update read as one call of staleness
+                (Figure 2 (c)): call t matches entries of calls <= t-2
   Oracle.step . match -> complete -> amend, one decode call (Figure 2, Figure 3 (c))
 
 Parity pins live in tests/test_oracle_pins.py; every function here has one.
@@ -27,6 +29,7 @@ _lib = None
 
 F_DISABLE_REUSE = 1
 F_RING_BF16 = 2          # the ring keeps pre-RoPE queries rounded to bfloat16
+F_STALE_RING = 4         # call t matches only entries inserted up to call t-2
 
 _dp = ctypes.POINTER(ctypes.c_double)
 _fp = ctypes.POINTER(ctypes.c_float)

@@ -33,6 +33,11 @@
 
 #define ORC_F_DISABLE_REUSE 1u
 #define ORC_F_RING_BF16 2u      /* ring keeps pre-RoPE queries rounded to bfloat16 */
+/* Stale-by-one ring: the match of call t sees only entries inserted by calls
+ * up to t-2.  The pages update the cache asynchronously (Figure 2 (c)); with
+ * this reading the amend of call t-1 may still be writing its slot while call
+ * t matches, so that slot takes no part in call t's match or override. */
+#define ORC_F_STALE_RING 4u
 
 /* ---------------------------------------------------------------- values */
 
@@ -357,11 +362,16 @@ int orc_step(orc_ctx *c, const void *const *k_grp, const void *const *v_grp,
         if (m < 0)
             continue;
 
-        /* Figure 2 (a): match on the pre-RoPE query. */
+        /* Figure 2 (a): match on the pre-RoPE query, over the entries this
+         * call may see. */
+        int32_t *vis = (int32_t *)malloc((size_t)W * sizeof(int32_t));
+        memcpy(vis, pos, (size_t)W * sizeof(int32_t));
+        if ((c->flags & ORC_F_STALE_RING) && c->calls > 0)
+            vis[(c->calls - 1) % W] = -1;
         int slot = -1;
         if (reuse) {
             double d1, d2;
-            int j = orc_nearest(qt, rq, pos, W, d, m, &d1, &d2);
+            int j = orc_nearest(qt, rq, vis, W, d, m, &d1, &d2);
             if (j >= 0) {
                 double qn2 = 0.0;
                 for (int e = 0; e < d; e++)
@@ -378,13 +388,14 @@ int orc_step(orc_ctx *c, const void *const *k_grp, const void *const *v_grp,
                 slot = -1;
                 if (override[bh] >= 0) {
                     for (int e = 0; e < W; e++)
-                        if (pos[e] == override[bh] && pos[e] <= m)
+                        if (vis[e] >= 0 && vis[e] == override[bh] && vis[e] <= m)
                             slot = e;
                     if (slot < 0)
                         invalid_total += 1;
                 }
             }
         }
+        free(vis);
         int32_t p = slot >= 0 ? pos[slot] : -1;
         int64_t st = slot >= 0 ? (int64_t)p - r + 1 : 0;
         if (st < 0)

@@ -43,6 +43,12 @@ class SegmentModel:
         self.ring = [[[None] * W for _ in range(Hq)] for _ in range(B)]
         self.calls = 0
 
+    def _visible(self, e):
+        """An entry inserted by call c takes part in call t's match when
+        c <= t - 1, or c <= t - 2 for the stale-by-one ring."""
+        lag = 2 if self.flags & oracle.F_STALE_RING else 1
+        return e["call"] <= self.calls - lag
+
     def _value(self, segs, Kf, Vf):
         logits, rows = [], []
         for q, a, b in segs:
@@ -71,7 +77,7 @@ class SegmentModel:
                     key = None
                     for j in range(W):
                         e = ring[j]
-                        if e is None or e["pos"] > m:
+                        if e is None or e["pos"] > m or not self._visible(e):
                             continue
                         D = float(np.sum((qt.astype(np.float64) - e["qt"].astype(np.float64)) ** 2))
                         kj = (D, -e["pos"], -j)
@@ -85,7 +91,7 @@ class SegmentModel:
                         slot = -1
                         for j in range(W):
                             if ring[j] is not None and ring[j]["pos"] == override[b, h] \
-                                    and ring[j]["pos"] <= m:
+                                    and ring[j]["pos"] <= m and self._visible(ring[j]):
                                 slot = j
                 q = _rope_complex(qt, m, self.theta)
                 Kf, Vf = Kg[b * self.Hkv + h // G], Vg[b * self.Hkv + h // G]
@@ -106,7 +112,7 @@ class SegmentModel:
                     if start <= m - r:
                         kept.append((q, start, m - r))
                 if reuse:
-                    ring[slot_new] = {"pos": m, "qt": qt.copy(), "segs": kept}
+                    ring[slot_new] = {"pos": m, "qt": qt.copy(), "segs": kept, "call": self.calls}
         self.calls += 1
         return out, hit, p_out
 
@@ -121,14 +127,21 @@ def _setup(kv="fp32", B=2, Hq=4, Hkv=2, d=8, C=12, steps=40, W=4, r=3, rho=0.9, 
     return w, Kg, Vg, queries(w)
 
 
-@pytest.mark.parametrize("kv,tau,W,r", [("fp32", 0.5, 4, 3), ("bf16", 0.45, 4, 5),
-                                        ("fp32", 1e9, 3, 2), ("bf16", 0.0, 2, 4),
-                                        ("fp32", 0.6, 1, 3)])
-def test_policy_matches_segment_model(kv, tau, W, r):
+_STALE = oracle.F_STALE_RING
+
+
+@pytest.mark.parametrize("kv,tau,W,r,flags", [("fp32", 0.5, 4, 3, 0), ("bf16", 0.45, 4, 5, 0),
+                                              ("fp32", 1e9, 3, 2, 0), ("bf16", 0.0, 2, 4, 0),
+                                              ("fp32", 0.6, 1, 3, 0),
+                                              ("fp32", 0.5, 4, 3, _STALE),
+                                              ("bf16", 1e9, 3, 2, _STALE),
+                                              ("fp32", 1e9, 1, 3, _STALE)])
+def test_policy_matches_segment_model(kv, tau, W, r, flags):
     w, Kg, Vg, qs = _setup(kv=kv, W=W, r=r)
     theta = 10000.0
-    orc = oracle.Oracle(w.B, w.Hq, w.Hkv, w.d, W, r, tau, theta, kv_fp32=(kv == "fp32"))
-    mod = SegmentModel(w.B, w.Hq, w.Hkv, w.d, W, r, tau, theta)
+    orc = oracle.Oracle(w.B, w.Hq, w.Hkv, w.d, W, r, tau, theta, kv_fp32=(kv == "fp32"),
+                        flags=flags)
+    mod = SegmentModel(w.B, w.Hq, w.Hkv, w.d, W, r, tau, theta, flags=flags)
     KgF = [_kvf(a) for a in Kg]
     VgF = [_kvf(a) for a in Vg]
     nhit = 0
@@ -141,7 +154,11 @@ def test_policy_matches_segment_model(kv, tau, W, r):
         np.testing.assert_allclose(res["out"], out, rtol=1e-10, atol=1e-12)
         nhit += int(hit.sum())
     if tau >= 1e9:
-        assert nhit == (w.steps - 1) * w.B * w.Hq
+        # every call hits the newest visible entry; the stale ring sees none
+        # in its first two calls, and none at all with a single slot
+        first = 2 if flags & _STALE else 1
+        want = 0 if (flags & _STALE and W == 1) else (w.steps - first) * w.B * w.Hq
+        assert nhit == want
     elif tau > 0:
         assert 0 < nhit < w.steps * w.B * w.Hq      # the case mixes hits and misses
 
@@ -280,3 +297,31 @@ def test_reset_empties_rings():
     orc.reset()
     res = orc.step(Kg, Vg, np.full(w.B, w.C + 4, np.int32), qs[3])
     assert not res["hit"].any()
+
+
+def test_stale_ring_hides_only_the_previous_call():
+    """Stale-by-one ring: call t's match and override skip the entry of call
+    t-1 and see every older one still stored.  The query repeats, so every
+    stored entry is at distance 0 and the tie rule picks the newest visible
+    one, call t-2's.  After a reset the first two calls miss."""
+    w, Kg, Vg, qs = _setup(kv="fp32", W=4, r=3)
+    orc = oracle.Oracle(w.B, w.Hq, w.Hkv, w.d, 4, 3, 1e9, 1e4, kv_fp32=True,
+                        flags=oracle.F_STALE_RING)
+    for rnd in range(2):
+        for t in range(6):
+            m = w.C + t
+            res = orc.step(Kg, Vg, np.full(w.B, m + 1, np.int32), qs[0])
+            if t < 2:
+                assert not res["hit"].any()
+            else:
+                assert res["hit"].all() and (res["p"] == m - 2).all()
+        m = w.C + 6
+        ov = np.full((w.B, w.Hq), -2, np.int32)
+        ov[0, 0] = m - 1                        # the previous call's entry: hidden
+        ov[0, 1] = m - 2
+        ov[1, 0] = m - 4                        # oldest entry still stored (W = 4)
+        res = orc.step(Kg, Vg, np.full(w.B, m + 1, np.int32), qs[0], override=ov)
+        assert res["override_invalid"] == 1
+        assert res["hit"][0, 0] == 0
+        assert res["p"][0, 1] == m - 2 and res["p"][1, 0] == m - 4
+        orc.reset()
