@@ -73,6 +73,8 @@ def parse():
                     help="MAC passes with MAC_F_FUSED_AMEND (the reduce updates the ring)")
     ap.add_argument("--ring-bf16", action="store_true",
                     help="MAC passes with MAC_F_RING_BF16 (ring queries kept as bfloat16)")
+    ap.add_argument("--stale-ring", action="store_true",
+                    help="MAC passes with MAC_F_STALE_RING (match skips the previous call's entry)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 2 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -132,25 +134,30 @@ class Bench:
         self.layer.decode_step(self.view, q, self.out, None, self.stream)
 
 
-def loop_us(w, flags, cache, q_dev, k_rows, v_rows, warmup, steps):
+def loop_us(w, flags, cache, q_dev, k_rows, v_rows, warmup, steps, hit_rate=None):
     """Microseconds per step of a decode loop run back to back (append and
     decode enqueued with no host synchronisation, as a serving loop runs):
-    each step's match waits for the previous step's amend, so this is the
-    step's whole cost, amend included.  Events on the decode stream around the
-    timed steps; a fresh ring, then `warmup` synchronised steps first."""
+    each step's match waits for the previous step's amend (the one before it
+    with the stale-by-one ring), so this is the step's whole cost, amend
+    included.  Events on the decode stream around the timed steps; a fresh
+    ring, then `warmup` synchronised steps first.  `hit_rate`, a dict, gets
+    the timed steps' share of heads that hit, under the same key."""
     import torch
     bn = Bench(w, flags, *cache)
     for t in range(warmup):
         bn.step(t, q_dev[t], k_rows[t], v_rows[t])
+    h0 = bn.layer.stats()["hits"]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(bn.stream)
     for t in range(warmup, warmup + steps):
         bn.enqueue(t, q_dev[t], k_rows[t], v_rows[t])
     e1.record(bn.stream)
-    bn.layer.stats()                       # synchronises every stream of the handle
+    h1 = bn.layer.stats()["hits"]          # synchronises every stream of the handle
     us = e0.elapsed_time(e1) * 1e3 / steps
     bn.layer.close()
+    if hit_rate is not None:
+        hit_rate[flags] = (h1 - h0) / (steps * w.B * w.Hq)
     return us
 
 
@@ -494,7 +501,8 @@ def main():
     # pass 1 (the timed region): the attention phase between two stream events
     # per step, no events between the kernels
     mac_flags = ((mac.MAC_F_FUSED_AMEND if args.fused_amend else 0) |
-                 (mac.MAC_F_RING_BF16 if args.ring_bf16 else 0))
+                 (mac.MAC_F_RING_BF16 if args.ring_bf16 else 0) |
+                 (mac.MAC_F_STALE_RING if args.stale_ring else 0))
     bench = Bench(w, mac_flags, kc, vc, paged, table)
     for t in range(args.warmup):
         bench.step(t, q_dev[t], k_rows[t], v_rows[t])
@@ -586,12 +594,31 @@ def main():
                       "mac": loop_us(wa, 0, cache, qa, k_rows, v_rows, 4, 16),
                       "mac_fused_amend": loop_us(wa, mac.MAC_F_FUSED_AMEND, cache, qa, k_rows,
                                                  v_rows, 4, 16)}}
-        # the mixed workload's decode loop, amend included, for both amend forms
-        loops = {"mac": loop_us(w, 0, cache, q_dev, k_rows, v_rows, 4, 16),
+        # the mixed workload's decode loop, amend included, for every amend form
+        lh = {}
+        loops = {"mac": loop_us(w, 0, cache, q_dev, k_rows, v_rows, 4, 16, lh),
                  "mac_fused_amend": loop_us(w, mac.MAC_F_FUSED_AMEND, cache, q_dev, k_rows,
-                                            v_rows, 4, 16),
+                                            v_rows, 4, 16, lh),
+                 "mac_stale_ring": loop_us(w, mac.MAC_F_STALE_RING, cache, q_dev, k_rows,
+                                           v_rows, 4, 16, lh),
                  "full_attention": loop_us(w, mac.MAC_F_DISABLE_REUSE, cache, q_dev, k_rows,
-                                           v_rows, 4, 16)}
+                                           v_rows, 4, 16),
+                 "head_hit_rate": {"mac": lh[0], "mac_stale_ring": lh[mac.MAC_F_STALE_RING]}}
+        # the stale-by-one ring matches two calls back: at rho = 0.99 the
+        # queries of the previous-but-one step are still within tau, so both
+        # ring forms hit everywhere and the loops differ by the overlap
+        ws = scaled(w, rho=("const", 0.99))
+        qsd = torch.as_tensor(queries(ws, steps=total), device="cuda")
+        sh = {}
+        stale = {"rho": 0.99,
+                 "loop_us_per_step": {
+                     "mac": loop_us(ws, 0, cache, qsd, k_rows, v_rows, 4, 16, sh),
+                     "mac_stale_ring": loop_us(ws, mac.MAC_F_STALE_RING, cache, qsd, k_rows,
+                                               v_rows, 4, 16, sh),
+                     "mac_fused_amend": loop_us(ws, mac.MAC_F_FUSED_AMEND, cache, qsd, k_rows,
+                                                v_rows, 4, 16)},
+                 "head_hit_rate": {"mac": sh[0], "mac_stale_ring": sh[mac.MAC_F_STALE_RING]}}
+        allhit["stale_ring_point"] = stale
 
     point_32k = None
     if not args.no_32k and args.config == "b16_128k" and not args.set and not args.r:
@@ -636,7 +663,8 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "context": w.C, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.d, "kv_layout": w.layout,
                    "ring": w.W, "band": w.r, "tau": w.tau, "rho": list(w.rho),
-                   "amend": "fused" if args.fused_amend else "async",
+                   "amend": ("fused" if args.fused_amend else
+                             "async, stale-by-one ring" if args.stale_ring else "async"),
                    "ring_queries": "bf16" if args.ring_bf16 else "fp32"},
         "hbm_gbps": float(np.mean(kv_bytes)) / (att_us * 1e-6) / 1e9,
         "tokens_per_s": w.B / (att_us * 1e-6),

@@ -72,7 +72,15 @@ enum {
      * to even) and match against those: half the match traffic, ~6x a token's
      * K/V bytes per ring entry as in the pages' Table 7.  Decisions can differ
      * from the fp32 ring where the nearest entries are within rounding. */
-    MAC_F_RING_BF16 = 32u
+    MAC_F_RING_BF16 = 32u,
+    /* Stale-by-one ring (the asynchronous cache update of Figure 2 (c) with
+     * one call of lag): the match of call t ignores the entry call t-1
+     * inserts, so it need not wait for that call's amend, which then runs
+     * beside call t's match (and, on a stream the handle owns, its complete).
+     * Call t's match and overrides see the entries of calls t-W .. t-2; the
+     * first two calls after init or reset miss, and W = 1 never hits.  Not
+     * combinable with MAC_F_FUSED_AMEND (MAC_EINVAL). */
+    MAC_F_STALE_RING = 64u
 };
 
 /* Layer configuration (host struct).  head_dim must be 128; Hq % Hkv == 0;
@@ -164,7 +172,8 @@ mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv /* host */, const v
  * queries, out receives [B][Hq][d] fp32 attention outputs.  override_pos is
  * NULL or [B][Hq] int32: -2 no override, -1 force a miss, p >= 0 force a hit
  * on the ring entry stored at position p (a counted miss when absent).
- * Waits on the previous step's amend; enqueues match, complete and the
+ * Waits on the previous step's amend (with MAC_F_STALE_RING, on the amend of
+ * the step before it); enqueues match, complete and the
  * reduce/merge on `stream`, then amend on the amend stream (or on `stream`
  * with MAC_F_SYNC_AMEND; with MAC_F_FUSED_AMEND the reduce does the ring
  * update and no amend is enqueued).  When the amend stream was supplied to

@@ -19,6 +19,10 @@
 //   partials   [NW + B*Hkv*nseg][G][SUMM] per-(worker, segment) unnormalised summaries
 //   as_full    [B][Hq][SUMM]        AS_{1:m} of this step, input of amend
 //   stats      [MAC_NSTAT] + [B*Hq][HEAD_NSTAT] + [B*Hkv][GRP_NSTAT] uint64 counters
+// With the stale-by-one ring (MAC_F_STALE_RING) q_copy, q_rot, m_buf and
+// as_full are held twice and calls alternate between the copies, so that the
+// amend of call t-1, still running, reads its own while call t writes the
+// other.
 // A group's union span (the keys complete streams for it) starts at the
 // smallest first key of its heads' spans; the plan derives it from dec_start.
 // The work list is cut into segments: one per group, or with fused amend two
@@ -88,10 +92,12 @@ struct State {
 
 // Launchers (enqueue only; return the launch status).
 // W > TILE_W: per-tile nearest entries, read by launch_match's kernel.
+// `hidden` is a ring slot this call's match and override ignore (-1: none).
 hipError_t launch_match_tiles(const Shape &s, const State &st, const KvView &kv,
-                              const int32_t *seq_lens, const float *q_pre, hipStream_t stream);
+                              const int32_t *seq_lens, const float *q_pre, int hidden,
+                              hipStream_t stream);
 hipError_t launch_match(const Shape &s, const State &st, const KvView &kv, const int32_t *seq_lens,
-                        const float *q_pre, const int32_t *override_pos, float *out,
+                        const float *q_pre, const int32_t *override_pos, float *out, int hidden,
                         hipStream_t stream);
 hipError_t launch_complete(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
                            int n_blocks, hipStream_t stream);

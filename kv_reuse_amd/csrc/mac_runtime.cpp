@@ -21,14 +21,16 @@ struct mac_ctx {
     mac_config cfg{};
     mac::Shape shape{};
     mac::State st{};
+    mac::State st_odd{};     // odd calls with the stale-by-one ring: own step buffers
     int device = 0;
     int n_blocks = 0;
     bool kv_fp32 = false;
     hipStream_t main_stream = nullptr;
     hipStream_t amend_stream = nullptr;
     bool own_amend = false;
-    hipEvent_t ev_attn = nullptr, ev_amend = nullptr, ev_drain = nullptr;
-    bool amend_pending = false;
+    hipEvent_t ev_attn = nullptr, ev_drain = nullptr;
+    hipEvent_t ev_amend[2] = {};     // after the amend of calls of even / odd index
+    bool amend_pending[2] = {};
     hipEvent_t tm[6] = {};
     bool timed_step = false;
     long long calls = 0;
@@ -66,10 +68,11 @@ mac_status fail_hip(mac_handle h, const char *what, hipError_t e)
 struct Sizes {
     size_t ring_q, ring_s, ring_pos, qvec, m_buf, dec_i, dec_f, grp_parts, partials, as_full,
         stats, inv_freq, tiles;
+    size_t step_copies;   // copies of the buffers amend reads: 2 with the stale-by-one ring
     size_t total() const
     {
-        return ring_q + ring_s + ring_pos + 2 * qvec + m_buf + 3 * dec_i + dec_f + grp_parts +
-               partials + as_full + stats + inv_freq + tiles;
+        return ring_q + ring_s + ring_pos + step_copies * (2 * qvec + m_buf + as_full) +
+               3 * dec_i + dec_f + grp_parts + partials + stats + inv_freq + tiles;
     }
 };
 
@@ -102,6 +105,7 @@ Sizes sizes_for(const mac_config &c, int n_workers)
     s.inv_freq = round256(mac::D / 2 * sizeof(double));
     const size_t ntiles = (W + mac::TILE_W - 1) / mac::TILE_W;
     s.tiles = W > (size_t)mac::TILE_W ? round256(B * Hq * ntiles * 3 * sizeof(float)) : 0;
+    s.step_copies = (c.flags & MAC_F_STALE_RING) ? 2 : 1;
     return s;
 }
 
@@ -168,9 +172,14 @@ mac_status validate(const mac_config *c, std::string &why)
         return MAC_EUNSUPPORTED;
     }
     const uint32_t known = MAC_F_DISABLE_REUSE | MAC_F_SYNC_AMEND | MAC_F_TIMING |
-                           MAC_F_RECORD_DEBUG | MAC_F_FUSED_AMEND | MAC_F_RING_BF16;
+                           MAC_F_RECORD_DEBUG | MAC_F_FUSED_AMEND | MAC_F_RING_BF16 |
+                           MAC_F_STALE_RING;
     if (c->flags & ~known) {
         why = "unknown flag bits";
+        return MAC_EINVAL;
+    }
+    if ((c->flags & MAC_F_STALE_RING) && (c->flags & MAC_F_FUSED_AMEND)) {
+        why = "MAC_F_STALE_RING needs the separate amend; it excludes MAC_F_FUSED_AMEND";
         return MAC_EINVAL;
     }
     return MAC_OK;
@@ -219,7 +228,8 @@ void release(mac_ctx *h)
         (void)hipFree(h->blocks[i]);
     h->n_alloc = 0;
     if (h->ev_attn) (void)hipEventDestroy(h->ev_attn);
-    if (h->ev_amend) (void)hipEventDestroy(h->ev_amend);
+    for (auto &e : h->ev_amend)
+        if (e) (void)hipEventDestroy(e);
     if (h->ev_drain) (void)hipEventDestroy(h->ev_drain);
     for (auto &e : h->tm)
         if (e) (void)hipEventDestroy(e);
@@ -337,6 +347,13 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     h->st.grp_stats = h->st.head_stats + (long)cfg->batch * cfg->num_q_heads * mac::HEAD_NSTAT;
     h->st.inv_freq = (const double *)take(sz.inv_freq);
     h->st.tile_best = sz.tiles ? (float *)take(sz.tiles) : nullptr;
+    h->st_odd = h->st;
+    if (sz.step_copies == 2) {
+        h->st_odd.q_copy = (float *)take(sz.qvec);
+        h->st_odd.q_rot = (float *)take(sz.qvec);
+        h->st_odd.m_buf = (int32_t *)take(sz.m_buf);
+        h->st_odd.as_full = (float *)take(sz.as_full);
+    }
 
     e = hipMemset(base, 0, sz.total());
     if (e != hipSuccess)
@@ -370,7 +387,8 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
         h->own_amend = true;
     }
     if (hipEventCreateWithFlags(&h->ev_attn, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_amend, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_amend[0], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_amend[1], hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&h->ev_drain, hipEventDisableTiming) != hipSuccess)
         return bail(MAC_EHIP, "hipEventCreate failed");
     for (auto &ev : h->tm)
@@ -399,8 +417,9 @@ mac_status mac_reset(mac_handle h)
 {
     if (!h)
         return fail(nullptr, MAC_EINVAL, "handle is NULL");
-    if (h->amend_pending)
-        MAC_HIP(h, hipStreamWaitEvent(h->main_stream, h->ev_amend, 0));
+    for (int i = 0; i < 2; ++i)
+        if (h->amend_pending[i])
+            MAC_HIP(h, hipStreamWaitEvent(h->main_stream, h->ev_amend[i], 0));
     MAC_HIP(h, mac::launch_reset(h->shape, h->st, h->main_stream));
     h->calls = 0;
     h->timed_step = false;
@@ -440,16 +459,23 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
     hipStream_t st = stream ? (hipStream_t)stream : h->main_stream;
     const mac::KvView v = to_view(h, kv);
     const bool timing = h->cfg.flags & MAC_F_TIMING;
+    const int cur = (int)(h->calls & 1);
 
-    // match(m) reads the ring amend(m-1) writes
-    if (h->amend_pending)
-        MAC_HIP(h, hipStreamWaitEvent(st, h->ev_amend, 0));
+    // match(t) reads the ring amend(t-1) writes.  The stale-by-one ring hides
+    // that slot from match(t), which then waits only for amend(t-2); the two
+    // calls also work on separate copies of the buffers amend reads.
+    const bool stale = h->cfg.flags & MAC_F_STALE_RING;
+    const mac::State &S = (stale && cur) ? h->st_odd : h->st;
+    const int wait_ev = stale ? cur : cur ^ 1;
+    if (h->amend_pending[wait_ev])
+        MAC_HIP(h, hipStreamWaitEvent(st, h->ev_amend[wait_ev], 0));
+    const int hidden = (stale && h->calls > 0) ? (int)((h->calls - 1) % h->cfg.ring_size) : -1;
     if (timing)
         MAC_HIP(h, hipEventRecord(h->tm[0], st));
     if (h->shape.reuse && h->cfg.ring_size > mac::TILE_W)
-        MAC_HIP(h, mac::launch_match_tiles(h->shape, h->st, v, kv->seq_lens, q_pre_rope, st));
-    MAC_HIP(h, mac::launch_match(h->shape, h->st, v, kv->seq_lens, q_pre_rope, override_pos, out,
-                                 st));
+        MAC_HIP(h, mac::launch_match_tiles(h->shape, S, v, kv->seq_lens, q_pre_rope, hidden, st));
+    MAC_HIP(h, mac::launch_match(h->shape, S, v, kv->seq_lens, q_pre_rope, override_pos, out,
+                                 hidden, st));
     // The complete kernel is a persistent grid with equal static shares per
     // wave: a kernel still holding CU slots when it launches delays some of
     // its waves and with them the whole launch (measured: +35 % when an amend
@@ -466,11 +492,11 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
     }
     if (timing)
         MAC_HIP(h, hipEventRecord(h->tm[1], st));
-    MAC_HIP(h, mac::launch_complete(h->shape, h->st, v, h->kv_fp32, h->n_blocks, st));
+    MAC_HIP(h, mac::launch_complete(h->shape, S, v, h->kv_fp32, h->n_blocks, st));
     if (timing)
         MAC_HIP(h, hipEventRecord(h->tm[2], st));
     const int slot_new = (int)(h->calls % h->cfg.ring_size);
-    MAC_HIP(h, mac::launch_reduce(h->shape, h->st, out, slot_new, st));
+    MAC_HIP(h, mac::launch_reduce(h->shape, S, out, slot_new, st));
     if (timing)
         MAC_HIP(h, hipEventRecord(h->tm[3], st));
 
@@ -482,11 +508,11 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
         }
         if (timing)
             MAC_HIP(h, hipEventRecord(h->tm[4], as));
-        MAC_HIP(h, mac::launch_amend(h->shape, h->st, v, h->kv_fp32, slot_new, as));
+        MAC_HIP(h, mac::launch_amend(h->shape, S, v, h->kv_fp32, slot_new, as));
         if (timing)
             MAC_HIP(h, hipEventRecord(h->tm[5], as));
-        MAC_HIP(h, hipEventRecord(h->ev_amend, as));
-        h->amend_pending = true;
+        MAC_HIP(h, hipEventRecord(h->ev_amend[cur], as));
+        h->amend_pending[cur] = true;
     }
     h->timed_step = timing;
     h->calls += 1;

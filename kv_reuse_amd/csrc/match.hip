@@ -165,7 +165,8 @@ __device__ __forceinline__ void scan_ring_tile(const Shape &s, const State &st, 
 // nearest entry; the match kernel then reduces the tiles of each head.
 __global__ __launch_bounds__(64) void match_tiles_kernel(Shape s, State st, KvView kv,
                                                          const int32_t *__restrict__ seq_lens,
-                                                         const float *__restrict__ q_pre)
+                                                         const float *__restrict__ q_pre,
+                                                         int hidden)
 {
     const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int ntiles = (s.W + TILE_W - 1) / TILE_W;
@@ -175,7 +176,9 @@ __global__ __launch_bounds__(64) void match_tiles_kernel(Shape s, State st, KvVi
     const int nslot = min(TILE_W, s.W - base);
     bool bad;
     const int m = query_position(kv, seq_lens[b], bad);
-    const int pos_l = lane < nslot ? st.ring_pos[(long)b * s.W + base + lane] : -1;
+    const int pos_l = (lane < nslot && base + lane != hidden)
+                          ? st.ring_pos[(long)b * s.W + base + lane]
+                          : -1;
     float kd;
     int kp, kj;
     scan_ring_tile(s, st, idx, base, nslot, q_pre + idx * D, pos_l, m, kd, kp, kj);
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
                                                    const int32_t *__restrict__ seq_lens,
                                                    const float *__restrict__ q_pre,
                                                    const int32_t *__restrict__ ovr,
-                                                   float *__restrict__ out)
+                                                   float *__restrict__ out, int hidden)
 {
     const int h = blockIdx.x, b = blockIdx.y;
     const long idx = (long)b * s.Hq + h;
@@ -216,7 +219,8 @@ __global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
     const float qa = q_pre[idx * D + lane], qb = q_pre[idx * D + lane + 64];
     const double inv = st.inv_freq[lane];
     const int ov = ovr ? ovr[idx] : -2;
-    const int pos_l = (s.reuse && lane < s.W) ? st.ring_pos[(long)b * s.W + lane] : -1;
+    const int pos_l =
+        (s.reuse && lane < s.W && lane != hidden) ? st.ring_pos[(long)b * s.W + lane] : -1;
     unsigned long long old[HEAD_NSTAT] = {};
     if (lane == 0) {
 #pragma unroll
@@ -306,7 +310,7 @@ __global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
                     const int sl = c0 + lane;
                     const int ps = c0 == 0 ? pos_l
                                            : (sl < s.W ? st.ring_pos[(long)b * s.W + sl] : -1);
-                    const bool mine = sl < s.W && ov <= m && ps == ov;
+                    const bool mine = sl < s.W && sl != hidden && ov <= m && ps == ov;
                     const unsigned long long bal = __ballot(mine);
                     if (bal) {
                         slot = c0 + 63 - __clzll(bal);
@@ -343,19 +347,21 @@ __global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
 }  // namespace
 
 hipError_t launch_match_tiles(const Shape &s, const State &st, const KvView &kv,
-                              const int32_t *seq_lens, const float *q_pre, hipStream_t stream)
+                              const int32_t *seq_lens, const float *q_pre, int hidden,
+                              hipStream_t stream)
 {
     const dim3 grid((s.W + TILE_W - 1) / TILE_W, s.Hq, s.B);
-    hipLaunchKernelGGL(match_tiles_kernel, grid, dim3(64), 0, stream, s, st, kv, seq_lens, q_pre);
+    hipLaunchKernelGGL(match_tiles_kernel, grid, dim3(64), 0, stream, s, st, kv, seq_lens, q_pre,
+                       hidden);
     return hipGetLastError();
 }
 
 hipError_t launch_match(const Shape &s, const State &st, const KvView &kv, const int32_t *seq_lens,
-                        const float *q_pre, const int32_t *override_pos, float *out,
+                        const float *q_pre, const int32_t *override_pos, float *out, int hidden,
                         hipStream_t stream)
 {
     hipLaunchKernelGGL(match_kernel, dim3(s.Hq, s.B), dim3(64), 0, stream, s, st, kv, seq_lens,
-                       q_pre, override_pos, out);
+                       q_pre, override_pos, out, hidden);
     return hipGetLastError();
 }
 

@@ -39,6 +39,19 @@ def test_valid_config_passes():
     mac.mac_config_validate(_cfg(layout=mac.MAC_KV_PAGED, kv_dtype=mac.MAC_FP32, ring_size=64,
                                  num_q_heads=32, num_kv_heads=4, tau=-1.0))
     mac.mac_config_validate(_cfg(ring_size=2048))     # the pages' largest window (Table 7)
+    mac.mac_config_validate(_cfg(flags=mac.MAC_F_STALE_RING | mac.MAC_F_RING_BF16))
+
+
+def test_stale_ring_doubles_only_the_step_buffers():
+    """The stale-by-one ring holds a second copy of the per-call buffers the
+    amend reads (two query vectors, a position and AS_{1:m} per head); the
+    rings themselves are not duplicated."""
+    B, Hq = 16, 32
+    base = mac.mac_aux_bytes(_cfg(batch=B, num_q_heads=Hq, num_kv_heads=8), 256)
+    st = mac.mac_aux_bytes(_cfg(batch=B, num_q_heads=Hq, num_kv_heads=8,
+                                flags=mac.MAC_F_STALE_RING), 256)
+    per_head = (2 * 128 + 132) * 4
+    assert st - base == pytest.approx(B * Hq * per_head + B * 4, abs=3 * 256)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -59,6 +72,7 @@ def test_valid_config_passes():
     (dict(max_seq_len=100), mac.MAC_EINVAL),
     (dict(batch=1024, num_q_heads=8, num_kv_heads=8), mac.MAC_EUNSUPPORTED),
     (dict(flags=1 << 9), mac.MAC_EINVAL),
+    (dict(flags=mac.MAC_F_STALE_RING | mac.MAC_F_FUSED_AMEND), mac.MAC_EINVAL),
 ])
 def test_invalid_configs_rejected(kw, status):
     with pytest.raises(mac.MacError) as ei:

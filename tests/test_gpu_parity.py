@@ -162,6 +162,43 @@ def test_ring_bf16_matches_oracle(gpu_lib, case):
     _run(w, w.steps, flags=flags, oracle_flags=oracle.F_RING_BF16)
 
 
+_STALE_CASES = {
+    "cpu4k_fp32": (lambda: scaled(get_config("cpu4k"), steps=120, rho=("const", 0.985)), {}),
+    "paged_mixed": (lambda: scaled(get_config("b16_128k"), B=4, C=3000, steps=48,
+                                   rho=("per_request_uniform", 0.95, 0.995)), {}),
+    "moe_g8": (lambda: scaled(get_config("moe_122k"), B=2, C=2500, steps=40), {"r": 64}),
+    "ragged": (lambda: scaled(get_config("b16_128k"), B=6, C=1200, steps=40, rho=("const", 0.985)),
+               {"prefill": [1200, 1199, 1185, 1024, 777, 17]}),
+    "window_100": (lambda: scaled(get_config("b16_128k"), B=2, C=600, steps=150, W=100,
+                                  rho=("const", 0.985)), {}),
+    "window_2": (lambda: scaled(get_config("b16_128k"), B=2, C=600, steps=30, W=2,
+                                rho=("const", 0.985)), {}),
+    "window_1": (lambda: scaled(get_config("cpu4k"), C=300, steps=20, W=1, r=1, kv="bf16"), {}),
+    "ring_bf16": (lambda: scaled(get_config("b16_128k"), B=2, C=600, steps=60, W=48,
+                                 rho=("const", 0.985)), {"bf16": True}),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_STALE_CASES))
+def test_stale_ring_matches_oracle(gpu_lib, case):
+    """MAC_F_STALE_RING: call t's match skips the slot call t-1 inserts, as
+    the oracle with F_STALE_RING; decisions bit-exact (W = 1 never hits).
+    The nearest visible entry is two calls back, so the AR(1) queries use
+    rho = 0.985 (relative distance ~ sqrt(2 (1 - rho^2)) ~ 0.24 < tau)."""
+    import kv_reuse_amd as mac
+    import oracle
+    make, kw = _STALE_CASES[case]
+    w = make()
+    bf16 = kw.pop("bf16", False)
+    flags = mac.MAC_F_STALE_RING | (mac.MAC_F_RING_BF16 if bf16 else 0)
+    oflags = oracle.F_STALE_RING | (oracle.F_RING_BF16 if bf16 else 0)
+    hits, _ = _run(w, w.steps, flags=flags, oracle_flags=oflags, **kw)
+    if w.W == 1:
+        assert hits == 0
+    else:
+        assert hits > 0
+
+
 def test_disable_reuse_is_full_attention(gpu_lib):
     import kv_reuse_amd as mac
     import oracle

@@ -61,10 +61,15 @@ class Plain:
         return self.out.clone()
 
 
-def test_async_amend_bit_identical_to_sync():
+@pytest.mark.parametrize("stale", [False, True])
+def test_async_amend_bit_identical_to_sync(stale):
+    """Steps issued back to back without synchronisation.  With the
+    stale-by-one ring, amend(t-1) may still run during call t's match and
+    complete; the bits must still equal those of amend on the decode stream."""
     w = _case(steps=160, W=8, r=64)
-    a = Plain(w, paged=True)
-    s = Plain(w, paged=True, flags=mac.MAC_F_SYNC_AMEND, K=a.K, V=a.V)
+    base = mac.MAC_F_STALE_RING if stale else 0
+    a = Plain(w, paged=True, flags=base)
+    s = Plain(w, paged=True, flags=base | mac.MAC_F_SYNC_AMEND, K=a.K, V=a.V)
     qs = queries(w)
     for t in range(w.steps):
         seq = np.full(w.B, w.C + t + 1)
@@ -117,6 +122,28 @@ def test_override_to_absent_position_is_counted_miss():
         assert info["hit_gpu"][0, 3] == 0
         assert info["res"]["override_invalid"] == 1
         assert ls.layer.stats()["override_invalid"] == before + 1
+    finally:
+        ls.close()
+
+
+def test_stale_ring_override_of_previous_call_is_counted_miss():
+    """With MAC_F_STALE_RING the previous call's entry is hidden from the
+    override too; the entry before it is not."""
+    from gpu_harness import Lockstep
+    w = _case(steps=6)
+    ls = Lockstep(w, flags=mac.MAC_F_STALE_RING, oracle_flags=oracle.F_STALE_RING)
+    try:
+        for t in range(5):
+            ls.step(t)
+        m = w.C + 5
+        ov = np.full((w.B, w.Hq), -2, np.int32)
+        ov[0, 3] = m - 1          # inserted by the previous call: hidden
+        ov[1, 2] = m - 2
+        info = ls.step(5, override=ov)
+        assert info["res"]["override_invalid"] == 1
+        assert info["hit_gpu"][0, 3] == 0
+        assert info["hit_gpu"][1, 2] == 1 and info["p_gpu"][1, 2] == m - 2
+        assert ls.layer.stats()["override_invalid"] == 1
     finally:
         ls.close()
 
