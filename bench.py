@@ -67,8 +67,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline-kernel", action="store_true")
     ap.add_argument("--no-32k", action="store_true", help="skip the 32K speedup point")
-    ap.add_argument("--figures", action="store_true",
-                    help="synthetic analogs of the pages' Figures 4, 5 and 8 (one JSON line)")
+    ap.add_argument("--figures", nargs="?", const="fig4,fig5,fig8a,fig8b", default=None,
+                    help="synthetic analogs of the pages' Figures 4, 5 and 8 (one JSON line); "
+                         "optionally a comma list of fig4, fig5, fig8a, fig8b")
     ap.add_argument("--fused-amend", action="store_true",
                     help="MAC passes with MAC_F_FUSED_AMEND (the reduce updates the ring)")
     ap.add_argument("--ring-bf16", action="store_true",
@@ -301,7 +302,10 @@ def figures(args):
             query correlation rho (128K x 16 paged cache);
       fig4: MAC-vs-full relative output error vs the reuse gap m - p (hits
             forced through the override input) and the band r;
-      fig8: match latency vs query heads per KV head G and window W.
+      fig8a: match latency vs query heads per KV head G and window W;
+      fig8b: complete kernel time with the balanced plan, with an unbalanced
+            one (the same number of waves per KV group), and the ideal
+            (bytes at the full-attention kernel's bandwidth).
     Prints one JSON line."""
     import torch
     import kv_reuse_amd as mac
@@ -334,15 +338,46 @@ def figures(args):
         return {"head_hit_rate": hits / (steps * B * Hq), "skipped_keys": 1.0 - toks / full,
                 "attention_us": float(np.mean(att))}
 
-    fig5 = []
-    for tau in (0.1, 0.2, 0.3, 0.45, 0.6):
+    parts = set(args.figures.split(","))
+    fig5, fig5_rho, fig4, fig8, fig8b, full_us = [], [], [], [], [], None
+    row_bytes = 2 * base.d * 2
+
+    def complete_us(w, flags, warm=4, steps=8):
+        qd = torch.as_tensor(queries(w, steps=warm + steps), device="cuda")
+        bn = Bench(w, flags | mac.MAC_F_TIMING, *cache)
+        us, toks, prev = [], 0, None
+        for t in range(warm + steps):
+            st = bn.step(t, qd[t], k_rows[t], v_rows[t])
+            if t >= warm:
+                us.append(st["last_us_complete"])
+                toks += st["kv_tokens_critical"] - prev["kv_tokens_critical"]
+            prev = st
+        bn.layer.close()
+        return float(np.mean(us)), toks * row_bytes / steps
+
+    if "fig8b" in parts:
+        # Figure 8 (b): the plan against an unbalanced split and the ideal
+        f_us, f_bytes = complete_us(scaled(base, tau=-1.0), 0)
+        bw = f_bytes / (f_us * 1e-6)
+        for label, w in (("headline queries", base),
+                         ("rho 0.96", scaled(base, rho=("const", 0.96))),
+                         ("rho 0.97", scaled(base, rho=("const", 0.97))),
+                         ("rho 0.99", scaled(base, rho=("const", 0.99)))):
+            bal, nb = complete_us(w, 0)
+            unb, nb2 = complete_us(w, mac.MAC_F_UNBALANCED_PLAN)
+            assert nb == nb2, "the two plans streamed different bytes"
+            fig8b.append({"queries": label, "kv_bytes_per_step": nb, "balanced_us": bal,
+                          "unbalanced_us": unb, "ideal_us": nb / bw * 1e6,
+                          "full_attention_complete_us": f_us})
+
+    for tau in ((0.1, 0.2, 0.3, 0.45, 0.6) if "fig5" in parts else ()):
         for W in (16, 32, 256, 1024):
             r = rates(scaled(base, tau=tau, W=W))
             r.update({"tau": tau, "W": W})
             fig5.append(r)
-    full_us = rates(scaled(base, tau=-1.0))["attention_us"]
-    fig5_rho = []
-    for rho in (0.9, 0.95, 0.96, 0.97, 0.98, 0.99):
+    if "fig5" in parts:
+        full_us = rates(scaled(base, tau=-1.0))["attention_us"]
+    for rho in ((0.9, 0.95, 0.96, 0.97, 0.98, 0.99) if "fig5" in parts else ()):
         r = rates(scaled(base, rho=("const", rho)))
         r.update({"rho": rho, "speedup_vs_full": full_us / r["attention_us"]})
         fig5_rho.append(r)
@@ -377,9 +412,8 @@ def figures(args):
         e = torch.stack([(g - f).norm(dim=-1) / f.norm(dim=-1) for g, f in zip(got, ref)])
         return float(e.mean()), float(e.max())
 
-    ref = outputs(wq, mac.MAC_F_DISABLE_REUSE)
-    fig4 = []
-    for r in (64, 256, 1024):
+    ref = outputs(wq, mac.MAC_F_DISABLE_REUSE) if "fig4" in parts else None
+    for r in ((64, 256, 1024) if "fig4" in parts else ()):
         for gap in (1, 2, 4, 8, 16, 32):
             mean_e, max_e = rel_err(outputs(scaled(wq, r=r), 0, gap, fresh=True), ref)
             fig4.append({"r": r, "gap": gap, "summaries": "fresh", "mean_rel_err": mean_e,
@@ -390,9 +424,8 @@ def figures(args):
     del cache, k_rows, v_rows
     torch.cuda.empty_cache()
 
-    # fig8: match latency (library HIP events) vs G and W at a short context
-    fig8 = []
-    for G in (1, 2, 4, 8):
+    # fig8a: match latency (library HIP events) vs G and W at a short context
+    for G in ((1, 2, 4, 8) if "fig8a" in parts else ()):
         w8 = scaled(base, Hkv=Hq // G, C=4096, steps=12, rho=("const", 0.97))
         K, V = kv_logical(w8, "cuda")
         idx = torch.arange(w8.C, w8.C + 12, device="cuda")
@@ -418,7 +451,7 @@ def figures(args):
 
     print(json.dumps({"figures": {"fig5_tau_window": fig5, "fig5_rho": fig5_rho,
                                   "full_attention_us": full_us, "fig4_gap_band": fig4,
-                                  "fig8_match": fig8},
+                                  "fig8_match": fig8, "fig8b_plan": fig8b},
                       "config": {"workload": "b16_128k", "batch": B, "context": base.C,
                                  "q_heads": Hq, "kv_heads": Hkv, "data": "synthetic"}}),
           flush=True)

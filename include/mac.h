@@ -80,7 +80,14 @@ enum {
      * Call t's match and overrides see the entries of calls t-W .. t-2; the
      * first two calls after init or reset miss, and W = 1 never hits.  Not
      * combinable with MAC_F_FUSED_AMEND (MAC_EINVAL). */
-    MAC_F_STALE_RING = 64u
+    MAC_F_STALE_RING = 64u,
+    /* Measurement baseline for Figure 8 (b): replace the balanced plan (the
+     * step's pages split evenly over the waves of the complete grid, Figure
+     * 3 (b)) with an unbalanced one that gives every (request, KV group) the
+     * same number of waves, so the longest span sets the step's time.  Same
+     * results up to rounding.  MAC_EUNSUPPORTED at mac_init when the grid has
+     * fewer waves than batch * num_kv_heads (x2 with MAC_F_FUSED_AMEND). */
+    MAC_F_UNBALANCED_PLAN = 128u
 };
 
 /* Layer configuration (host struct).  head_dim must be 128; Hq % Hkv == 0;

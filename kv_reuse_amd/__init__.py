@@ -5,7 +5,7 @@ include/mac.h).  This package marshals arguments; see kv_reuse_amd._lib.
 """
 from ._lib import (EXPORTS, LIB_PATH, MAC_BF16, MAC_EHIP, MAC_EINVAL, MAC_ENOMEM, MAC_ESTATE,
                    MAC_EUNSUPPORTED, MAC_F_DISABLE_REUSE, MAC_F_FUSED_AMEND, MAC_F_RECORD_DEBUG,
-                   MAC_F_RING_BF16, MAC_F_STALE_RING,
+                   MAC_F_RING_BF16, MAC_F_STALE_RING, MAC_F_UNBALANCED_PLAN,
                    MAC_F_SYNC_AMEND,
                    MAC_F_TIMING, MAC_FP32, MAC_KV_CONTIGUOUS, MAC_KV_PAGED, MAC_OK, MacConfig,
                    MacError, MacKvView, MacStats, load, mac_append_kv, mac_aux_bytes,

@@ -20,6 +20,7 @@ MAC_F_DISABLE_REUSE, MAC_F_SYNC_AMEND, MAC_F_TIMING, MAC_F_RECORD_DEBUG = 1, 2, 
 MAC_F_FUSED_AMEND = 16
 MAC_F_RING_BF16 = 32
 MAC_F_STALE_RING = 64
+MAC_F_UNBALANCED_PLAN = 128
 
 EXPORTS = ["mac_config_validate", "mac_aux_bytes", "mac_init", "mac_destroy", "mac_reset",
            "mac_append_kv", "mac_decode_step", "mac_stats", "mac_debug_last", "mac_last_error",

@@ -23,14 +23,14 @@ __global__ __launch_bounds__(BLOCK) void complete_kernel(Shape s, State st, KvVi
     const int P = s_off[nS];
     if (P == 0)
         return;
-    const int nW = active_workers(st.n_workers, P);
+    const int nW = s.unbalanced ? st.n_workers : active_workers(st.n_workers, P);
     if (blockIdx.x == 0)
         publish_plan(s, st, s_off, nW);
     const int w = blockIdx.x * WAVES + (threadIdx.x >> 6);
     if (w >= nW)
         return;
-    long x = (long)w * P / nW;
-    const long x1 = (long)(w + 1) * P / nW;
+    long x, x1;
+    worker_share(s, st, s_off, nS, nW, P, w, x, x1);
     int sg = find_segment(s_off, nS, x);
     unsigned long long *bad = &st.stats[ST_BAD_INPUT];
     while (x < x1) {
@@ -402,15 +402,15 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
     const int P = s_off[nS];
     if (P == 0)
         return;
-    const int nW = active_workers(st.n_workers, P);
+    const int nW = s.unbalanced ? st.n_workers : active_workers(st.n_workers, P);
     if (blockIdx.x == 0)
         publish_plan(s, st, s_off, nW);
     const int wv = threadIdx.x >> 6, lane = lane_id();
     const int w = blockIdx.x * WAVES + wv;
     if (w >= nW)
         return;
-    long x = (long)w * P / nW;
-    const long x1 = (long)(w + 1) * P / nW;
+    long x, x1;
+    worker_share(s, st, s_off, nS, nW, P, w, x, x1);
     int sg = find_segment(s_off, nS, x);
     unsigned long long *bad = &st.stats[ST_BAD_INPUT];
     const uint16_t *kb = reinterpret_cast<const uint16_t *>(kv.k);

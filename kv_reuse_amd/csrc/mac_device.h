@@ -460,6 +460,38 @@ __device__ __forceinline__ int page_owner(long x, int nW, int P)
     return (int)(((x + 1) * (long)nW - 1) / P);
 }
 
+// Waves of the unbalanced plan given to each segment (the host checks that
+// every segment gets at least one).
+__device__ __forceinline__ int waves_per_segment(const State &st, int nS)
+{
+    return st.n_workers / nS;
+}
+
+// Worker w's share [x0, x1) of the flattened page list (x0 >= x1: none).
+// Balanced plan (the default, Figure 3 (b)): the nW active waves split all P
+// pages of the step evenly, whatever segment they belong to.  Unbalanced plan
+// (MAC_F_UNBALANCED_PLAN, the baseline of Figure 8 (b)): every segment gets
+// the same k waves, which split that segment's own pages evenly (one wave per
+// page when it has fewer than k), so the longest span sets the time.
+__device__ __forceinline__ void worker_share(const Shape &s, const State &st, const int *off,
+                                             int nS, int nW, int P, int w, long &x0, long &x1)
+{
+    if (!s.unbalanced) {
+        x0 = (long)w * P / nW;
+        x1 = (long)(w + 1) * P / nW;
+        return;
+    }
+    const int k = waves_per_segment(st, nS), sg = w / k, j = w % k;
+    x0 = x1 = 0;
+    if (sg >= nS)
+        return;
+    const int n = off[sg + 1] - off[sg], kk = min(k, n);
+    if (j >= kk)
+        return;
+    x0 = off[sg] + (long)j * n / kk;
+    x1 = off[sg] + (long)(j + 1) * n / kk;
+}
+
 // Last segment i with off[i] <= x (segments with no pages are skipped by the
 // caller).
 __device__ __forceinline__ int find_segment(const int *off, int nS, long x)
@@ -483,9 +515,13 @@ __device__ __forceinline__ int find_segment(const int *off, int nS, long x)
 __device__ inline void publish_plan(const Shape &s, const State &st, const int *off, int nW)
 {
     const int nG = s.B * s.Hkv, nS = nG * s.nseg, P = off[nS];
+    const int k = s.unbalanced ? waves_per_segment(st, nS) : 0;
     for (int i = threadIdx.x; i < nS; i += blockDim.x) {
         int2 r = make_int2(0, -1);
-        if (off[i + 1] > off[i])
+        const int n = off[i + 1] - off[i];
+        if (n > 0 && s.unbalanced)
+            r = make_int2(i * k, i * k + min(k, n) - 1);
+        else if (n > 0)
             r = make_int2(page_owner(off[i], nW, P), page_owner((long)off[i + 1] - 1, nW, P));
         reinterpret_cast<int2 *>(st.grp_parts)[i] = r;
     }

@@ -75,6 +75,7 @@ struct Shape {
     int32_t reuse;          // 0: every head misses
     int32_t nseg;           // work-list segments per group: 1, or 2 when amend is fused
     int32_t ring_bf16;      // ring queries stored as bf16 (rounded to nearest, ties to even)
+    int32_t unbalanced;     // plan: the same number of waves per segment (measurement baseline)
 };
 
 struct State {

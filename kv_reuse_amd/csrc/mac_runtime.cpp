@@ -173,7 +173,7 @@ mac_status validate(const mac_config *c, std::string &why)
     }
     const uint32_t known = MAC_F_DISABLE_REUSE | MAC_F_SYNC_AMEND | MAC_F_TIMING |
                            MAC_F_RECORD_DEBUG | MAC_F_FUSED_AMEND | MAC_F_RING_BF16 |
-                           MAC_F_STALE_RING;
+                           MAC_F_STALE_RING | MAC_F_UNBALANCED_PLAN;
     if (c->flags & ~known) {
         why = "unknown flag bits";
         return MAC_EINVAL;
@@ -310,6 +310,10 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
         (size_t)(cfg->batch * cfg->num_kv_heads * segments_per_group(*cfg) + 1) * sizeof(int);
     h->n_blocks = n_cu * mac::complete_blocks_per_cu(h->kv_fp32, G, plan_lds);
     h->st.n_workers = h->n_blocks * mac::WAVES;
+    const long n_seg = (long)cfg->batch * cfg->num_kv_heads * segments_per_group(*cfg);
+    if ((cfg->flags & MAC_F_UNBALANCED_PLAN) && n_seg > h->st.n_workers)
+        return bail(MAC_EUNSUPPORTED, "MAC_F_UNBALANCED_PLAN needs at least one wave of the "
+                                      "complete grid per work-list segment");
 
     Sizes sz = sizes_for(*cfg, h->st.n_workers);
     h->aux_bytes = sz.total();
@@ -377,6 +381,7 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     h->shape.reuse = !(cfg->flags & MAC_F_DISABLE_REUSE) && cfg->tau >= 0.f;
     h->shape.nseg = segments_per_group(*cfg);
     h->shape.ring_bf16 = (cfg->flags & MAC_F_RING_BF16) ? 1 : 0;
+    h->shape.unbalanced = (cfg->flags & MAC_F_UNBALANCED_PLAN) ? 1 : 0;
 
     if (amend_stream) {
         h->amend_stream = (hipStream_t)amend_stream;

@@ -199,6 +199,30 @@ def test_stale_ring_matches_oracle(gpu_lib, case):
         assert hits > 0
 
 
+_UNBALANCED_CASES = {
+    "cpu4k_fp32": (lambda: scaled(get_config("cpu4k"), steps=60), 0),
+    "paged_mixed": (lambda: scaled(get_config("b16_128k"), B=4, C=3000, steps=48), 0),
+    "moe_g8": (lambda: scaled(get_config("moe_122k"), B=2, C=2500, steps=40), 0),
+    "ragged_fused": (lambda: scaled(get_config("b16_128k"), B=6, C=1200, steps=40,
+                                    rho=("const", 0.96)), 1),
+    "allhit_short": (lambda: scaled(get_config("b16_128k"), B=3, C=40, steps=30,
+                                    rho=("const", 0.99)), 0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_UNBALANCED_CASES))
+def test_unbalanced_plan_matches_oracle(gpu_lib, case):
+    """MAC_F_UNBALANCED_PLAN (the baseline of Figure 8 (b)): every group gets
+    the same number of waves; spans shorter than that get one wave per page.
+    Same decisions, outputs within tolerance."""
+    import kv_reuse_amd as mac
+    make, fused = _UNBALANCED_CASES[case]
+    w = make()
+    kw = {"prefill": [1200, 1199, 1185, 1024, 777, 17]} if case.startswith("ragged") else {}
+    flags = mac.MAC_F_UNBALANCED_PLAN | (mac.MAC_F_FUSED_AMEND if fused else 0)
+    _run(w, w.steps, flags=flags, **kw)
+
+
 def test_disable_reuse_is_full_attention(gpu_lib):
     import kv_reuse_amd as mac
     import oracle
