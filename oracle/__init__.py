@@ -63,6 +63,7 @@ def _load():
     lib.orc_create.restype = _vp
     lib.orc_destroy.argtypes = [_vp]
     lib.orc_reset.argtypes = [_vp]
+    lib.orc_set_bands.argtypes = [_vp, _i32p]
     lib.orc_ring_entry.argtypes = [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _fp, _dp]
     lib.orc_step.argtypes = [_vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32p, _fp, _i32p,
                              _u8p, _dp, _dp, _u8p, _i32p, _dp, _u8p, _u8p, _i32p, _i64p]
@@ -152,13 +153,19 @@ class Oracle:
     """Per-(request, query head) MAC policy state and the batched decode call."""
 
     def __init__(self, B, Hq, Hkv, d, W, r, tau, theta, scale=None, kv_fp32=False, flags=0):
+        """r: the band, one int for every head or a sequence of Hq per-head
+        bands (Figure 3 (b))."""
         assert Hq % Hkv == 0
-        self.B, self.Hq, self.Hkv, self.d, self.W, self.r = B, Hq, Hkv, d, W, r
+        bands = np.broadcast_to(np.asarray(r, np.int32), (Hq,)).copy()
+        assert (bands >= 1).all()
+        self.B, self.Hq, self.Hkv, self.d, self.W = B, Hq, Hkv, d, W
+        self.r = int(bands[0]) if np.ndim(r) == 0 else bands
         self.tau = float(tau)
         scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
         self._lib = _load()
-        self._h = self._lib.orc_create(B, Hq, Hkv, d, W, r, float(tau), float(theta), scale,
-                                       1 if kv_fp32 else 0, int(flags))
+        self._h = self._lib.orc_create(B, Hq, Hkv, d, W, int(bands.max()), float(tau),
+                                       float(theta), scale, 1 if kv_fp32 else 0, int(flags))
+        self._lib.orc_set_bands(self._h, _ptr(bands, _i32p))
 
     def __del__(self):
         h, self._h = getattr(self, "_h", None), None

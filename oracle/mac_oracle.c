@@ -249,6 +249,7 @@ typedef struct {
     int kv_fp32;
     unsigned flags;
     int64_t calls;    /* decode calls so far; the next insert goes to slot calls % W */
+    int32_t *band;    /* [Hq] band r of each query head (r for all unless set) */
     int32_t *pos;     /* [B][Hq][W] stored positions, -1 = empty */
     float *ring_q;    /* [B][Hq][W][d] pre-RoPE queries */
     double *ring_s;   /* [B][Hq][W][d+2] stored summaries AS_{1:pos-r} */
@@ -263,6 +264,9 @@ orc_ctx *orc_create(int B, int Hq, int Hkv, int d, int W, int r, double tau,
     c->flags = flags;
     size_t nslot = (size_t)B * Hq * W;
     c->pos = (int32_t *)malloc(nslot * sizeof(int32_t));
+    c->band = (int32_t *)malloc((size_t)Hq * sizeof(int32_t));
+    for (int h = 0; h < Hq; h++)
+        c->band[h] = r;
     c->ring_q = (float *)calloc(nslot * d, sizeof(float));
     c->ring_s = (double *)calloc(nslot * (d + 2), sizeof(double));
     for (size_t i = 0; i < nslot; i++)
@@ -276,9 +280,19 @@ void orc_destroy(orc_ctx *c)
     if (!c)
         return;
     free(c->pos);
+    free(c->band);
     free(c->ring_q);
     free(c->ring_s);
     free(c);
+}
+
+/* Per-head bands (Figure 3 (b): the band size r varies by head): query head
+ * h, in every request, uses band[h] >= 1 for its hit span [p - r_h + 1, m]
+ * and for the amend band [m - r_h + 1, m]. */
+void orc_set_bands(orc_ctx *c, const int32_t *band)
+{
+    for (int h = 0; h < c->Hq; h++)
+        c->band[h] = band[h];
 }
 
 /* Empty every ring; the next call misses everywhere. */
@@ -334,7 +348,7 @@ int orc_step(orc_ctx *c, const void *const *k_grp, const void *const *v_grp,
              int32_t *p_out, double *rel, uint8_t *near_tau, uint8_t *near_tie,
              int32_t *start, int64_t *kv_tokens)
 {
-    const int B = c->B, Hq = c->Hq, Hkv = c->Hkv, d = c->d, W = c->W, r = c->r;
+    const int B = c->B, Hq = c->Hq, Hkv = c->Hkv, d = c->d, W = c->W;
     const int G = Hq / Hkv;
     const int slot_new = (int)(c->calls % W);
     const int reuse = !(c->flags & ORC_F_DISABLE_REUSE) && c->tau >= 0.0;
@@ -344,6 +358,7 @@ int orc_step(orc_ctx *c, const void *const *k_grp, const void *const *v_grp,
     #pragma omp parallel for schedule(dynamic, 1) reduction(+ : invalid_total)
     for (int bh = 0; bh < B * Hq; bh++) {
         int b = bh / Hq, h = bh % Hq, g = h / G;
+        const int r = c->band[h];
         int64_t m = (int64_t)seq_lens[b] - 1;
         const float *qt = q_pre + (size_t)bh * d;
         int32_t *pos = c->pos + (size_t)bh * W;

@@ -37,7 +37,8 @@ def _kvf(a):
 
 class SegmentModel:
     def __init__(self, B, Hq, Hkv, d, W, r, tau, theta, flags=0):
-        self.B, self.Hq, self.Hkv, self.d, self.W, self.r = B, Hq, Hkv, d, W, r
+        self.B, self.Hq, self.Hkv, self.d, self.W = B, Hq, Hkv, d, W
+        self.band = [int(x) for x in np.broadcast_to(np.asarray(r), (Hq,))]
         self.tau, self.theta, self.flags = tau, theta, flags
         self.scale = 1.0 / math.sqrt(d)
         self.ring = [[[None] * W for _ in range(Hq)] for _ in range(B)]
@@ -58,7 +59,7 @@ class SegmentModel:
         return softmax(np.concatenate(logits)) @ np.concatenate(rows)
 
     def step(self, Kg, Vg, seq_lens, q_pre, override=None):
-        B, Hq, W, r = self.B, self.Hq, self.W, self.r
+        B, Hq, W = self.B, self.Hq, self.W
         G = Hq // self.Hkv
         slot_new = self.calls % W
         reuse = not (self.flags & oracle.F_DISABLE_REUSE) and self.tau >= 0
@@ -70,6 +71,7 @@ class SegmentModel:
             if m < 0:
                 continue
             for h in range(Hq):
+                r = self.band[h]
                 qt = q_pre[b, h]
                 ring = self.ring[b][h]
                 slot = -1
@@ -161,6 +163,33 @@ def test_policy_matches_segment_model(kv, tau, W, r, flags):
         assert nhit == want
     elif tau > 0:
         assert 0 < nhit < w.steps * w.B * w.Hq      # the case mixes hits and misses
+
+
+@pytest.mark.parametrize("kv,bands,W,flags", [("fp32", [1, 3, 6, 2], 4, 0),
+                                              ("bf16", [5, 5, 2, 9], 3, 0),
+                                              ("fp32", [2, 7, 1, 4], 4, _STALE)])
+def test_per_head_bands_match_segment_model(kv, bands, W, flags):
+    """Per-head band r_h (Figure 3 (b)): each head's hit span and amend band
+    use its own r_h, including heads of one KV group with different bands."""
+    w, Kg, Vg, qs = _setup(kv=kv, W=W, r=max(bands), rho=0.95)
+    theta = 10000.0
+    orc = oracle.Oracle(w.B, w.Hq, w.Hkv, w.d, W, bands, 0.5, theta, kv_fp32=(kv == "fp32"),
+                        flags=flags)
+    mod = SegmentModel(w.B, w.Hq, w.Hkv, w.d, W, bands, 0.5, theta, flags=flags)
+    KgF = [_kvf(a) for a in Kg]
+    VgF = [_kvf(a) for a in Vg]
+    nhit = 0
+    for t in range(w.steps):
+        seq = np.full(w.B, w.C + t + 1, np.int32)
+        res = orc.step(Kg, Vg, seq, qs[t])
+        out, hit, p = mod.step(KgF, VgF, seq, qs[t])
+        assert np.array_equal(res["hit"], hit), t
+        assert np.array_equal(res["p"], p), t
+        np.testing.assert_allclose(res["out"], out, rtol=1e-10, atol=1e-12)
+        starts = np.where(hit != 0, np.maximum(p - np.asarray(bands)[None, :] + 1, 0), 0)
+        assert np.array_equal(res["start"], starts), t
+        nhit += int(hit.sum())
+    assert 0 < nhit < w.steps * w.B * w.Hq
 
 
 def test_tau_zero_hits_only_exact_repeats():
