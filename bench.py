@@ -76,13 +76,15 @@ def parse():
                     help="MAC passes with MAC_F_RING_BF16 (ring queries kept as bfloat16)")
     ap.add_argument("--stale-ring", action="store_true",
                     help="MAC passes with MAC_F_STALE_RING (match skips the previous call's entry)")
+    ap.add_argument("--band-per-head", default="",
+                    help="comma list of bands r_h, cycled over the query heads of the MAC passes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 2 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
 
 
 class Bench:
-    def __init__(self, w, flags, K, V, paged, table):
+    def __init__(self, w, flags, K, V, paged, table, bands=None):
         import torch
         import kv_reuse_amd as mac
         self.w = w
@@ -96,7 +98,7 @@ class Bench:
             batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, ring_size=w.W, band=w.r, tau=w.tau,
             rope_theta=w.theta, layout=mac.MAC_KV_PAGED if paged else mac.MAC_KV_CONTIGUOUS,
             kv_dtype=mac.MAC_FP32 if w.kv == "fp32" else mac.MAC_BF16, max_seq_len=w.n_cap,
-            flags=flags)
+            flags=flags, band_per_head=bands)
         self.stream = torch.cuda.current_stream()
         self.layer = mac.MacLayer(self.cfg, main_stream=self.stream)
         self.view = mac.make_kv_view(self.kc, self.vc, self.seq, self.table,
@@ -536,7 +538,11 @@ def main():
     mac_flags = ((mac.MAC_F_FUSED_AMEND if args.fused_amend else 0) |
                  (mac.MAC_F_RING_BF16 if args.ring_bf16 else 0) |
                  (mac.MAC_F_STALE_RING if args.stale_ring else 0))
-    bench = Bench(w, mac_flags, kc, vc, paged, table)
+    bands = None
+    if args.band_per_head:
+        cyc = [int(x) for x in args.band_per_head.split(",")]
+        bands = [cyc[h % len(cyc)] for h in range(w.Hq)]
+    bench = Bench(w, mac_flags, kc, vc, paged, table, bands)
     for t in range(args.warmup):
         bench.step(t, q_dev[t], k_rows[t], v_rows[t])
     st0 = bench.layer.stats()
@@ -557,7 +563,7 @@ def main():
 
     # pass 2: the same steps from a fresh ring (same decisions, same bytes)
     # with the library's HIP events around every kernel (MAC_F_TIMING)
-    kb = Bench(w, mac_flags | mac.MAC_F_TIMING, kc, vc, paged, table)
+    kb = Bench(w, mac_flags | mac.MAC_F_TIMING, kc, vc, paged, table, bands)
     comp, match, red, amend, att_ev, toks2 = [], [], [], [], [], []
     prev = None
     for t in range(total):
@@ -605,7 +611,8 @@ def main():
     # the reuse path's own speedup at this context: the same cache, queries
     # with rho = 0.97 (nearly every head hits its previous step)
     allhit = loops = None
-    if not args.no_baseline_kernel and args.config == "b16_128k" and not args.set and not args.r:
+    if (not args.no_baseline_kernel and args.config == "b16_128k" and not args.set and not args.r
+            and not args.band_per_head):
         wa = scaled(w, rho=("const", 0.97))
         qa = torch.as_tensor(queries(wa, steps=total), device="cuda")
         ab = Bench(wa, mac_flags, kc, vc, paged, table)
@@ -671,14 +678,28 @@ def main():
                          "empty ring, scaled by %d/%d to the batch" % (n_req, w.B, w.Hq, n_steps,
                                                                        w.B, n_req)}
 
-    if args.copy_calibration:
-        n = 1 << 30
-        a = torch.empty(n, dtype=torch.int16, device="cuda")
-        b = torch.empty_like(a)
-        a.fill_(1)
-        for _ in range(3):
-            b.copy_(a)
+    # measured HBM rates beside the published peak: a plain device copy of
+    # 2 GiB (2 GiB read + 2 GiB written) and a read-only reduction over 2 GiB
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.int16, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(2 if args.copy_calibration else 1):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    hbm_measured = {}
+    for name, fn, nbytes in (("copy_gbps", lambda: b.copy_(a), 4 * n),
+                             ("read_gbps", lambda: a.max(), 2 * n)):
+        fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            fn()
+        e1.record()
         torch.cuda.synchronize()
+        hbm_measured[name] = nbytes * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
 
     line = {
         "metric": "attention-phase µs/decode step + HBM GB/s at 128K ctx, batch 16, GQA 32q/8kv",
@@ -698,7 +719,8 @@ def main():
                    "ring": w.W, "band": w.r, "tau": w.tau, "rho": list(w.rho),
                    "amend": ("fused" if args.fused_amend else
                              "async, stale-by-one ring" if args.stale_ring else "async"),
-                   "ring_queries": "bf16" if args.ring_bf16 else "fp32"},
+                   "ring_queries": "bf16" if args.ring_bf16 else "fp32",
+                   "band_per_head": bands},
         "hbm_gbps": float(np.mean(kv_bytes)) / (att_us * 1e-6) / 1e9,
         "tokens_per_s": w.B / (att_us * 1e-6),
         "kv_bytes_per_step": float(np.mean(kv_bytes)),
@@ -706,6 +728,7 @@ def main():
         "kernel_us": {"match": float(np.mean(match)), "complete": comp_us,
                       "reduce": float(np.mean(red)), "amend": float(np.mean(amend)),
                       "attention_with_kernel_events": float(np.mean(att_ev))},
+        "hbm_measured": hbm_measured,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(w.name),
                      "kernel": "complete_mfma_kernel" if w.kv == "bf16" else "complete_kernel",

@@ -108,6 +108,14 @@ typedef struct {
     int32_t page_size;      /* tokens per page (16) */
     int32_t max_seq_len;    /* token capacity per request (multiple of page_size) */
     uint32_t flags;         /* MAC_F_* */
+    /* NULL, or host array [num_q_heads] of per-head bands r_h >= 1 (Figure
+     * 3 (b): the band size varies by head); query head h of every request
+     * then uses r_h for its hit span [p - r_h + 1, m] and its amend band, and
+     * `band` is ignored.  Read by mac_init, mac_config_validate and
+     * mac_aux_bytes only (copied; the caller may free it afterwards).  With
+     * MAC_F_FUSED_AMEND the heads of one KV group must share a band
+     * (MAC_EUNSUPPORTED otherwise). */
+    const int32_t *band_per_head;
 } mac_config;
 
 /* Borrowed view of one layer's KV cache (host struct; pointed-to memory is

@@ -44,7 +44,8 @@ class MacConfig(ctypes.Structure):
                 ("tau", ctypes.c_float), ("rope_theta", ctypes.c_float),
                 ("sm_scale", ctypes.c_float), ("layout", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("page_size", ctypes.c_int32),
-                ("max_seq_len", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("max_seq_len", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("band_per_head", ctypes.c_void_p)]
 
 
 class MacKvView(ctypes.Structure):
@@ -128,9 +129,18 @@ def _stream(s):
 
 def make_config(batch, num_q_heads, num_kv_heads, head_dim=128, ring_size=32, band=256, tau=0.3,
                 rope_theta=500000.0, sm_scale=0.0, layout=MAC_KV_CONTIGUOUS, kv_dtype=MAC_BF16,
-                page_size=16, max_seq_len=0, flags=0):
-    return MacConfig(batch, num_q_heads, num_kv_heads, head_dim, ring_size, band, tau, rope_theta,
-                     sm_scale, layout, kv_dtype, page_size, max_seq_len, flags)
+                page_size=16, max_seq_len=0, flags=0, band_per_head=None):
+    """band_per_head: None or a sequence of num_q_heads per-head bands (the
+    config keeps the int32 array alive; the library copies it at init)."""
+    cfg = MacConfig(batch, num_q_heads, num_kv_heads, head_dim, ring_size, band, tau, rope_theta,
+                    sm_scale, layout, kv_dtype, page_size, max_seq_len, flags, None)
+    if band_per_head is not None:
+        arr = (ctypes.c_int32 * num_q_heads)(*[int(x) for x in band_per_head])
+        if len(band_per_head) != num_q_heads:
+            raise ValueError("band_per_head needs num_q_heads entries")
+        cfg._bands = arr
+        cfg.band_per_head = ctypes.cast(arr, ctypes.c_void_p)
+    return cfg
 
 
 def make_kv_view(k, v, seq_lens, page_table=None, num_pages=0):

@@ -28,13 +28,19 @@ __global__ __launch_bounds__(64 * amend_waves<G>()) void amend_kernel(Shape s, S
     const int m = st.m_buf[b];
     if (m < 0)
         return;
-    const bool has_prefix = m - s.r >= 0;
-    if (has_prefix) {
-        const int lo = m - s.r + 1;
-        int hs[G];
+    // head h removes its own band [m - r_h + 1, m] (nothing when m - r_h < 0:
+    // its stored summary is EMPTY); the waves walk the union of the bands
+    int hs[G];
+    int lo = m + 1, hmax = 0;
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-            hs[h] = lo;
+    for (int h = 0; h < G; ++h) {
+        const int rh = st.band[kvh * G + h];
+        hs[h] = m - rh >= 0 ? m - rh + 1 : m + 1;
+        lo = min(lo, hs[h]);
+        hmax = max(hmax, hs[h]);
+    }
+    const bool has_prefix = lo <= m;   // some head keeps a prefix
+    if (has_prefix) {
         float q[G][K::E];
         load_group_queries<T, G>(s, st, b, kvh, q);
         WaveAcc<G, K::E> acc;
@@ -44,7 +50,7 @@ __global__ __launch_bounds__(64 * amend_waves<G>()) void amend_kernel(Shape s, S
             load_page<T>(r, kv_page<T>(kv, kv.k, b, kvh, s.Hkv, page, &st.stats[ST_BAD_INPUT]),
                          kv_page<T>(kv, kv.v, b, kvh, s.Hkv, page, &st.stats[ST_BAD_INPUT]));
             const int tok0 = page * PAGE;
-            compute_page<T, G>(r, tok0, m, hs, tok0 < lo || tok0 + PAGE - 1 > m, q, acc);
+            compute_page<T, G>(r, tok0, m, hs, tok0 < hmax || tok0 + PAGE - 1 > m, q, acc);
         }
         store_wave_summary<T, G>(acc, &red[wv][0][0]);
     }
@@ -52,7 +58,7 @@ __global__ __launch_bounds__(64 * amend_waves<G>()) void amend_kernel(Shape s, S
     for (int hh = wv; hh < G; hh += AMEND_WAVES) {
         const long idx = (long)b * s.Hq + kvh * G + hh;
         float so0 = 0.f, so1 = 0.f, sM = NEG_INF, sL = 0.f;   // EMPTY
-        if (has_prefix) {
+        if (m - st.band[kvh * G + hh] >= 0) {
             float Mx = NEG_INF;
 #pragma unroll
             for (int w = 0; w < AMEND_WAVES; ++w)
@@ -97,7 +103,7 @@ __global__ __launch_bounds__(64 * amend_waves<G>()) void amend_kernel(Shape s, S
             st.ring_pos[(long)b * s.W + slot_new] = m;
         if (has_prefix)   // this block owns the group's amend counter
             st.grp_stats[((long)b * s.Hkv + kvh) * GRP_NSTAT + GS_TOK_AMEND] +=
-                (unsigned long long)s.r;
+                (unsigned long long)(m - lo + 1);
     }
 }
 

@@ -425,7 +425,8 @@ __device__ __forceinline__ Seg segment(const Shape &s, const State &st, int seg)
         r.lo = gs;
         r.hi = r.m;
     } else {
-        const int cut = max(gs, r.m - s.r + 1);   // first key of the band part
+        // first key of the band part (the group's heads share one band)
+        const int cut = max(gs, r.m - st.band[r.kvh * s.G] + 1);
         r.lo = part == 0 ? gs : cut;
         r.hi = part == 0 ? cut - 1 : r.m;
     }

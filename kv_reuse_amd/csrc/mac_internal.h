@@ -18,6 +18,7 @@
 //   tile_best  [B][Hq][W/64][3]     W > 64: nearest entry of each 64-slot tile
 //   partials   [NW + B*Hkv*nseg][G][SUMM] per-(worker, segment) unnormalised summaries
 //   as_full    [B][Hq][SUMM]        AS_{1:m} of this step, input of amend
+//   band       [Hq]    int32        band r_h of each query head
 //   stats      [MAC_NSTAT] + [B*Hq][HEAD_NSTAT] + [B*Hkv][GRP_NSTAT] uint64 counters
 // With the stale-by-one ring (MAC_F_STALE_RING) q_copy, q_rot, m_buf and
 // as_full are held twice and calls alternate between the copies, so that the
@@ -70,7 +71,7 @@ struct KvView {
 };
 
 struct Shape {
-    int32_t B, Hq, Hkv, G, W, r;
+    int32_t B, Hq, Hkv, G, W;
     float tau, scale_log2;  // scale_log2 = sm_scale * log2(e)
     int32_t reuse;          // 0: every head misses
     int32_t nseg;           // work-list segments per group: 1, or 2 when amend is fused
@@ -87,6 +88,7 @@ struct State {
     unsigned long long *head_stats;   // [B*Hq][HEAD_NSTAT]
     unsigned long long *grp_stats;    // [B*Hkv][GRP_NSTAT]
     const double *inv_freq;   // [D/2] theta^(-2i/D), fp64
+    const int32_t *band;      // [Hq] band r_h of each query head
     float *tile_best;         // W > TILE_W: [B*Hq][ceil(W/TILE_W)][3] per-tile nearest (D, pos, slot)
     int32_t n_workers;        // waves in the complete grid
 };

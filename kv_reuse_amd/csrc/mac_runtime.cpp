@@ -67,12 +67,12 @@ mac_status fail_hip(mac_handle h, const char *what, hipError_t e)
 
 struct Sizes {
     size_t ring_q, ring_s, ring_pos, qvec, m_buf, dec_i, dec_f, grp_parts, partials, as_full,
-        stats, inv_freq, tiles;
+        stats, inv_freq, band, tiles;
     size_t step_copies;   // copies of the buffers amend reads: 2 with the stale-by-one ring
     size_t total() const
     {
         return ring_q + ring_s + ring_pos + step_copies * (2 * qvec + m_buf + as_full) +
-               3 * dec_i + dec_f + grp_parts + partials + stats + inv_freq + tiles;
+               3 * dec_i + dec_f + grp_parts + partials + stats + inv_freq + band + tiles;
     }
 };
 
@@ -103,6 +103,7 @@ Sizes sizes_for(const mac_config &c, int n_workers)
     s.stats = round256(mac::stats_count((long)(B * Hq), (long)(B * Hkv)) *
                        sizeof(unsigned long long));
     s.inv_freq = round256(mac::D / 2 * sizeof(double));
+    s.band = round256(Hq * sizeof(int32_t));
     const size_t ntiles = (W + mac::TILE_W - 1) / mac::TILE_W;
     s.tiles = W > (size_t)mac::TILE_W ? round256(B * Hq * ntiles * 3 * sizeof(float)) : 0;
     s.step_copies = (c.flags & MAC_F_STALE_RING) ? 2 : 1;
@@ -135,7 +136,7 @@ mac_status validate(const mac_config *c, std::string &why)
         why = "ring_size must be in [1, 2048]";
         return MAC_EINVAL;
     }
-    if (c->band < 1) {
+    if (!c->band_per_head && c->band < 1) {
         why = "band must be >= 1";
         return MAC_EINVAL;
     }
@@ -181,6 +182,19 @@ mac_status validate(const mac_config *c, std::string &why)
     if ((c->flags & MAC_F_STALE_RING) && (c->flags & MAC_F_FUSED_AMEND)) {
         why = "MAC_F_STALE_RING needs the separate amend; it excludes MAC_F_FUSED_AMEND";
         return MAC_EINVAL;
+    }
+    if (c->band_per_head) {
+        const int G = c->num_q_heads / c->num_kv_heads;
+        for (int h = 0; h < c->num_q_heads; ++h) {
+            if (c->band_per_head[h] < 1) {
+                why = "every entry of band_per_head must be >= 1";
+                return MAC_EINVAL;
+            }
+            if ((c->flags & MAC_F_FUSED_AMEND) && c->band_per_head[h] != c->band_per_head[h / G * G]) {
+                why = "MAC_F_FUSED_AMEND needs one band per KV group";
+                return MAC_EUNSUPPORTED;
+            }
+        }
     }
     return MAC_OK;
 }
@@ -350,6 +364,7 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     h->st.head_stats = h->st.stats + mac::MAC_NSTAT;
     h->st.grp_stats = h->st.head_stats + (long)cfg->batch * cfg->num_q_heads * mac::HEAD_NSTAT;
     h->st.inv_freq = (const double *)take(sz.inv_freq);
+    h->st.band = (const int32_t *)take(sz.band);
     h->st.tile_best = sz.tiles ? (float *)take(sz.tiles) : nullptr;
     h->st_odd = h->st;
     if (sz.step_copies == 2) {
@@ -368,13 +383,20 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     e = hipMemcpy((void *)h->st.inv_freq, inv, sizeof inv, hipMemcpyHostToDevice);
     if (e != hipSuccess)
         return bail(MAC_EHIP, std::string("hipMemcpy: ") + hipGetErrorString(e));
+    std::vector<int32_t> bands(cfg->num_q_heads, cfg->band);
+    if (cfg->band_per_head)
+        bands.assign(cfg->band_per_head, cfg->band_per_head + cfg->num_q_heads);
+    h->cfg.band_per_head = nullptr;   // borrowed for this call only
+    e = hipMemcpy((void *)h->st.band, bands.data(), bands.size() * sizeof(int32_t),
+                  hipMemcpyHostToDevice);
+    if (e != hipSuccess)
+        return bail(MAC_EHIP, std::string("hipMemcpy: ") + hipGetErrorString(e));
 
     h->shape.B = cfg->batch;
     h->shape.Hq = cfg->num_q_heads;
     h->shape.Hkv = cfg->num_kv_heads;
     h->shape.G = G;
     h->shape.W = cfg->ring_size;
-    h->shape.r = cfg->band;
     h->shape.tau = cfg->tau;
     const double scale = cfg->sm_scale > 0.f ? (double)cfg->sm_scale : 1.0 / std::sqrt((double)mac::D);
     h->shape.scale_log2 = (float)(scale * 1.4426950408889634);

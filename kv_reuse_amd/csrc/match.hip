@@ -219,6 +219,7 @@ __global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
     const float qa = q_pre[idx * D + lane], qb = q_pre[idx * D + lane + 64];
     const double inv = st.inv_freq[lane];
     const int ov = ovr ? ovr[idx] : -2;
+    const int band = st.band[h];
     const int pos_l =
         (s.reuse && lane < s.W && lane != hidden) ? st.ring_pos[(long)b * s.W + lane] : -1;
     unsigned long long old[HEAD_NSTAT] = {};
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
             }
         }
         if (slot >= 0)
-            start = max(p - s.r + 1, 0);
+            start = max(p - band + 1, 0);
     }
     if (lane == 0) {
         st.dec_slot[idx] = slot;

@@ -26,7 +26,8 @@ def _kv_nan(dtype):
 
 class Lockstep:
     def __init__(self, w, flags=0, track=None, device="cuda", oracle_flags=0, tau=None, r=None,
-                 W=None, sync_amend=False, layer=0, amend_stream=None, prefill=None):
+                 W=None, sync_amend=False, layer=0, amend_stream=None, prefill=None,
+                 bands=None):
         self.w = w
         # per-request prefill length (ragged batches); request b decodes
         # position prefill[b] + t at step t
@@ -35,6 +36,8 @@ class Lockstep:
         assert self.prefill.shape == (w.B,) and self.prefill.max() <= w.C
         self.tau = w.tau if tau is None else tau
         self.r = w.r if r is None else r
+        # per-head bands: the config's band_per_head and the oracle's r_h
+        self.bands = None if bands is None else [int(x) for x in bands]
         self.W = w.W if W is None else W
         self.dev = device
         B, Hkv, d = w.B, w.Hkv, w.d
@@ -78,11 +81,12 @@ class Lockstep:
             band=self.r, tau=self.tau, rope_theta=w.theta,
             layout=mac.MAC_KV_PAGED if self.paged else mac.MAC_KV_CONTIGUOUS,
             kv_dtype=mac.MAC_FP32 if w.kv == "fp32" else mac.MAC_BF16,
-            max_seq_len=w.n_cap, flags=fl)
+            max_seq_len=w.n_cap, flags=fl, band_per_head=self.bands)
         self.layer = mac.MacLayer(self.cfg, amend_stream=amend_stream)
         self.view = mac.make_kv_view(self.kc, self.vc, self.seq, self.table,
                                      num_pages=self.kc.shape[0] if self.paged else 0)
-        self.orc = oracle.Oracle(B, w.Hq, Hkv, d, self.W, self.r, self.tau, w.theta,
+        self.orc = oracle.Oracle(B, w.Hq, Hkv, d, self.W,
+                                 self.r if self.bands is None else self.bands, self.tau, w.theta,
                                  kv_fp32=(w.kv == "fp32"), flags=oracle_flags)
         self.out = torch.empty((B, w.Hq, d), dtype=torch.float32, device=device)
         self.stats = []

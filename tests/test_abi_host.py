@@ -40,6 +40,10 @@ def test_valid_config_passes():
                                  num_q_heads=32, num_kv_heads=4, tau=-1.0))
     mac.mac_config_validate(_cfg(ring_size=2048))     # the pages' largest window (Table 7)
     mac.mac_config_validate(_cfg(flags=mac.MAC_F_STALE_RING | mac.MAC_F_RING_BF16))
+    # per-head bands; with fused amend one band per KV group (4 heads here)
+    mac.mac_config_validate(_cfg(band=0, band_per_head=[1, 2, 3, 4, 5, 6, 7, 8]))
+    mac.mac_config_validate(_cfg(band_per_head=[9, 9, 9, 9, 2, 2, 2, 2],
+                                 flags=mac.MAC_F_FUSED_AMEND))
 
 
 def test_stale_ring_doubles_only_the_step_buffers():
@@ -73,6 +77,9 @@ def test_stale_ring_doubles_only_the_step_buffers():
     (dict(batch=1024, num_q_heads=8, num_kv_heads=8), mac.MAC_EUNSUPPORTED),
     (dict(flags=1 << 9), mac.MAC_EINVAL),
     (dict(flags=mac.MAC_F_STALE_RING | mac.MAC_F_FUSED_AMEND), mac.MAC_EINVAL),
+    (dict(band_per_head=[64, 64, 0, 64, 64, 64, 64, 64]), mac.MAC_EINVAL),
+    (dict(band_per_head=[64, 32, 64, 64, 64, 64, 64, 64], flags=mac.MAC_F_FUSED_AMEND),
+     mac.MAC_EUNSUPPORTED),
 ])
 def test_invalid_configs_rejected(kw, status):
     with pytest.raises(mac.MacError) as ei:

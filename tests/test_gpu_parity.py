@@ -223,6 +223,44 @@ def test_unbalanced_plan_matches_oracle(gpu_lib, case):
     _run(w, w.steps, flags=flags, **kw)
 
 
+def _bands(Hq, choices):
+    return [choices[h % len(choices)] for h in range(Hq)]
+
+
+_BAND_CASES = {
+    # bands differ inside every KV group
+    "paged_mixed": (lambda: scaled(get_config("b16_128k"), B=4, C=3000, steps=48),
+                    (64, 256, 1024, 16), 0),
+    "moe_g8": (lambda: scaled(get_config("moe_122k"), B=2, C=2500, steps=40),
+               (64, 256, 1024, 1, 700, 33, 256, 2048), 0),
+    "cpu4k_fp32": (lambda: scaled(get_config("cpu4k"), steps=80), (8, 64, 300, 1), 0),
+    # short prefill: heads cross m - r_h >= 0 at different steps
+    "shorter_than_band": (lambda: scaled(get_config("b16_128k"), B=2, C=3, steps=100, W=16,
+                                         rho=("const", 0.96)), (4, 16, 64, 90), 0),
+    "stale_ring": (lambda: scaled(get_config("b16_128k"), B=2, C=600, steps=50,
+                                  rho=("const", 0.985)), (16, 128, 512, 5), 1),
+    # fused amend: one band per KV group
+    "fused_per_group": (lambda: scaled(get_config("b16_128k"), B=4, C=3000, steps=48),
+                        (64, 64, 64, 64, 256, 256, 256, 256, 1024, 1024, 1024, 1024,
+                         16, 16, 16, 16), 2),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_BAND_CASES))
+def test_per_head_bands_match_oracle(gpu_lib, case):
+    """Per-head band r_h (band_per_head, Figure 3 (b)) against the oracle with
+    the same bands: spans, amend bands and fused cuts follow each head's r_h."""
+    import kv_reuse_amd as mac
+    import oracle
+    make, choices, mode = _BAND_CASES[case]
+    w = make()
+    bands = _bands(w.Hq, choices)
+    flags = {0: 0, 1: mac.MAC_F_STALE_RING, 2: mac.MAC_F_FUSED_AMEND}[mode]
+    oflags = oracle.F_STALE_RING if mode == 1 else 0
+    hits, _ = _run(w, w.steps, flags=flags, oracle_flags=oflags, bands=bands)
+    assert hits > 0
+
+
 def test_disable_reuse_is_full_attention(gpu_lib):
     import kv_reuse_amd as mac
     import oracle
