@@ -76,6 +76,9 @@ def parse():
                     help="MAC passes with MAC_F_RING_BF16 (ring queries kept as bfloat16)")
     ap.add_argument("--stale-ring", action="store_true",
                     help="MAC passes with MAC_F_STALE_RING (match skips the previous call's entry)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="Table 8 analog: MAC over a prompt (mac_prefill, unbounded window) vs "
+                         "the same engine with reuse off (one JSON line)")
     ap.add_argument("--band-per-head", default="",
                     help="comma list of bands r_h, cycled over the query heads of the MAC passes")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -459,6 +462,63 @@ def figures(args):
           flush=True)
 
 
+def prefill_table8(args):
+    """MAC-Attention in prefill (mac_prefill; window unbounded over the prompt)
+    on a 4096-token prompt, batch 4, 32q/8kv paged bf16, AR(1) queries at rho
+    0.97: hit and skipped-key rates and time per call at the (tau, r) pairs of
+    the pages' Table 8, against the same engine with reuse off (plain causal
+    attention).  Time: HIP events around the call, median of 5 after 1."""
+    import torch
+    import kv_reuse_amd as mac
+    from workloads import get_config, kv_logical, page_table, queries, scaled, to_paged
+    N = 4096
+    w = scaled(get_config("b16_128k"), B=4, C=0, steps=N, rho=("const", 0.97))
+    K, V = kv_logical(w, "cuda")
+    tab = page_table(w)
+    kc, vc, table = to_paged(K, tab), to_paged(V, tab), torch.as_tensor(tab, device="cuda")
+    del K, V
+    qd = torch.as_tensor(np.ascontiguousarray(queries(w, steps=N).transpose(1, 0, 2, 3)),
+                         device="cuda")
+    seq = torch.full((w.B,), N, dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, N, w.Hq, w.d), device="cuda")
+    view = mac.make_kv_view(kc, vc, seq, table, num_pages=kc.shape[0])
+    causal_keys = w.B * w.Hkv * N * (N + 1) // 2
+
+    def run(tau, r, flags):
+        cfg = mac.make_config(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, ring_size=w.W,
+                              band=r, tau=tau, rope_theta=w.theta, layout=mac.MAC_KV_PAGED,
+                              kv_dtype=mac.MAC_BF16, max_seq_len=w.n_cap, flags=flags)
+        layer = mac.MacLayer(cfg)
+        ms = []
+        for it in range(6):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            layer.prefill(view, N, qd, out)
+            e1.record()
+            torch.cuda.synchronize()
+            if it:
+                ms.append(e0.elapsed_time(e1))
+        st = layer.stats()
+        layer.close()
+        calls = 6
+        return {"ms": float(np.median(ms)),
+                "hit_rate": st["prefill_hits"] / st["prefill_decisions"],
+                "skipped_keys": 1.0 - st["prefill_kv_tokens"] / (calls * causal_keys)}
+
+    base = run(0.3, 256, mac.MAC_F_DISABLE_REUSE)
+    rows = []
+    for tau, r in ((0.30, 512), (0.35, 512), (0.45, 128), (0.45, 256)):
+        x = run(tau, r, 0)
+        x.update({"tau": tau, "r": r, "speedup_vs_causal": base["ms"] / x["ms"]})
+        rows.append(x)
+    print(json.dumps({"prefill_table8": rows, "causal_ms": base["ms"],
+                      "config": {"workload": "prefill_4k", "batch": w.B, "prompt": N,
+                                 "q_heads": w.Hq, "kv_heads": w.Hkv, "kv_layout": "paged",
+                                 "rho": 0.97, "window": "unbounded (whole prompt)",
+                                 "data": "synthetic"}}), flush=True)
+
+
 def oracle_baseline(w, K, V, qs, n_req, n_steps):
     """fp64 oracle, as it stands, on the first n_req requests for n_steps steps."""
     import oracle
@@ -491,6 +551,9 @@ def main():
     torch.cuda.set_device(0)
     if args.config == "contgen":
         contgen(args)
+        return
+    if args.prefill:
+        prefill_table8(args)
         return
     if args.figures:
         figures(args)

@@ -153,6 +153,11 @@ typedef struct {
     float last_us_reduce;        /* combine of the partial summaries + merge with the stored one */
     float last_us_amend;
     float last_us_attention;     /* match + complete + reduce, one event pair */
+    uint64_t prefill_tokens;     /* prompt tokens taken by mac_prefill */
+    uint64_t prefill_decisions;  /* their (token, query head) decisions */
+    uint64_t prefill_hits;
+    uint64_t prefill_kv_tokens;  /* keys attended, per KV group and prompt token */
+    uint64_t prefill_override_invalid;
 } mac_stats_t;
 
 /* Check a configuration without touching the GPU (host only). */
@@ -201,6 +206,30 @@ mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv /* host */, const v
 mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv /* host */,
                            const float *q_pre_rope, float *out, const int32_t *override_pos,
                            void *stream);
+
+/* MAC-Attention over the prompt, the pages' Table 8 ablation (reuse in
+ * prefill as well as decode, window unbounded).  Request b's prompt tokens
+ * t = 0 .. seq_lens[b]-1, whose post-RoPE keys and values are already in the
+ * cache, are taken as decode steps in order: token t matches the pre-RoPE
+ * queries of every earlier prompt token of its (request, query head), with
+ * the handle's tau, bands and scale, and on a hit at p attends only
+ * [p - r_h + 1, t] merged with the summary token p stored.  The decode rings
+ * are neither read nor written, and ring_size does not apply.
+ *   q_pre:        [B][num_tokens][Hq][d] fp32 pre-RoPE queries (16-byte aligned)
+ *   out:          [B][num_tokens][Hq][d] fp32 outputs; rows t >= seq_lens[b] get zeros
+ *   override_pos: NULL or [B][num_tokens][Hq] int32 (-2 none, -1 miss, p >= 0 hit
+ *                 on earlier token p; p >= t is a counted miss)
+ *   p_out:        NULL or [B][num_tokens][Hq] int32 device: matched position or -1
+ * 1 <= num_tokens <= 32768; a seq_lens[b] beyond num_tokens or the cache idles
+ * request b (counted in bad_input).  Honours MAC_F_DISABLE_REUSE (plain
+ * causal attention) and MAC_F_RING_BF16 (earlier queries rounded to bf16
+ * for the match); the other flags do not apply.  Enqueued on `stream` (NULL:
+ * the main stream); its scratch (~(d + 2.6 (d + 4)) * 4 bytes per (token,
+ * head)) is allocated and released stream-ordered on that stream (MAC_ENOMEM
+ * if that fails).  Counters: mac_stats' prefill_* fields. */
+mac_status mac_prefill(mac_handle h, const mac_kv_view *kv /* host */, int32_t num_tokens,
+                       const float *q_pre, float *out, const int32_t *override_pos,
+                       int32_t *p_out, void *stream);
 
 /* Synchronise the handle's streams and copy the counters (host). */
 mac_status mac_stats(mac_handle h, mac_stats_t *out /* host */);

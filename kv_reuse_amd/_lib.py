@@ -24,7 +24,7 @@ MAC_F_UNBALANCED_PLAN = 128
 
 EXPORTS = ["mac_config_validate", "mac_aux_bytes", "mac_init", "mac_destroy", "mac_reset",
            "mac_append_kv", "mac_decode_step", "mac_stats", "mac_debug_last", "mac_last_error",
-           "mac_status_string"]
+           "mac_status_string", "mac_prefill"]
 
 
 class MacError(RuntimeError):
@@ -61,7 +61,10 @@ class MacStats(ctypes.Structure):
                  "kv_bytes_amend", "aux_bytes", "bad_input")] + \
                [(n, ctypes.c_float) for n in
                 ("last_us_match", "last_us_complete", "last_us_reduce", "last_us_amend",
-                 "last_us_attention")]
+                 "last_us_attention")] + \
+               [(n, ctypes.c_uint64) for n in
+                ("prefill_tokens", "prefill_decisions", "prefill_hits", "prefill_kv_tokens",
+                 "prefill_override_invalid")]
 
 
 _lib = None
@@ -92,6 +95,8 @@ def load():
     lib.mac_decode_step.restype = st
     lib.mac_stats.argtypes = [vp, ctypes.POINTER(MacStats)]
     lib.mac_stats.restype = st
+    lib.mac_prefill.argtypes = [vp, ctypes.POINTER(MacKvView), i32, vp, vp, vp, vp, vp]
+    lib.mac_prefill.restype = st
     lib.mac_debug_last.argtypes = [vp, vp, vp, vp]
     lib.mac_debug_last.restype = st
     lib.mac_last_error.argtypes = [vp]
@@ -182,6 +187,11 @@ def mac_append_kv(h, kv, k_new, v_new, positions, stream=None):
 def mac_decode_step(h, kv, q_pre_rope, out, override_pos=None, stream=None):
     _check(load().mac_decode_step(h, ctypes.byref(kv), _ptr(q_pre_rope), _ptr(out),
                                   _ptr(override_pos), _stream(stream)), h)
+
+
+def mac_prefill(h, kv, num_tokens, q_pre, out, override_pos=None, p_out=None, stream=None):
+    _check(load().mac_prefill(h, ctypes.byref(kv), int(num_tokens), _ptr(q_pre), _ptr(out),
+                              _ptr(override_pos), _ptr(p_out), _stream(stream)), h)
 
 
 def mac_stats(h):

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmac.so")
-SOURCES = ["match.hip", "complete.hip", "reduce.hip", "amend.hip", "mac_runtime.cpp"]
+SOURCES = ["match.hip", "complete.hip", "reduce.hip", "amend.hip", "prefill.hip", "mac_runtime.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

@@ -119,6 +119,23 @@ __device__ __forceinline__ void to_f32(const uint4 &w, float (&f)[4])
     f[3] = __uint_as_float(w.w);
 }
 
+// Rotate-half RoPE of the column pair (i, i + D/2) at position m, with
+// inv = theta^(-2i/D): the angle m * inv is formed in fp64 and reduced to
+// [-pi, pi] in fp64 (Cody-Waite, 2*pi split in two doubles, fma), so sincos
+// stays on its short-argument path.
+__device__ __forceinline__ void rope_pair(float qa, float qb, int m, double inv, float &ra,
+                                          float &rb)
+{
+    const double phi = (double)m * inv;
+    const double k = rint(phi * 0.15915494309189535);   // 1 / (2*pi)
+    double red = fma(-k, 6.283185307179586232, phi);      // 2*pi rounded to double
+    red = fma(-k, 2.4492935982947064e-16, red);            // 2*pi minus that double
+    double sn, cs;
+    sincos(red, &sn, &cs);
+    ra = (float)((double)qa * cs - (double)qb * sn);
+    rb = (float)((double)qb * cs + (double)qa * sn);
+}
+
 // bf16 bit pattern of x rounded to nearest, ties to even (finite inputs; an
 // overflow rounds to infinity).
 __device__ __forceinline__ uint32_t bf16_rne_bits(float x)

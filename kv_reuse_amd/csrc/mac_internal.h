@@ -46,13 +46,22 @@ constexpr int TILE_W = 64;      // ring slots a wave scans at once (LDS tile or 
 constexpr int MAX_GROUPS = 4096;  // B * Hkv
 constexpr int MIN_PAGES_PER_WORKER = 1;
 
-// Counters, one uint64 block: MAC_NSTAT device-wide ones (only ST_BAD_INPUT,
-// by atomics on error paths), then HEAD_NSTAT per (request, query head),
+// Counters, one uint64 block: MAC_NSTAT device-wide ones (by atomics: bad
+// input on error paths, the prefill's counts once per block), then
+// HEAD_NSTAT per (request, query head),
 // written without atomics by the match wave that owns the head, then
 // GRP_NSTAT per (request, KV group): keys streamed by complete (written by
 // block 0 of the complete grid) and re-read by amend (written by the amend
 // block of the group).  The host sums them.
-enum GlobalStat { ST_BAD_INPUT = 0, MAC_NSTAT = 8 };
+enum GlobalStat {
+    ST_BAD_INPUT = 0,
+    ST_PF_TOKENS,        // prompt tokens taken by the prefill
+    ST_PF_DECISIONS,     // their (token, head) decisions
+    ST_PF_HITS,
+    ST_PF_KV,            // keys attended per (KV group, token)
+    ST_PF_OVR_INVALID,   // prefill overrides naming no earlier token
+    MAC_NSTAT = 8
+};
 enum HeadStat { HS_HITS = 0, HS_MISSES, HS_NEAR_TAU, HS_OVR_INVALID, HEAD_NSTAT };
 enum GroupStat { GS_TOK_CRIT = 0, GS_TOK_AMEND, GRP_NSTAT };
 inline long stats_count(long n_heads, long n_groups)
@@ -113,6 +122,13 @@ hipError_t launch_append(const Shape &s, const State &st, const KvView &kv, bool
                          const void *k_new, const void *v_new, const int32_t *positions,
                          hipStream_t stream);
 hipError_t launch_reset(const Shape &s, const State &st, hipStream_t stream);
+// MAC over the prompt (seq_lens[b] tokens of request b, N rows each) with an
+// unbounded window; scratch holds prefill_scratch_bytes(s, N) bytes.
+size_t prefill_scratch_bytes(const Shape &s, int N);
+hipError_t launch_prefill(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
+                          const int32_t *seq_lens, int N, const float *q_pre, float *out,
+                          const int32_t *override_pos, int32_t *p_out, void *scratch,
+                          hipStream_t stream);
 // Workgroups of the complete kernel resident per CU (occupancy query).
 int complete_blocks_per_cu(bool kv_fp32, int G, size_t plan_lds_bytes);
 bool supported_group(int G);

@@ -546,6 +546,39 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
     return MAC_OK;
 }
 
+mac_status mac_prefill(mac_handle h, const mac_kv_view *kv, int32_t num_tokens,
+                       const float *q_pre, float *out, const int32_t *override_pos,
+                       int32_t *p_out, void *stream)
+{
+    if (!h)
+        return fail(nullptr, MAC_EINVAL, "handle is NULL");
+    mac_status s = check_view(h, kv);
+    if (s != MAC_OK)
+        return s;
+    if (num_tokens < 1 || num_tokens > 32768)
+        return fail(h, MAC_EINVAL, "num_tokens must be in [1, 32768]");
+    if (!q_pre || !out)
+        return fail(h, MAC_EINVAL, "q_pre and out must be non-NULL");
+    if (!aligned16(q_pre) || !aligned16(out))
+        return fail(h, MAC_EINVAL, "q_pre and out must be 16-byte aligned");
+    hipStream_t st = stream ? (hipStream_t)stream : h->main_stream;
+    const size_t bytes = mac::prefill_scratch_bytes(h->shape, num_tokens);
+    void *scratch = nullptr;
+    if (hipMallocAsync(&scratch, bytes, st) != hipSuccess || !scratch) {
+        (void)hipGetLastError();
+        return fail(h, MAC_ENOMEM, "stream-ordered allocation of the prefill scratch failed");
+    }
+    const hipError_t e = mac::launch_prefill(h->shape, h->st, to_view(h, kv), h->kv_fp32,
+                                             kv->seq_lens, num_tokens, q_pre, out, override_pos,
+                                             p_out, scratch, st);
+    const hipError_t ef = hipFreeAsync(scratch, st);
+    if (e != hipSuccess)
+        return fail_hip(h, "launch_prefill", e);
+    if (ef != hipSuccess)
+        return fail_hip(h, "hipFreeAsync", ef);
+    return MAC_OK;
+}
+
 mac_status mac_stats(mac_handle h, mac_stats_t *out)
 {
     if (!h || !out)
@@ -582,6 +615,11 @@ mac_status mac_stats(mac_handle h, mac_stats_t *out)
     out->kv_bytes_amend = gs[mac::GS_TOK_AMEND] * row;
     out->aux_bytes = h->aux_bytes;
     out->bad_input = raw[mac::ST_BAD_INPUT];
+    out->prefill_tokens = raw[mac::ST_PF_TOKENS];
+    out->prefill_decisions = raw[mac::ST_PF_DECISIONS];
+    out->prefill_hits = raw[mac::ST_PF_HITS];
+    out->prefill_kv_tokens = raw[mac::ST_PF_KV];
+    out->prefill_override_invalid = raw[mac::ST_PF_OVR_INVALID];
     if (h->timed_step) {
         float t = 0.f;
         if (hipEventElapsedTime(&t, h->tm[0], h->tm[1]) == hipSuccess) out->last_us_match = t * 1e3f;

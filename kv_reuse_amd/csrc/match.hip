@@ -246,17 +246,10 @@ __global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
     if (act) {
         st.q_copy[idx * D + lane] = qa;
         st.q_copy[idx * D + lane + 64] = qb;
-        // rotate-half RoPE, angle m * theta^(-2i/D) formed in fp64 and reduced
-        // to [-pi, pi] in fp64 (Cody-Waite, 2*pi split in two doubles, fma), so
-        // sincos stays on its short-argument path
-        const double phi = (double)m * inv;
-        const double k = rint(phi * 0.15915494309189535);   // 1 / (2*pi)
-        double red = fma(-k, 6.283185307179586232, phi);      // 2*pi rounded to double
-        red = fma(-k, 2.4492935982947064e-16, red);            // 2*pi minus that double
-        double sn, cs;
-        sincos(red, &sn, &cs);
-        st.q_rot[idx * D + lane] = (float)((double)qa * cs - (double)qb * sn);
-        st.q_rot[idx * D + lane + 64] = (float)((double)qb * cs + (double)qa * sn);
+        float ra, rb;
+        rope_pair(qa, qb, m, inv, ra, rb);
+        st.q_rot[idx * D + lane] = ra;
+        st.q_rot[idx * D + lane + 64] = rb;
     } else {
         // idle request: its output is zero (no group of it gets work)
         out[idx * D + lane] = 0.f;

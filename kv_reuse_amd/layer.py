@@ -29,6 +29,9 @@ class MacLayer:
     def decode_step(self, kv, q_pre_rope, out, override_pos=None, stream=None):
         _lib.mac_decode_step(self.h, kv, q_pre_rope, out, override_pos, stream)
 
+    def prefill(self, kv, num_tokens, q_pre, out, override_pos=None, p_out=None, stream=None):
+        _lib.mac_prefill(self.h, kv, num_tokens, q_pre, out, override_pos, p_out, stream)
+
     def stats(self):
         return _lib.mac_stats(self.h)
 

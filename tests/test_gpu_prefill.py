@@ -1,0 +1,143 @@
+"""GPU parity of mac_prefill (MAC-Attention over the prompt with an unbounded
+window, the pages' Table 8 ablation) through the C ABI.
+
+The oracle takes the prompt as decode calls in order, one per token, with a
+ring as long as the prompt: no entry is ever evicted, which is the unbounded
+window.  Decisions (matched positions) bit-exact; outputs within max-abs 2e-3
+and per-row relative 1e-2.  Near-threshold and near-tie decisions are forced
+to the oracle's through the override input, as in the decode tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_harness import MAX_ABS, ROW_REL
+from workloads import bf16_bits, get_config, kv_logical, page_table, queries, scaled, to_paged
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill_case(w, lens=None, bands=None, flags=0, oflags=0):
+    import kv_reuse_amd as mac
+    import oracle
+    N, B, Hq, d = w.steps, w.B, w.Hq, w.d
+    lens = np.full(B, N, np.int32) if lens is None else np.asarray(lens, np.int32)
+    print("prefill case", w.name, "B", B, "Hq", Hq, "Hkv", w.Hkv, "N", N, "lens", lens.tolist(),
+          w.kv, w.layout, "flags", flags, flush=True)
+    K, V = kv_logical(w, "cuda")
+    paged = w.layout == "paged"
+    if paged:
+        tab = page_table(w)
+        kc, vc, table = to_paged(K, tab), to_paged(V, tab), torch.as_tensor(tab, device="cuda")
+    else:
+        kc, vc, table = K, V, None
+    q = queries(w, steps=N)                                  # [N][B][Hq][d]
+    Kg = [bf16_bits(K[b, g]) for b in range(B) for g in range(w.Hkv)]
+    Vg = [bf16_bits(V[b, g]) for b in range(B) for g in range(w.Hkv)]
+    orc = oracle.Oracle(B, Hq, w.Hkv, d, N, w.r if bands is None else bands, w.tau, w.theta,
+                        kv_fp32=(w.kv == "fp32"), flags=oflags)
+    ov = np.full((B, N, Hq), -2, np.int32)
+    want_p = np.full((B, N, Hq), -1, np.int32)
+    want_o = np.zeros((B, N, Hq, d))
+    keys = 0
+    for t in range(N):
+        seq = np.where(t < lens, t + 1, 0).astype(np.int32)
+        res = orc.step(Kg, Vg, seq, q[t])
+        flag = (res["near_tau"] | res["near_tie"]).astype(bool)
+        ov[:, t][flag] = np.where(res["hit"][flag] != 0, res["p"][flag], -1)
+        want_p[:, t] = np.where(res["hit"] != 0, res["p"], -1)
+        want_o[:, t] = res["out"]
+        keys += int(res["kv_tokens"].sum())
+    cfg = mac.make_config(batch=B, num_q_heads=Hq, num_kv_heads=w.Hkv, ring_size=w.W, band=w.r,
+                          tau=w.tau, rope_theta=w.theta,
+                          layout=mac.MAC_KV_PAGED if paged else mac.MAC_KV_CONTIGUOUS,
+                          kv_dtype=mac.MAC_FP32 if w.kv == "fp32" else mac.MAC_BF16,
+                          max_seq_len=w.n_cap, flags=flags, band_per_head=bands)
+    layer = mac.MacLayer(cfg)
+    try:
+        seq_d = torch.as_tensor(lens, device="cuda")
+        view = mac.make_kv_view(kc, vc, seq_d, table, num_pages=kc.shape[0] if paged else 0)
+        qd = torch.as_tensor(np.ascontiguousarray(q.transpose(1, 0, 2, 3)), device="cuda")
+        out = torch.full((B, N, Hq, d), float("nan"), device="cuda")
+        pout = torch.full((B, N, Hq), -7, dtype=torch.int32, device="cuda")
+        layer.prefill(view, N, qd, out, torch.as_tensor(ov, device="cuda"), pout)
+        torch.cuda.synchronize()
+        st = layer.stats()
+    finally:
+        layer.close()
+    p_g = pout.cpu().numpy()
+    o_g = out.cpu().numpy().astype(np.float64)
+    assert np.array_equal(p_g, want_p), np.argwhere(p_g != want_p)[:8]
+    live = np.arange(N)[None, :] < lens[:, None]              # [B][N]
+    assert not o_g[~live].any(), "rows past a prompt must be zero"
+    g, o = o_g[live], want_o[live]
+    assert np.all(np.isfinite(g))
+    err = np.abs(g - o)
+    rel = np.linalg.norm(g - o, axis=-1) / np.maximum(np.linalg.norm(o, axis=-1), 1e-30)
+    hits = int((want_p >= 0).sum())
+    print("  hits", hits, "of", int(lens.sum()) * Hq, "forced", int((ov != -2).sum()),
+          "max-abs %.2e row-rel %.2e" % (err.max(), rel.max()), flush=True)
+    assert err.max() <= MAX_ABS and rel.max() <= ROW_REL
+    assert st["prefill_tokens"] == lens.sum()
+    assert st["prefill_decisions"] == lens.sum() * Hq
+    assert st["prefill_hits"] == hits
+    assert st["prefill_kv_tokens"] == keys
+    assert st["prefill_override_invalid"] == 0 and st["bad_input"] == 0
+    return hits
+
+
+def _w(base, **kw):
+    return scaled(get_config(base), C=0, **kw)
+
+
+def test_prefill_paged_mixed_rho(gpu_lib):
+    """128K workload's head shape and paged cache, per-request rho 0.95..0.995
+    over a 700-token prompt: hits chain back over many tokens, misses too."""
+    w = _w("b16_128k", B=2, steps=700, rho=("per_request_uniform", 0.95, 0.995))
+    hits = _prefill_case(w)
+    assert 0 < hits < 2 * 700 * 32
+
+
+def test_prefill_moe_heads(gpu_lib):
+    """32q/4kv (8 query heads per KV head), per-head rho 0.5..0.99, r = 64."""
+    w = _w("moe_122k", B=1, steps=600, r=64)
+    assert _prefill_case(w) > 0
+
+
+def test_prefill_fp32_contiguous(gpu_lib):
+    w = _w("cpu4k", steps=500, r=64, rho=("const", 0.97))
+    assert _prefill_case(w) > 0
+
+
+def test_prefill_ragged_prompts(gpu_lib):
+    """Prompts of 300, 151 and 1 tokens in one call of 300 rows."""
+    w = _w("b16_128k", B=3, steps=300, rho=("const", 0.98))
+    assert _prefill_case(w, lens=[300, 151, 1]) > 0
+
+
+def test_prefill_per_head_bands(gpu_lib):
+    w = _w("b16_128k", B=1, steps=400, rho=("const", 0.98))
+    bands = [(16, 64, 256, 3)[h % 4] for h in range(w.Hq)]
+    assert _prefill_case(w, bands=bands) > 0
+
+
+def test_prefill_ring_bf16(gpu_lib):
+    import kv_reuse_amd as mac
+    import oracle
+    w = _w("b16_128k", B=1, steps=400, rho=("const", 0.98))
+    assert _prefill_case(w, flags=mac.MAC_F_RING_BF16, oflags=oracle.F_RING_BF16) > 0
+
+
+def test_prefill_disable_reuse_is_causal_attention(gpu_lib):
+    import kv_reuse_amd as mac
+    import oracle
+    w = _w("b16_128k", B=1, steps=300, rho=("const", 0.98))
+    assert _prefill_case(w, flags=mac.MAC_F_DISABLE_REUSE, oflags=oracle.F_DISABLE_REUSE) == 0
+
+
+@pytest.mark.parametrize("n", [1, 64, 65])
+def test_prefill_tile_edges(gpu_lib, n):
+    """One token (no earlier query: a miss), and prompts ending on and just past
+    the match kernel's 64-token tiles."""
+    w = _w("b16_128k", B=1, steps=n, rho=("const", 0.98))
+    _prefill_case(w)

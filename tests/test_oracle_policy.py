@@ -135,6 +135,9 @@ _STALE = oracle.F_STALE_RING
 @pytest.mark.parametrize("kv,tau,W,r,flags", [("fp32", 0.5, 4, 3, 0), ("bf16", 0.45, 4, 5, 0),
                                               ("fp32", 1e9, 3, 2, 0), ("bf16", 0.0, 2, 4, 0),
                                               ("fp32", 0.6, 1, 3, 0),
+                                              # a ring longer than the run never evicts:
+                                              # the unbounded window of the prefill reading
+                                              ("fp32", 0.5, 64, 3, 0),
                                               ("fp32", 0.5, 4, 3, _STALE),
                                               ("bf16", 1e9, 3, 2, _STALE),
                                               ("fp32", 1e9, 1, 3, _STALE)])
