@@ -696,7 +696,9 @@ def main():
                   "loop_us_per_step": {
                       "mac": loop_us(wa, 0, cache, qa, k_rows, v_rows, 4, 16),
                       "mac_fused_amend": loop_us(wa, mac.MAC_F_FUSED_AMEND, cache, qa, k_rows,
-                                                 v_rows, 4, 16)}}
+                                                 v_rows, 4, 16),
+                      "mac_sync_amend": loop_us(wa, mac.MAC_F_SYNC_AMEND, cache, qa, k_rows,
+                                                v_rows, 4, 16)}}
         # the mixed workload's decode loop, amend included, for every amend form
         lh = {}
         loops = {"mac": loop_us(w, 0, cache, q_dev, k_rows, v_rows, 4, 16, lh),
@@ -704,6 +706,8 @@ def main():
                                             v_rows, 4, 16, lh),
                  "mac_stale_ring": loop_us(w, mac.MAC_F_STALE_RING, cache, q_dev, k_rows,
                                            v_rows, 4, 16, lh),
+                 "mac_sync_amend": loop_us(w, mac.MAC_F_SYNC_AMEND, cache, q_dev, k_rows,
+                                           v_rows, 4, 16),
                  "full_attention": loop_us(w, mac.MAC_F_DISABLE_REUSE, cache, q_dev, k_rows,
                                            v_rows, 4, 16),
                  "head_hit_rate": {"mac": lh[0], "mac_stale_ring": lh[mac.MAC_F_STALE_RING]}}
@@ -719,7 +723,9 @@ def main():
                      "mac_stale_ring": loop_us(ws, mac.MAC_F_STALE_RING, cache, qsd, k_rows,
                                                v_rows, 4, 16, sh),
                      "mac_fused_amend": loop_us(ws, mac.MAC_F_FUSED_AMEND, cache, qsd, k_rows,
-                                                v_rows, 4, 16)},
+                                                v_rows, 4, 16),
+                     "mac_sync_amend": loop_us(ws, mac.MAC_F_SYNC_AMEND, cache, qsd, k_rows,
+                                               v_rows, 4, 16)},
                  "head_hit_rate": {"mac": sh[0], "mac_stale_ring": sh[mac.MAC_F_STALE_RING]}}
         allhit["stale_ring_point"] = stale
 
