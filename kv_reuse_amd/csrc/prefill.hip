@@ -344,12 +344,12 @@ __global__ __launch_bounds__(64) void prefill_attend_kernel(Shape s, State st, K
 }
 
 // =================================================================== count
-// Grid (Hkv, B), 256 threads: the group's prompt tokens, decisions, hits and
-// keys attended (t - min_g lo_g + 1 per token), then one atomic each.
+// Grid (Hkv, B), 256 threads (4 waves): the group's prompt tokens, decisions,
+// hits and keys attended (t - min_g lo_g + 1 per token), then one atomic each.
 __global__ __launch_bounds__(256) void prefill_count_kernel(Shape s, State st, KvView kv, Pf pf,
                                                             const int32_t *__restrict__ seq_lens)
 {
-    __shared__ unsigned long long red[3][4];
+    __shared__ unsigned long long red[2][4];   // hits, keys per wave
     const int kvh = blockIdx.x, b = blockIdx.y;
     bool bad;
     const int n = prompt_len(kv, seq_lens[b], pf.N, bad);
