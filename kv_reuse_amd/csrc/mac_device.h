@@ -478,6 +478,59 @@ __device__ __forceinline__ int page_owner(long x, int nW, int P)
     return (int)(((x + 1) * (long)nW - 1) / P);
 }
 
+// Dispatch-round weights.  The grid holds `slots` blocks per CU, dispatched
+// round by round (block b in round b / CUs), and the CU's issue arbiter
+// favours older waves: with equal shares the first round's waves finish
+// first.  At three rounds (G <= 4) the last round also holds the slowest
+// waves and sets the end of the launch (wave ends at 128K x 16 per round,
+// median / max: 967 / 1004, 998 / 1025, 1025 / 1054 us), so with many pages
+// per wave the balanced plan gives round k the weight
+// 1000 + SLOT_TILT * (slots - 1 - 2k) per mille (complete 1081 -> 1070 us).
+// At two rounds (G = 8) the rounds' slowest waves end together (310 / 312 us
+// of 8 x 122880) and the weights only lengthened the first round (+2.8 %).
+constexpr int SLOT_TILT = 30;
+
+__device__ __forceinline__ bool tilted_plan(const State &st, int nW, int P)
+{
+    return st.slots >= 3 && nW == st.n_workers && P >= 16 * nW;
+}
+
+// Weight of the workers before worker w (nW = slots * Nk workers, round w / Nk).
+__device__ __forceinline__ long long cum_weight(int w, int Nk, int S)
+{
+    const int k = w / Nk, j = w % Nk;
+    long long c = 0;
+    for (int i = 0; i < k; ++i)
+        c += (long long)Nk * (1000 + SLOT_TILT * (S - 1 - 2 * i));
+    return c + (long long)j * (1000 + SLOT_TILT * (S - 1 - 2 * k));
+}
+
+// First flattened page of worker w's share (w = nW gives P).
+__device__ __forceinline__ long share_start(const State &st, int w, int nW, int P)
+{
+    if (!tilted_plan(st, nW, P))
+        return (long)w * P / nW;
+    const int S = st.slots, Nk = nW / S;
+    return (long)((long long)P * cum_weight(w, Nk, S) / cum_weight(nW, Nk, S));
+}
+
+// Owner of flattened page x under share_start: the last worker whose share
+// starts at or before x (every share holds at least 15 pages when tilted).
+__device__ inline int share_owner(const State &st, long x, int nW, int P)
+{
+    if (!tilted_plan(st, nW, P))
+        return page_owner(x, nW, P);
+    int lo = 0, hi = nW - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (share_start(st, mid, nW, P) <= x)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
 // Waves of the unbalanced plan given to each segment (the host checks that
 // every segment gets at least one).
 __device__ __forceinline__ int waves_per_segment(const State &st, int nS)
@@ -487,7 +540,8 @@ __device__ __forceinline__ int waves_per_segment(const State &st, int nS)
 
 // Worker w's share [x0, x1) of the flattened page list (x0 >= x1: none).
 // Balanced plan (the default, Figure 3 (b)): the nW active waves split all P
-// pages of the step evenly, whatever segment they belong to.  Unbalanced plan
+// pages of the step evenly (weighted by dispatch round when the shares are
+// long), whatever segment they belong to.  Unbalanced plan
 // (MAC_F_UNBALANCED_PLAN, the baseline of Figure 8 (b)): every segment gets
 // the same k waves, which split that segment's own pages evenly (one wave per
 // page when it has fewer than k), so the longest span sets the time.
@@ -495,8 +549,8 @@ __device__ __forceinline__ void worker_share(const Shape &s, const State &st, co
                                              int nS, int nW, int P, int w, long &x0, long &x1)
 {
     if (!s.unbalanced) {
-        x0 = (long)w * P / nW;
-        x1 = (long)(w + 1) * P / nW;
+        x0 = share_start(st, w, nW, P);
+        x1 = share_start(st, w + 1, nW, P);
         return;
     }
     const int k = waves_per_segment(st, nS), sg = w / k, j = w % k;
@@ -540,7 +594,8 @@ __device__ inline void publish_plan(const Shape &s, const State &st, const int *
         if (n > 0 && s.unbalanced)
             r = make_int2(i * k, i * k + min(k, n) - 1);
         else if (n > 0)
-            r = make_int2(page_owner(off[i], nW, P), page_owner((long)off[i + 1] - 1, nW, P));
+            r = make_int2(share_owner(st, off[i], nW, P),
+                          share_owner(st, (long)off[i + 1] - 1, nW, P));
         reinterpret_cast<int2 *>(st.grp_parts)[i] = r;
     }
     for (int g = threadIdx.x; g < nG; g += blockDim.x) {

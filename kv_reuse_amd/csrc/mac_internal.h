@@ -100,6 +100,7 @@ struct State {
     const int32_t *band;      // [Hq] band r_h of each query head
     float *tile_best;         // W > TILE_W: [B*Hq][ceil(W/TILE_W)][3] per-tile nearest (D, pos, slot)
     int32_t n_workers;        // waves in the complete grid
+    int32_t slots;            // blocks of the complete grid per CU (dispatch rounds)
 };
 
 // Launchers (enqueue only; return the launch status).

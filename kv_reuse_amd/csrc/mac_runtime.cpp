@@ -322,7 +322,8 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     const int G = cfg->num_q_heads / cfg->num_kv_heads;
     const size_t plan_lds =
         (size_t)(cfg->batch * cfg->num_kv_heads * segments_per_group(*cfg) + 1) * sizeof(int);
-    h->n_blocks = n_cu * mac::complete_blocks_per_cu(h->kv_fp32, G, plan_lds);
+    h->st.slots = mac::complete_blocks_per_cu(h->kv_fp32, G, plan_lds);
+    h->n_blocks = n_cu * h->st.slots;
     h->st.n_workers = h->n_blocks * mac::WAVES;
     const long n_seg = (long)cfg->batch * cfg->num_kv_heads * segments_per_group(*cfg);
     if ((cfg->flags & MAC_F_UNBALANCED_PLAN) && n_seg > h->st.n_workers)
