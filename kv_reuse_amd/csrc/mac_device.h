@@ -432,12 +432,13 @@ __device__ __forceinline__ Seg segment(const Shape &s, const State &st, int seg)
     Seg r;
     r.b = g / s.Hkv;
     r.kvh = g % s.Hkv;
+    // the heads' starts are loaded together with m (one round trip, not two)
     r.m = st.m_buf[r.b];
+    const int gs = group_start(s, st, g);
     r.lo = 0;
     r.hi = -1;
     if (r.m < 0)
         return r;
-    const int gs = group_start(s, st, g);
     if (s.nseg == 1) {
         r.lo = gs;
         r.hi = r.m;
