@@ -1,7 +1,7 @@
 // mac_device.h -- device helpers shared by the gfx950 kernels of the
-// MAC-Attention decode step (match.hip, complete.hip, reduce.hip, amend.hip):
-// wave64 lane exchanges (DPP, ds_swizzle), key/value row loads, the VALU
-// flash-decode wave worker and the device-side work plan.
+// MAC-Attention decode step (match.hip, complete.hip, reduce.hip, amend.hip,
+// prefill.hip): wave64 lane exchanges (DPP, ds_swizzle), RoPE, key/value row
+// loads, the VALU flash-decode wave worker and the device-side work plan.
 //
 // Key/value rows stream as 16-byte loads: for bf16 a row of 128 elements is
 // 16 lanes, a wave load covers 4 tokens and a 16-token page is 4 loads of K

@@ -1,6 +1,6 @@
 // mac_internal.h -- state layout and kernel launch interface shared by the
 // host runtime (mac_runtime.cpp) and the gfx950 kernels (match.hip,
-// complete.hip, reduce.hip, amend.hip).
+// complete.hip, reduce.hip, amend.hip, prefill.hip).
 //
 // Device memory owned by a handle (fp32 unless noted):
 //   ring_q     [B][Hq][W][D]        pre-RoPE queries of recent steps (fp32, or
@@ -42,17 +42,16 @@ constexpr int PAGE = 16;        // tokens per page
 constexpr int BLOCK = 256;      // threads per workgroup (4 waves of 64)
 constexpr int WAVES = BLOCK / 64;
 constexpr int MAX_W = 2048;     // ring slots per (request, head)
-constexpr int TILE_W = 64;      // ring slots a wave scans at once (LDS tile or one tile wave)
+constexpr int TILE_W = 64;      // ring slots one wave scans (the whole ring, or one tile of it)
 constexpr int MAX_GROUPS = 4096;  // B * Hkv
 constexpr int MIN_PAGES_PER_WORKER = 1;
 
 // Counters, one uint64 block: MAC_NSTAT device-wide ones (by atomics: bad
 // input on error paths, the prefill's counts once per block), then
-// HEAD_NSTAT per (request, query head),
-// written without atomics by the match wave that owns the head, then
-// GRP_NSTAT per (request, KV group): keys streamed by complete (written by
-// block 0 of the complete grid) and re-read by amend (written by the amend
-// block of the group).  The host sums them.
+// HEAD_NSTAT per (request, query head), written without atomics by the match
+// wave that owns the head, then GRP_NSTAT per (request, KV group): keys
+// streamed by complete (written by block 0 of the complete grid) and re-read
+// by amend (written by the amend block of the group).  The host sums them.
 enum GlobalStat {
     ST_BAD_INPUT = 0,
     ST_PF_TOKENS,        // prompt tokens taken by the prefill

@@ -1,9 +1,10 @@
 // mac_runtime.cpp -- host side of the C ABI declared in include/mac.h.
 //
 // Owns a layer's device state, the amend stream and the events that order
-// match(m) after amend(m-1) (the pages' "async cache update", MAC-Attention
-// Figure 2 (c)).  No host synchronisation happens inside a decode step: the
-// hit/miss decisions, the work plan and the merge all stay on the device.
+// match(t) after amend(t-1), or after amend(t-2) with the stale-by-one ring
+// (the pages' "async cache update", MAC-Attention Figure 2 (c)).  No host
+// synchronisation happens inside a decode step or a prefill: the hit/miss
+// decisions, the work plan and the merge all stay on the device.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
