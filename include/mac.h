@@ -9,12 +9,14 @@
  * matched entry's cached prefix summary (complete, Figure 2 (b)); off the
  * critical path the last r keys are removed from the new summary and the pair
  * (pre-RoPE query, summary) enters the ring (amend, Figure 2 (c)).  A miss is
- * full attention over the whole context.
+ * full attention over the whole context.  mac_prefill applies the same policy
+ * to a prompt with an unbounded window (the pages' Table 8 ablation).
  *
  * Conventions for every call:
  *  - Pointers are device pointers unless marked "host".  The key/value
- *    caches, k_new, v_new, q_pre_rope and out must be 16-byte aligned (the
- *    kernels move rows as 16-byte vectors); a misaligned one is MAC_EINVAL.
+ *    caches, k_new, v_new, the queries (q_pre_rope, q_pre) and out must be
+ *    16-byte aligned (the kernels move rows as 16-byte vectors); a misaligned
+ *    one is MAC_EINVAL.
  *  - Positions are 0-based.  For request b the query position is
  *    m = seq_lens[b] - 1; its own K/V row must already be in the cache.
  *  - A summary (o, M, l) is the normalised attention output o[d], a reference
