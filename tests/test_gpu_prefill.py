@@ -141,3 +141,66 @@ def test_prefill_tile_edges(gpu_lib, n):
     the match kernel's 64-token tiles."""
     w = _w("b16_128k", B=1, steps=n, rho=("const", 0.98))
     _prefill_case(w)
+
+
+def _small_layer(w, flags=0):
+    import kv_reuse_amd as mac
+    K, V = kv_logical(w, "cuda")
+    tab = page_table(w)
+    kc, vc, table = to_paged(K, tab), to_paged(V, tab), torch.as_tensor(tab, device="cuda")
+    cfg = mac.make_config(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, ring_size=w.W,
+                          band=w.r, tau=w.tau, rope_theta=w.theta, layout=mac.MAC_KV_PAGED,
+                          kv_dtype=mac.MAC_BF16, max_seq_len=w.n_cap, flags=flags)
+    return mac.MacLayer(cfg), kc, vc, table
+
+
+def test_prefill_bad_lengths_and_overrides_are_counted(gpu_lib):
+    """A prompt length beyond the rows given idles its request (zero output,
+    counted in bad_input); an override naming the token itself or a later one
+    is a counted miss; the other requests are unaffected."""
+    import kv_reuse_amd as mac
+    w = _w("b16_128k", B=2, steps=80, rho=("const", 0.98))
+    N = 64
+    layer, kc, vc, table = _small_layer(w)
+    try:
+        seq = torch.tensor([N + 5, N], dtype=torch.int32, device="cuda")   # request 0: too long
+        view = mac.make_kv_view(kc, vc, seq, table, num_pages=kc.shape[0])
+        q = queries(w, steps=N)
+        qd = torch.as_tensor(np.ascontiguousarray(q.transpose(1, 0, 2, 3)), device="cuda")
+        out = torch.full((w.B, N, w.Hq, w.d), float("nan"), device="cuda")
+        ov = torch.full((w.B, N, w.Hq), -2, dtype=torch.int32, device="cuda")
+        ov[1, 10, 3] = 10          # the token itself: no earlier entry
+        ov[1, 11, 4] = 40          # a later token
+        ov[1, 12, 5] = 3           # a valid earlier token: forced hit
+        pout = torch.full((w.B, N, w.Hq), -7, dtype=torch.int32, device="cuda")
+        layer.prefill(view, N, qd, out, ov, pout)
+        torch.cuda.synchronize()
+        st = layer.stats()
+        assert st["bad_input"] == 1 and st["prefill_tokens"] == N
+        assert st["prefill_override_invalid"] == 2
+        assert not out[0].any() and (pout[0] == -1).all()
+        assert torch.isfinite(out[1]).all()
+        assert pout[1, 10, 3] == -1 and pout[1, 11, 4] == -1 and pout[1, 12, 5] == 3
+    finally:
+        layer.close()
+
+
+def test_prefill_host_checks(gpu_lib):
+    import kv_reuse_amd as mac
+    w = _w("b16_128k", B=1, steps=16)
+    layer, kc, vc, table = _small_layer(w)
+    try:
+        seq = torch.tensor([16], dtype=torch.int32, device="cuda")
+        view = mac.make_kv_view(kc, vc, seq, table, num_pages=kc.shape[0])
+        q = torch.zeros((1, 16, w.Hq, w.d), device="cuda")
+        out = torch.zeros_like(q)
+        for n in (0, 32769):
+            with pytest.raises(mac.MacError) as ei:
+                layer.prefill(view, n, q, out)
+            assert ei.value.status == mac.MAC_EINVAL
+        qm = torch.zeros(1 * 16 * w.Hq * w.d + 1, device="cuda")[1:]   # 4-byte offset
+        with pytest.raises(mac.MacError) as ei:
+            layer.prefill(view, 16, qm, out)
+        assert ei.value.status == mac.MAC_EINVAL
+    finally:
+        layer.close()
