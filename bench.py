@@ -627,11 +627,16 @@ def main():
 
     # pass 2: the same steps from a fresh ring (same decisions, same bytes)
     # with the library's HIP events around every kernel (MAC_F_TIMING)
-    kb = Bench(w, mac_flags | mac.MAC_F_TIMING, kc, vc, paged, table, bands)
+    kb = Bench(w, mac_flags | mac.MAC_F_TIMING | mac.MAC_F_RECORD_DEBUG, kc, vc, paged, table,
+               bands)
     comp, match, red, amend, att_ev, toks2 = [], [], [], [], [], []
+    mac_out, mac_hit = {}, {}     # steps 4..19: outputs and hit flags, for the deviation
     prev = None
     for t in range(total):
         st = kb.step(t, q_dev[t], k_rows[t], v_rows[t])
+        if 4 <= t < 20:
+            mac_out[t] = kb.out.clone()
+            mac_hit[t] = torch.as_tensor(kb.layer.debug_last()[1], device="cuda").bool()
         if t >= args.warmup:
             comp.append(st["last_us_complete"])
             match.append(st["last_us_match"])
@@ -657,6 +662,7 @@ def main():
     base = None
     if not args.no_baseline_kernel:
         fa, fc = [], []
+        dev_all, dev_hit = [], []
         for fl in (mac.MAC_F_DISABLE_REUSE, mac.MAC_F_DISABLE_REUSE | mac.MAC_F_TIMING):
             fb = Bench(w, fl, kc, vc, paged, table)
             for t in range(min(total, 4 + 16)):
@@ -666,9 +672,24 @@ def main():
                         fc.append(st["last_us_complete"])
                     else:
                         fa.append(st["span_us"])
+                        if bands is None and t in mac_out:
+                            # MAC vs full attention on the same step (information)
+                            f = fb.out
+                            rel = (mac_out[t] - f).norm(dim=-1) / f.norm(dim=-1)
+                            dev_all.append(rel.flatten())
+                            dev_hit.append(rel[mac_hit[t]])
             fb.layer.close()
         full_tok = (w.C + total) * w.B * w.Hkv
+        deviation = None
+        if dev_all:
+            da, dh = torch.cat(dev_all), torch.cat(dev_hit)
+            deviation = {"what": "||O_mac - O_full|| / ||O_full|| per (request, head), steps 4-19",
+                         "mean_all_heads": float(da.mean()),
+                         "mean_hit_heads": float(dh.mean()) if dh.numel() else None,
+                         "max_hit_heads": float(dh.max()) if dh.numel() else None,
+                         "hit_heads": int(dh.numel()), "heads": int(da.numel())}
         base = {"attention_us": float(np.mean(fa)), "complete_us": float(np.mean(fc)),
+                "mac_vs_full_deviation": deviation,
                 "hbm_gbps": full_tok * row_bytes / (float(np.mean(fc)) * 1e-6) / 1e9,
                 "speedup_vs_full": float(np.mean(fa)) / att_us}
 
