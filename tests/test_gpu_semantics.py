@@ -181,6 +181,47 @@ def test_idle_request_outputs_zero_and_stores_nothing():
         ls.close()
 
 
+def test_all_requests_idle_then_resume():
+    """A step with every request idle has no work at all (no pages for the
+    complete grid): outputs are zero, nothing enters the rings, and the next
+    steps continue as the oracle does."""
+    from gpu_harness import Lockstep
+    w = _case(steps=8)
+    ls = Lockstep(w)
+    try:
+        for t in range(8):
+            seq = np.full(w.B, w.C + t + 1, np.int32)
+            if t in (0, 3):
+                seq[:] = 0
+            info = ls.step(t, seq_lens=seq)
+            if t in (0, 3):
+                assert not info["out_gpu"].any() and not info["hit_gpu"].any()
+    finally:
+        ls.close()
+
+
+def test_tau_zero_hits_only_exact_repeats():
+    """tau = 0: a hit needs distance exactly 0.  Repeating the previous step's
+    query hits it (span [m-1-r+1, m]); a fresh query misses."""
+    from gpu_harness import Lockstep
+    w = _case(steps=10)
+    ls = Lockstep(w, tau=0.0)
+    try:
+        q = ls.q
+        # steps 4 and 5 repeat step 3's query, step 8 repeats step 7's
+        src = {4: 3, 5: 3, 8: 7}
+        for t in range(10):
+            info = ls.step(t, q=q[src.get(t, t)])
+            if t in src:
+                # distance 0 to the entries holding that query; ties go to the
+                # newest, the previous step's (p = m - 1)
+                assert info["hit_gpu"].all() and (info["p_gpu"] == w.C + t - 1).all()
+            else:
+                assert not info["hit_gpu"].any()
+    finally:
+        ls.close()
+
+
 @pytest.mark.parametrize("fused", [False, True])
 def test_stats_match_oracle_counts(fused):
     """Counters against the oracle's decisions and key counts; amend re-reads
