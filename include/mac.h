@@ -204,7 +204,9 @@ mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv /* host */, const v
  * an equal share, and a kernel still resident when it starts would delay some
  * of its waves.  The library copies what amend needs, so the caller
  * may reuse q_pre_rope, out and seq_lens as soon as the step's work on
- * `stream` has run. */
+ * `stream` has run.  The ring slot a call writes and the events it waits on
+ * are chosen on the host per call, so a decode step is not meant to be
+ * captured into a HIP graph and replayed. */
 mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv /* host */,
                            const float *q_pre_rope, float *out, const int32_t *override_pos,
                            void *stream);
