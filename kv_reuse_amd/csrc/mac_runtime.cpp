@@ -32,6 +32,10 @@ struct mac_ctx {
     hipEvent_t ev_attn = nullptr, ev_drain = nullptr;
     hipEvent_t ev_amend[2] = {};     // after the amend of calls of even / odd index
     bool amend_pending[2] = {};
+    // an amend run on the decode stream records no event: a later call on the
+    // same stream is ordered after it anyway, one on another stream records
+    // the event on this stream first (amend_on: that stream, or null)
+    hipStream_t amend_on[2] = {};
     hipEvent_t tm[6] = {};
     bool timed_step = false;
     long long calls = 0;
@@ -217,6 +221,22 @@ mac_status check_view(mac_handle h, const mac_kv_view *kv)
         (!kv->page_table || kv->max_pages_per_req < 1 || kv->num_pages < 1))
         return fail(h, MAC_EINVAL, "paged kv view needs page_table, max_pages_per_req and num_pages");
     return MAC_OK;
+}
+
+// Order `st` after the amend of calls of parity i (when one is pending).
+hipError_t wait_amend(mac_ctx *h, int i, hipStream_t st)
+{
+    if (!h->amend_pending[i])
+        return hipSuccess;
+    if (h->amend_on[i]) {   // ran on a decode stream, no event recorded yet
+        if (h->amend_on[i] == st)
+            return hipSuccess;
+        const hipError_t e = hipEventRecord(h->ev_amend[i], h->amend_on[i]);
+        if (e != hipSuccess)
+            return e;
+        h->amend_on[i] = nullptr;
+    }
+    return hipStreamWaitEvent(st, h->ev_amend[i], 0);
 }
 
 mac::KvView to_view(const mac_ctx *h, const mac_kv_view *kv)
@@ -447,8 +467,7 @@ mac_status mac_reset(mac_handle h)
     if (!h)
         return fail(nullptr, MAC_EINVAL, "handle is NULL");
     for (int i = 0; i < 2; ++i)
-        if (h->amend_pending[i])
-            MAC_HIP(h, hipStreamWaitEvent(h->main_stream, h->ev_amend[i], 0));
+        MAC_HIP(h, wait_amend(h, i, h->main_stream));
     MAC_HIP(h, mac::launch_reset(h->shape, h->st, h->main_stream));
     h->calls = 0;
     h->timed_step = false;
@@ -495,9 +514,7 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
     // calls also work on separate copies of the buffers amend reads.
     const bool stale = h->cfg.flags & MAC_F_STALE_RING;
     const mac::State &S = (stale && cur) ? h->st_odd : h->st;
-    const int wait_ev = stale ? cur : cur ^ 1;
-    if (h->amend_pending[wait_ev])
-        MAC_HIP(h, hipStreamWaitEvent(st, h->ev_amend[wait_ev], 0));
+    MAC_HIP(h, wait_amend(h, stale ? cur : cur ^ 1, st));
     const int hidden = (stale && h->calls > 0) ? (int)((h->calls - 1) % h->cfg.ring_size) : -1;
     if (timing)
         MAC_HIP(h, hipEventRecord(h->tm[0], st));
@@ -540,7 +557,12 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
         MAC_HIP(h, mac::launch_amend(h->shape, S, v, h->kv_fp32, slot_new, as));
         if (timing)
             MAC_HIP(h, hipEventRecord(h->tm[5], as));
-        MAC_HIP(h, hipEventRecord(h->ev_amend[cur], as));
+        if (as != st) {
+            MAC_HIP(h, hipEventRecord(h->ev_amend[cur], as));
+            h->amend_on[cur] = nullptr;
+        } else {
+            h->amend_on[cur] = st;
+        }
         h->amend_pending[cur] = true;
     }
     h->timed_step = timing;
