@@ -150,15 +150,13 @@ __global__ __launch_bounds__(64) void append_kernel(Shape s, State st, KvView kv
 
 // ================================================================== reset
 __global__ void reset_kernel(int32_t *ring_pos, long n_pos, unsigned long long *stats,
-                             long n_stats, int32_t *split_cnt, long n_cnt)
+                             long n_stats)
 {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n_pos)
         ring_pos[i] = -1;
     if (i < n_stats)
         stats[i] = 0ULL;
-    if (i < n_cnt)
-        split_cnt[i] = 0;
 }
 
 template <typename T>
@@ -210,11 +208,9 @@ hipError_t launch_reset(const Shape &s, const State &st, hipStream_t stream)
 {
     const long n = (long)s.B * s.W;
     const long ns = stats_count((long)s.B * s.Hq, (long)s.B * s.Hkv);
-    const long nc = (long)s.B * s.Hq;
-    long tot = n > ns ? n : ns;
-    tot = tot > nc ? tot : nc;
+    const long tot = n > ns ? n : ns;
     hipLaunchKernelGGL(reset_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream,
-                       st.ring_pos, n, st.stats, ns, st.split_cnt, nc);
+                       st.ring_pos, n, st.stats, ns);
     return hipGetLastError();
 }
 

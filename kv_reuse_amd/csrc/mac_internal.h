@@ -19,8 +19,6 @@
 //   partials   [NW + B*Hkv*nseg][G][SUMM] per-(worker, segment) unnormalised summaries
 //   as_full    [B][Hq][SUMM]        AS_{1:m} of this step, input of amend
 //   band       [Hq]    int32        band r_h of each query head
-//   split_buf  [B][Hq][8][2][SUMM]  reduce's per-block summaries of heads it splits
-//   split_cnt  [B][Hq] int32        reduce's arrival counters (back to zero each step)
 //   stats      [MAC_NSTAT] + [B*Hq][HEAD_NSTAT] + [B*Hkv][GRP_NSTAT] uint64 counters
 // With the stale-by-one ring (MAC_F_STALE_RING) q_copy, q_rot, m_buf and
 // as_full are held twice and calls alternate between the copies, so that the
@@ -47,7 +45,6 @@ constexpr int MAX_W = 2048;     // ring slots per (request, head)
 constexpr int TILE_W = 64;      // ring slots one wave scans (the whole ring, or one tile of it)
 constexpr int MAX_GROUPS = 4096;  // B * Hkv
 constexpr int MIN_PAGES_PER_WORKER = 1;
-constexpr int REDUCE_SPLIT = 8;   // reduce blocks per head with a long list of partials
 
 // Counters, one uint64 block: MAC_NSTAT device-wide ones (by atomics: bad
 // input on error paths, the prefill's counts once per block), then
@@ -103,8 +100,6 @@ struct State {
     float *tile_best;         // W > TILE_W: [B*Hq][ceil(W/TILE_W)][3] per-tile nearest (D, pos, slot)
     int32_t n_workers;        // waves in the complete grid
     int32_t slots;            // blocks of the complete grid per CU (dispatch rounds)
-    float *split_buf;         // [B*Hq][RSPLIT][2][SUMM] reduce: per-block summaries of split heads
-    int32_t *split_cnt;       // [B*Hq] reduce: blocks done on a split head (zero between steps)
 };
 
 // Launchers (enqueue only; return the launch status).

@@ -72,13 +72,12 @@ mac_status fail_hip(mac_handle h, const char *what, hipError_t e)
 
 struct Sizes {
     size_t ring_q, ring_s, ring_pos, qvec, m_buf, dec_i, dec_f, grp_parts, partials, as_full,
-        stats, inv_freq, band, split_buf, split_cnt, tiles;
+        stats, inv_freq, band, tiles;
     size_t step_copies;   // copies of the buffers amend reads: 2 with the stale-by-one ring
     size_t total() const
     {
         return ring_q + ring_s + ring_pos + step_copies * (2 * qvec + m_buf + as_full) +
-               3 * dec_i + dec_f + grp_parts + partials + stats + inv_freq + band + split_buf +
-               split_cnt + tiles;
+               3 * dec_i + dec_f + grp_parts + partials + stats + inv_freq + band + tiles;
     }
 };
 
@@ -110,8 +109,6 @@ Sizes sizes_for(const mac_config &c, int n_workers)
                        sizeof(unsigned long long));
     s.inv_freq = round256(mac::D / 2 * sizeof(double));
     s.band = round256(Hq * sizeof(int32_t));
-    s.split_buf = round256(B * Hq * mac::REDUCE_SPLIT * 2 * mac::SUMM * sizeof(float));
-    s.split_cnt = round256(B * Hq * sizeof(int32_t));
     const size_t ntiles = (W + mac::TILE_W - 1) / mac::TILE_W;
     s.tiles = W > (size_t)mac::TILE_W ? round256(B * Hq * ntiles * 3 * sizeof(float)) : 0;
     s.step_copies = (c.flags & MAC_F_STALE_RING) ? 2 : 1;
@@ -399,8 +396,6 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     h->st.grp_stats = h->st.head_stats + (long)cfg->batch * cfg->num_q_heads * mac::HEAD_NSTAT;
     h->st.inv_freq = (const double *)take(sz.inv_freq);
     h->st.band = (const int32_t *)take(sz.band);
-    h->st.split_buf = (float *)take(sz.split_buf);
-    h->st.split_cnt = (int32_t *)take(sz.split_cnt);
     h->st.tile_best = sz.tiles ? (float *)take(sz.tiles) : nullptr;
     h->st_odd = h->st;
     if (sz.step_copies == 2) {

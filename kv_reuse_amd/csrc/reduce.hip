@@ -14,7 +14,9 @@ namespace {
 // long span shares the workers with short ones.  The block is laid out as
 // RLANES partials x RCH float4 column chunks: thread (k, c) folds chunk c of
 // partials k, k + RLANES, ... into an online-softmax state (running max,
-// rescaled sums), RUNROLL partials per round with all their loads in flight;
+// rescaled sums), RUNROLL partials per round with all their loads in flight
+// (RLONG per round while a whole such round is left: a list of thousands
+// takes a handful of round trips, not dozens);
 // the RLANES states are then combined in LDS.
 //
 // Then, per head, with the matched entry's stored prefix S = AS_{1:p-r}
@@ -24,25 +26,11 @@ namespace {
 //                 of this step together with the pre-RoPE query and m;
 //                 O = X (+) band.
 // out receives O's normalised output.
-//
-// When the grid has fewer heads than the GPU has CUs (a small batch), a head
-// whose segments hold more than SPLIT_MIN partials (say one missing head among
-// hits, its span cut over thousands of waves) is folded by gridDim.z = RSPLIT
-// blocks, each over an equal part of the partials.  Each writes its summaries
-// to split_buf, then adds one to the head's counter (agent-scope fence
-// before, so the other XCDs' L2s see the summaries); the block that brings it
-// to RSPLIT (fence after) folds the RSPLIT summaries, finishes the head as
-// above and clears the counter for the next step.  Otherwise block z = 0 does
-// the whole head and the others return at once.  With a block per CU or more
-// already in the grid, splitting measured slower (1097 -> 1102 us at 128K x 16,
-// 101 -> 112 us on its all-hit steps); at batch 1 x 32 heads it takes the
-// reduce from 15.0 to 11.6 us.
 constexpr int REDUCE_THREADS = 1024;
 constexpr int RCH = D / 4;                       // float4 chunks of a row
 constexpr int RLANES = REDUCE_THREADS / RCH;     // partials combined side by side
 constexpr int RUNROLL = 4;                       // partials per round of loads
-constexpr int RSPLIT = REDUCE_SPLIT;             // blocks per head for long partial lists
-constexpr int SPLIT_MIN = 256;                   // partials above which a head is split
+constexpr int RLONG = 8;                        // the same, for long lists
 
 // A summary as threads 0..RCH-1 hold it: normalised output chunk c (o), the
 // reference max M (log2 units) and the normaliser L; EMPTY is (0, -inf, 0).
@@ -71,12 +59,13 @@ __device__ __forceinline__ Sum4 merge(const Sum4 &x, const Sum4 &y)
     return r;
 }
 
-__device__ __forceinline__ void fold(float4 &a, float &L, float &M, const float4 (&ov)[RUNROLL],
-                                     const float (&mv)[RUNROLL], const float (&lv)[RUNROLL], int cnt)
+template <int U>
+__device__ __forceinline__ void fold(float4 &a, float &L, float &M, const float4 (&ov)[U],
+                                     const float (&mv)[U], const float (&lv)[U], int cnt)
 {
     float mn = M;
 #pragma unroll
-    for (int u = 0; u < RUNROLL; ++u)
+    for (int u = 0; u < U; ++u)
         if (u < cnt)
             mn = fmaxf(mn, mv[u]);
     if (mn == NEG_INF)
@@ -89,7 +78,7 @@ __device__ __forceinline__ void fold(float4 &a, float &L, float &M, const float4
     L *= al;
     M = mn;
 #pragma unroll
-    for (int u = 0; u < RUNROLL; ++u) {
+    for (int u = 0; u < U; ++u) {
         if (u < cnt) {
             const float sc = exp2f(mv[u] - mn);
             a.x = fmaf(ov[u].x, sc, a.x);
@@ -123,7 +112,21 @@ __device__ __forceinline__ void combine_partials(const float *part0, int n0, con
     const int n = set == 0 ? n0 : n1;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     float L = 0.f, M = NEG_INF;
-    for (int i = kk; i < n; i += RUNROLL * PER) {
+    int i = kk;
+    for (; i + (RLONG - 1) * PER < n; i += RLONG * PER) {
+        float4 ov[RLONG];
+        float mv[RLONG], lv[RLONG];
+#pragma unroll
+        for (int u = 0; u < RLONG; ++u) {
+            const float *pi = part + (long)(i + u * PER) * pstride;
+            ov[u] = *reinterpret_cast<const float4 *>(pi + 4 * c);
+            const float2 ml = *reinterpret_cast<const float2 *>(pi + D);
+            mv[u] = ml.x;
+            lv[u] = ml.y;
+        }
+        fold<RLONG>(a, L, M, ov, mv, lv, RLONG);
+    }
+    for (; i < n; i += RUNROLL * PER) {
         float4 ov[RUNROLL];
         float mv[RUNROLL], lv[RUNROLL];
         const int cnt = min(RUNROLL, (n - i + PER - 1) / PER);
@@ -136,7 +139,7 @@ __device__ __forceinline__ void combine_partials(const float *part0, int n0, con
                 lv[u] = pi[D + 1];
             }
         }
-        fold(a, L, M, ov, mv, lv, cnt);
+        fold<RUNROLL>(a, L, M, ov, mv, lv, cnt);
     }
     lds.o[k][c] = a;
     if (c == 0) {
@@ -190,9 +193,10 @@ __device__ __forceinline__ void combine_partials(const float *part0, int n0, con
     }
 }
 
-__global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(Shape s, State st,
-                                                                float *__restrict__ out,
-                                                                int slot_new)
+// Five waves per SIMD (at most 102 VGPRs): a CU holds one block and the next
+// one starts while wave 0 of the last finishes its head.
+__global__ __launch_bounds__(REDUCE_THREADS) __attribute__((amdgpu_waves_per_eu(5))) void
+reduce_kernel(Shape s, State st, float *__restrict__ out, int slot_new)
 {
     __shared__ ReduceLds lds;
     const int b = blockIdx.y, h = blockIdx.x, kvh = h / s.G, hh = h % s.G;
@@ -222,71 +226,14 @@ __global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(Shape s, State s
     if (m < 0)
         return;   // idle request: match wrote its zero output, nothing is stored
     const long pstride = (long)s.G * SUMM;   // one slot
-    const int n0 = rg0.y - rg0.x + 1, n1 = rg1.y - rg1.x + 1;
-    const int nsplit = gridDim.z;   // RSPLIT or 1
-    const bool split = nsplit > 1 && n0 + n1 > SPLIT_MIN;
-    const int z = blockIdx.z;
-    if (!split && z > 0)
-        return;
-    // this block's part of each set: all of it, or the z-th of RSPLIT parts
-    const int a0 = split ? (int)((long)z * n0 / nsplit) : 0;
-    const int e0 = split ? (int)((long)(z + 1) * n0 / nsplit) : n0;
-    const int a1 = split ? (int)((long)z * n1 / nsplit) : 0;
-    const int e1 = split ? (int)((long)(z + 1) * n1 / nsplit) : n1;
-    const float *p0 = st.partials + ((long)rg0.x + a0 + seg0) * pstride + hh * SUMM;
+    const float *p0 = st.partials + ((long)rg0.x + seg0) * pstride + hh * SUMM;
     Sum4 part0, part1;
     if (s.nseg == 2)
-        combine_partials<2>(p0, e0 - a0,
-                            st.partials + ((long)rg1.x + a1 + seg0 + 1) * pstride + hh * SUMM,
-                            e1 - a1, pstride, lds, part0, part1);
+        combine_partials<2>(p0, rg0.y - rg0.x + 1,
+                            st.partials + ((long)rg1.x + seg0 + 1) * pstride + hh * SUMM,
+                            rg1.y - rg1.x + 1, pstride, lds, part0, part1);
     else
-        combine_partials<1>(p0, e0 - a0, nullptr, 0, pstride, lds, part0, part1);
-    if (t >= 64)
-        return;
-    if (split) {
-        // wave 0 alone from here: publish this block's summaries, count in
-        float *mine = st.split_buf + ((idx * RSPLIT + z) * 2) * SUMM;
-        if (t < RCH) {
-            *reinterpret_cast<float4 *>(mine + 4 * c) = part0.o;
-            *reinterpret_cast<float4 *>(mine + SUMM + 4 * c) = part1.o;
-            if (t == 0) {
-                mine[D] = part0.M;
-                mine[D + 1] = part0.L;
-                mine[SUMM + D] = part1.M;
-                mine[SUMM + D + 1] = part1.L;
-            }
-        }
-        __threadfence();
-        int prior = 0;
-        if (t == 0)
-            prior = atomicAdd(&st.split_cnt[idx], 1);
-        prior = __shfl(prior, 0, 64);
-        if (prior != nsplit - 1)
-            return;   // another block finishes this head
-        __threadfence();
-        if (t < RCH) {
-            Sum4 x0, x1;
-            x0.o = x1.o = make_float4(0.f, 0.f, 0.f, 0.f);
-            x0.M = x1.M = NEG_INF;
-            x0.L = x1.L = 0.f;
-            for (int q = 0; q < nsplit; ++q) {
-                const float *o = st.split_buf + ((idx * RSPLIT + q) * 2) * SUMM;
-                Sum4 y0, y1;
-                y0.o = *reinterpret_cast<const float4 *>(o + 4 * c);
-                y0.M = o[D];
-                y0.L = o[D + 1];
-                y1.o = *reinterpret_cast<const float4 *>(o + SUMM + 4 * c);
-                y1.M = o[SUMM + D];
-                y1.L = o[SUMM + D + 1];
-                x0 = merge(x0, y0);
-                x1 = merge(x1, y1);
-            }
-            part0 = x0;
-            part1 = x1;
-        }
-        if (t == 0)
-            st.split_cnt[idx] = 0;   // ready for the next step
-    }
+        combine_partials<1>(p0, rg0.y - rg0.x + 1, nullptr, 0, pstride, lds, part0, part1);
     if (t >= RCH)
         return;
     Sum4 O;
@@ -328,10 +275,8 @@ hipError_t launch_reduce(const Shape &s, const State &st, float *out, int slot_n
 {
     if (!supported_group(s.G) || s.nseg < 1 || s.nseg > 2)
         return hipErrorInvalidValue;
-    const int n_cu = st.n_workers / (WAVES * (st.slots > 0 ? st.slots : 1));
-    const int nsplit = (long)s.B * s.Hq < n_cu ? RSPLIT : 1;
-    hipLaunchKernelGGL(reduce_kernel, dim3(s.Hq, s.B, nsplit), dim3(REDUCE_THREADS), 0, stream, s,
-                       st, out, slot_new);
+    hipLaunchKernelGGL(reduce_kernel, dim3(s.Hq, s.B), dim3(REDUCE_THREADS), 0, stream, s, st,
+                       out, slot_new);
     return hipGetLastError();
 }
 
