@@ -30,90 +30,81 @@ __device__ __forceinline__ int query_position(const KvView &kv, int seq, bool &b
     return bad ? -1 : m;
 }
 
-// Scan slots [base, base + nslot) (nslot <= 64) of one head's ring with one
-// wave: each 1 KB wave load covers two slots (lanes 0-31 and 32-63, four
-// columns each), the squared differences are summed over each half, and every
-// lane of a half keeps the nearest valid entry it has seen.  Loads are issued
-// eight at a time; indices past the tile are clamped to its last slot
-// (in-bounds re-reads whose distances are discarded).  qv holds columns
-// 4c .. 4c+3 of the pre-RoPE query (c = lane % 32); pos_l is the stamp of slot
-// base + lane.  Returns the nearest entry over the whole tile (wave-uniform).
-__device__ __forceinline__ void scan_tile(const float4 *rq, int base, int nslot, float4 qv,
-                                          int pos_l, int m, float &kd, int &kp, int &kj)
-{
-    const int lane = lane_id(), half = lane >> 5, c = lane & 31;
-    kd = INFINITY;
-    kp = INT_MIN;
-    kj = -1;
-    for (int i = 0; i < nslot; i += 16) {
-        float4 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int sl = min(i + 2 * u + half, nslot - 1);
-            v[u] = rq[(long)sl * (D / 4) + c];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int sl = i + 2 * u + half;
-            const float t0 = qv.x - v[u].x, t1 = qv.y - v[u].y, t2 = qv.z - v[u].z,
-                        t3 = qv.w - v[u].w;
-            float d = t0 * t0;
-            d = fmaf(t1, t1, d);
-            d = fmaf(t2, t2, d);
-            d = fmaf(t3, t3, d);
-            d = half_sum(d);
-            const int pos = __shfl(pos_l, sl & 63, 64);
-            const bool valid = sl < nslot && pos >= 0 && pos <= m;
-            if (valid && nearer(d, pos, base + sl, kd, kp, kj)) {
-                kd = d;
-                kp = pos;
-                kj = base + sl;
-            }
-        }
-    }
-    // the two halves saw different slots
-    const float d2 = xor_lanes<32>(kd);
-    const int p2 = xor_lanes_i<32>(kp);
-    const int j2 = xor_lanes_i<32>(kj);
-    if (nearer(d2, p2, j2, kd, kp, kj)) {
-        kd = d2;
-        kp = p2;
-        kj = j2;
-    }
-}
+// One wave holds up to SLOTS (16, 32 or 64) ring slots of one head in
+// registers, loaded in a single round: with fp32 queries each 1 KB wave load
+// covers two slots (lanes 0-31 and 32-63, four columns each), with bf16
+// queries four (lanes 16j .. 16j+15 hold one slot, eight columns each).  Slots
+// past nslot are not loaded (zero).  The loads do not depend on the query position,
+// so the match kernel issues them with its other loads.
+template <int SLOTS, bool BF16>
+struct RingTile {
+    static constexpr int PER = BF16 ? 4 : 2;   // slots per wave load
+    static constexpr int NL = SLOTS / PER;
+    using Vec = typename std::conditional<BF16, uint4, float4>::type;
+    Vec v[NL];
 
-// The same scan over a ring of bf16 queries: a slot is 256 bytes, so one
-// 1 KB wave load covers four slots (lanes 16j .. 16j+15 hold slot 4u + j,
-// eight columns each) and the squared differences are summed over each
-// 16-lane row with DPP.  q8 holds columns 8c .. 8c+7 of the query
-// (c = lane % 16).
-__device__ __forceinline__ void scan_tile_bf16(const uint4 *rq, int base, int nslot,
-                                               const float (&q8)[8], int pos_l, int m, float &kd,
-                                               int &kp, int &kj)
-{
-    const int lane = lane_id(), sub = lane >> 4, c = lane & 15;
-    kd = INFINITY;
-    kp = INT_MIN;
-    kj = -1;
-    for (int i = 0; i < nslot; i += 32) {
-        uint4 v[8];
+    // slots [base, base + nslot) of head idx
+    __device__ __forceinline__ void load(const Shape &s, const State &st, long idx, int base,
+                                         int nslot)
+    {
+        const int lane = lane_id();
+        const long row = (idx * s.W + base) * D;
+        const int sub = lane / (64 / PER), c = lane % (64 / PER);
+        const Vec *rq = BF16 ? reinterpret_cast<const Vec *>(
+                                   static_cast<const uint16_t *>(st.ring_q) + row)
+                             : reinterpret_cast<const Vec *>(
+                                   static_cast<const float *>(st.ring_q) + row);
+        constexpr int VPR = BF16 ? D / 8 : D / 4;   // vectors per slot
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int sl = min(i + 4 * u + sub, nslot - 1);
-            v[u] = rq[(long)sl * (D / 8) + c];
+        for (int u = 0; u < NL; ++u) {
+            const int sl = PER * u + sub;
+            v[u] = sl < nslot ? rq[(long)sl * VPR + c] : Vec{};
         }
+    }
+
+    // Nearest valid entry of the loaded slots (wave-uniform result): squared
+    // L2 distance to the pre-RoPE query qsrc, summed over each slot's lanes;
+    // pos_l is the stamp of slot base + lane; valid stamps are 0 .. m.
+    __device__ __forceinline__ void scan(const float *qsrc, int base, int nslot, int pos_l, int m,
+                                         float &kd, int &kp, int &kj) const
+    {
+        const int lane = lane_id();
+        const int sub = lane / (64 / PER), c = lane % (64 / PER);
+        float q[8];
+        if constexpr (BF16) {
+            const float4 a = reinterpret_cast<const float4 *>(qsrc)[2 * c];
+            const float4 b = reinterpret_cast<const float4 *>(qsrc)[2 * c + 1];
+            q[0] = a.x, q[1] = a.y, q[2] = a.z, q[3] = a.w;
+            q[4] = b.x, q[5] = b.y, q[6] = b.z, q[7] = b.w;
+        } else {
+            const float4 a = reinterpret_cast<const float4 *>(qsrc)[c];
+            q[0] = a.x, q[1] = a.y, q[2] = a.z, q[3] = a.w;
+        }
+        kd = INFINITY;
+        kp = INT_MIN;
+        kj = -1;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int sl = i + 4 * u + sub;
-            float f[8];
-            to_f32(v[u], f);
+        for (int u = 0; u < NL; ++u) {
+            const int sl = PER * u + sub;
             float d = 0.f;
+            if constexpr (BF16) {
+                float f[8];
+                to_f32(v[u], f);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float t = q8[e] - f[e];
-                d = fmaf(t, t, d);
+                for (int e = 0; e < 8; ++e) {
+                    const float t = q[e] - f[e];
+                    d = fmaf(t, t, d);
+                }
+                d = row16_sum(d);
+            } else {
+                const float t0 = q[0] - v[u].x, t1 = q[1] - v[u].y, t2 = q[2] - v[u].z,
+                            t3 = q[3] - v[u].w;
+                d = t0 * t0;
+                d = fmaf(t1, t1, d);
+                d = fmaf(t2, t2, d);
+                d = fmaf(t3, t3, d);
+                d = half_sum(d);
             }
-            d = row16_sum(d);
             const int pos = __shfl(pos_l, sl & 63, 64);
             const bool valid = sl < nslot && pos >= 0 && pos <= m;
             if (valid && nearer(d, pos, base + sl, kd, kp, kj)) {
@@ -122,47 +113,35 @@ __device__ __forceinline__ void scan_tile_bf16(const uint4 *rq, int base, int ns
                 kj = base + sl;
             }
         }
-    }
-    // the four rows saw different slots
-#pragma unroll
-    for (int off = 16; off <= 32; off *= 2) {
-        const float d2 = off == 16 ? xor_lanes<16>(kd) : xor_lanes<32>(kd);
-        const int p2 = off == 16 ? xor_lanes_i<16>(kp) : xor_lanes_i<32>(kp);
-        const int j2 = off == 16 ? xor_lanes_i<16>(kj) : xor_lanes_i<32>(kj);
+        // the lane groups saw different slots
+        if constexpr (BF16) {
+            const float d2 = xor_lanes<16>(kd);
+            const int p2 = xor_lanes_i<16>(kp);
+            const int j2 = xor_lanes_i<16>(kj);
+            if (nearer(d2, p2, j2, kd, kp, kj)) {
+                kd = d2;
+                kp = p2;
+                kj = j2;
+            }
+        }
+        const float d2 = xor_lanes<32>(kd);
+        const int p2 = xor_lanes_i<32>(kp);
+        const int j2 = xor_lanes_i<32>(kj);
         if (nearer(d2, p2, j2, kd, kp, kj)) {
             kd = d2;
             kp = p2;
             kj = j2;
         }
     }
-}
-
-// Nearest valid entry among ring slots [base, base + nslot) of head idx, in
-// whichever form the ring stores its queries.  qsrc: the head's pre-RoPE query.
-__device__ __forceinline__ void scan_ring_tile(const Shape &s, const State &st, long idx, int base,
-                                               int nslot, const float *qsrc, int pos_l, int m,
-                                               float &kd, int &kp, int &kj)
-{
-    const int lane = lane_id();
-    const long row = (idx * s.W + base) * D;
-    if (s.ring_bf16) {
-        const float4 a = reinterpret_cast<const float4 *>(qsrc)[2 * (lane & 15)];
-        const float4 b = reinterpret_cast<const float4 *>(qsrc)[2 * (lane & 15) + 1];
-        const float q8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        scan_tile_bf16(reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(st.ring_q) + row),
-                       base, nslot, q8, pos_l, m, kd, kp, kj);
-    } else {
-        const float4 qv = reinterpret_cast<const float4 *>(qsrc)[lane & 31];
-        scan_tile(reinterpret_cast<const float4 *>(static_cast<const float *>(st.ring_q) + row),
-                  base, nslot, qv, pos_l, m, kd, kp, kj);
-    }
-}
+};
 
 // =========================================================== match tiles
 // Rings longer than one 64-slot tile (the pages' windows of 512-2048 entries,
 // Figure 6, Tables 5 and 7).  Grid (tiles, Hq, B), one wave per tile: the
-// wave streams the tile's 64 pre-RoPE queries (32 KB) and records the tile's
-// nearest entry; the match kernel then reduces the tiles of each head.
+// wave loads the tile's 64 pre-RoPE queries (32 KB fp32, 16 KB bf16) and
+// records the tile's nearest entry; the match kernel then reduces the tiles
+// of each head.
+template <bool BF16>
 __global__ __launch_bounds__(64) void match_tiles_kernel(Shape s, State st, KvView kv,
                                                          const int32_t *__restrict__ seq_lens,
                                                          const float *__restrict__ q_pre,
@@ -174,14 +153,17 @@ __global__ __launch_bounds__(64) void match_tiles_kernel(Shape s, State st, KvVi
     const int lane = lane_id();
     const int base = tile * TILE_W;
     const int nslot = min(TILE_W, s.W - base);
-    bool bad;
-    const int m = query_position(kv, seq_lens[b], bad);
+    RingTile<TILE_W, BF16> ring;
+    ring.load(s, st, idx, base, nslot);
+    const int seq = seq_lens[b];
     const int pos_l = (lane < nslot && base + lane != hidden)
                           ? st.ring_pos[(long)b * s.W + base + lane]
                           : -1;
+    bool bad;
+    const int m = query_position(kv, seq, bad);
     float kd;
     int kp, kj;
-    scan_ring_tile(s, st, idx, base, nslot, q_pre + idx * D, pos_l, m, kd, kp, kj);
+    ring.scan(q_pre + idx * D, base, nslot, pos_l, m, kd, kp, kj);
     if (lane == 0) {
         float *o = st.tile_best + (idx * ntiles + tile) * 3;
         o[0] = kd;
@@ -192,7 +174,7 @@ __global__ __launch_bounds__(64) void match_tiles_kernel(Shape s, State st, KvVi
 
 // ================================================================== match
 // Grid (Hq, B), one wave per (request, query head).  A ring of up to 64
-// entries is scanned in registers (scan_tile); a longer one arrives as
+// entries is held in registers (RingTile); a longer one arrives as
 // per-tile nearest entries from match_tiles_kernel.  The kernel is
 // latency-bound, so every load that does not depend on the query position
 // (query, angles, ring, stamps, override, the head's counters) is issued
@@ -201,6 +183,7 @@ __global__ __launch_bounds__(64) void match_tiles_kernel(Shape s, State st, KvVi
 // squared), applies an override, rotates its query (rotate-half RoPE, angle in
 // fp64) and records its key span: [max(p - r + 1, 0), m] on a hit, [0, m] on
 // a miss.
+template <int SLOTS, bool BF16>
 __global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
                                                    const int32_t *__restrict__ seq_lens,
                                                    const float *__restrict__ q_pre,
@@ -215,6 +198,9 @@ __global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
     unsigned long long *hstat = st.head_stats + idx * HEAD_NSTAT;
 
     // ---- loads independent of the position
+    RingTile<SLOTS, BF16> ring;
+    if (s.reuse && !tiled)
+        ring.load(s, st, idx, 0, s.W);
     const int seq = seq_lens[b];
     const float qa = q_pre[idx * D + lane], qb = q_pre[idx * D + lane + 64];
     const double inv = st.inv_freq[lane];
@@ -259,7 +245,7 @@ __global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
         float kd;
         int kp, kj;
         if (!tiled) {
-            scan_ring_tile(s, st, idx, 0, s.W, q_pre + idx * D, pos_l, m, kd, kp, kj);
+            ring.scan(q_pre + idx * D, 0, s.W, pos_l, m, kd, kp, kj);
         } else {
             // nearest entry over the head's tiles
             kd = td;
@@ -345,8 +331,12 @@ hipError_t launch_match_tiles(const Shape &s, const State &st, const KvView &kv,
                               hipStream_t stream)
 {
     const dim3 grid((s.W + TILE_W - 1) / TILE_W, s.Hq, s.B);
-    hipLaunchKernelGGL(match_tiles_kernel, grid, dim3(64), 0, stream, s, st, kv, seq_lens, q_pre,
-                       hidden);
+    if (s.ring_bf16)
+        hipLaunchKernelGGL(match_tiles_kernel<true>, grid, dim3(64), 0, stream, s, st, kv,
+                           seq_lens, q_pre, hidden);
+    else
+        hipLaunchKernelGGL(match_tiles_kernel<false>, grid, dim3(64), 0, stream, s, st, kv,
+                           seq_lens, q_pre, hidden);
     return hipGetLastError();
 }
 
@@ -354,8 +344,29 @@ hipError_t launch_match(const Shape &s, const State &st, const KvView &kv, const
                         const float *q_pre, const int32_t *override_pos, float *out, int hidden,
                         hipStream_t stream)
 {
-    hipLaunchKernelGGL(match_kernel, dim3(s.Hq, s.B), dim3(64), 0, stream, s, st, kv, seq_lens,
-                       q_pre, override_pos, out, hidden);
+    // ring slots held in registers: the whole ring up to 64 (a longer one is
+    // read by match_tiles_kernel)
+    const int slots = s.W > 32 ? 64 : s.W > 16 ? 32 : 16;
+    const dim3 grid(s.Hq, s.B);
+#define MAC_MATCH(SL, BF)                                                                      \
+    hipLaunchKernelGGL((match_kernel<SL, BF>), grid, dim3(64), 0, stream, s, st, kv, seq_lens,  \
+                       q_pre, override_pos, out, hidden)
+    if (s.ring_bf16) {
+        if (slots == 16)
+            MAC_MATCH(16, true);
+        else if (slots == 32)
+            MAC_MATCH(32, true);
+        else
+            MAC_MATCH(64, true);
+    } else {
+        if (slots == 16)
+            MAC_MATCH(16, false);
+        else if (slots == 32)
+            MAC_MATCH(32, false);
+        else
+            MAC_MATCH(64, false);
+    }
+#undef MAC_MATCH
     return hipGetLastError();
 }
 
