@@ -168,10 +168,11 @@ def loop_us(w, flags, cache, q_dev, k_rows, v_rows, warmup, steps, hit_rate=None
 
 
 def speedup_point(name, steps=24, warmup=40):
-    """MAC attention phase vs the in-house full-attention kernel on one workload,
-    with a 1 GiB scrub read before every step (the KV of small contexts fits in
-    the 256 MB Infinity Cache).  The attention phase is timed by stream events
-    around the decode call, so the scrub is not in it."""
+    """MAC attention phase (async, fused and decode-stream amend) vs the in-house
+    full-attention kernel on one workload, with a 1 GiB scrub read before every
+    step (the KV of small contexts fits in the 256 MB Infinity Cache).  The
+    attention phase is timed by stream events around the decode call, so the
+    scrub is not in it."""
     import torch
     import kv_reuse_amd as mac
     from workloads import get_config, kv_logical, page_table, queries, to_paged
@@ -191,7 +192,9 @@ def speedup_point(name, steps=24, warmup=40):
     scrub = [torch.ones(1 << 28, dtype=torch.float32, device="cuda"),
              torch.zeros((), dtype=torch.float32, device="cuda")]
     res = {}
-    for label, flags in (("mac", 0), ("full", mac.MAC_F_DISABLE_REUSE)):
+    for label, flags in (("mac", 0), ("mac_fused_amend", mac.MAC_F_FUSED_AMEND),
+                         ("mac_sync_amend", mac.MAC_F_SYNC_AMEND),
+                         ("full", mac.MAC_F_DISABLE_REUSE)):
         bn = Bench(w, flags, kc, vc, paged, table)
         att, hits = [], []
         prev = None
@@ -206,6 +209,11 @@ def speedup_point(name, steps=24, warmup=40):
     return {"workload": name, "context": w.C, "batch": w.B,
             "mac_attention_us": res["mac"][0], "full_attention_us": res["full"][0],
             "head_hit_rate": res["mac"][1], "speedup": res["full"][0] / res["mac"][0],
+            # the other amend forms: no second stream, so no cross-queue event
+            # after the reduce (sync: amend runs inside the span)
+            "mac_fused_amend_attention_us": res["mac_fused_amend"][0],
+            "mac_sync_amend_attention_us": res["mac_sync_amend"][0],
+            "speedup_fused_amend": res["full"][0] / res["mac_fused_amend"][0],
             "steps": steps, "warmup": warmup}
 
 
