@@ -1,0 +1,108 @@
+"""GPU parity over a seeded random sweep of configurations.
+
+Each case draws its shape and options together (batch, GQA layout, ragged
+prefill lengths, ring length on both sides of the 64-slot tile, band or
+per-head bands, AR(1) rho and a tau near the nearest entry's distance, KV
+dtype and layout, and a mix of the option flags the library accepts
+together), so that combinations the hand-picked cases do not name are
+exercised too.  The bar is the one of every parity
+case: decisions bit-exact, outputs within max-abs 2e-3 and per-row relative
+1e-2 of the fp64 oracle.  The draw is fixed (seed 2026), so a failure names
+a reproducible case.
+"""
+import numpy as np
+import pytest
+
+from workloads import get_config, scaled
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 24
+_OPTS = [(), ("fused",), ("stale",), ("ring_bf16",), ("sync",), ("unbalanced",),
+         ("fused", "ring_bf16"), ("stale", "sync"), ("fused", "unbalanced"), ("sync", "ring_bf16"),
+         ("stale", "unbalanced"), ("fused", "sync")]
+_GQA = [(8, 8), (8, 4), (16, 4), (8, 2), (32, 8), (16, 2), (8, 1), (32, 4)]
+_W = [1, 3, 16, 32, 48, 64, 100, 200]
+_R = [1, 16, 64, 300]
+
+
+def _draw(i, rng):
+    Hq, Hkv = _GQA[rng.integers(len(_GQA))]
+    G = Hq // Hkv
+    B = int(rng.choice([1, 2, 3, 5]))
+    C = int(rng.integers(40, 2500))
+    steps = int(rng.integers(12, 25))
+    W = int(rng.choice(_W))
+    r = int(rng.choice(_R))
+    rho = float(rng.uniform(0.93, 0.995))
+    kv = "fp32" if rng.random() < 0.3 else "bf16"
+    layout = "paged" if rng.random() < 0.6 else "contiguous"
+    # the option set cycles with the case index, so every flag is in the sweep
+    opts = _OPTS[i % len(_OPTS)]
+    fused, stale = "fused" in opts, "stale" in opts
+    ring_bf16 = "ring_bf16" in opts or rng.random() < 0.2
+    sync = "sync" in opts
+    unbalanced = "unbalanced" in opts or rng.random() < 0.15
+    # tau around the AR(1) walk's distance to the nearest visible entry
+    # (sqrt(2(1 - rho)) one step back, sqrt(2) times that two steps back with
+    # the stale ring), so that most cases mix hits and misses
+    tau = round(float(rng.uniform(0.85, 1.4)) * np.sqrt(2 * (1 - rho)) * (np.sqrt(2) if stale else 1), 3)
+    bands = None
+    if rng.random() < 0.3:
+        per_group = rng.choice(_R, size=Hkv)
+        bands = [int(x) for x in np.repeat(per_group, G)]
+        if not fused:   # a separate amend takes any band per head
+            bands = [int(x) for x in rng.choice(_R, size=Hq)]
+    # ragged prefill: every request at most C tokens, at least one token
+    prefill = [int(x) for x in rng.integers(max(1, C // 3), C + 1, size=B)]
+    return dict(i=i, B=B, Hq=Hq, Hkv=Hkv, C=C, steps=steps, W=W, r=r, tau=tau, rho=rho, kv=kv,
+                layout=layout, fused=fused, stale=stale, ring_bf16=ring_bf16, sync=sync,
+                unbalanced=unbalanced, bands=bands, prefill=prefill)
+
+
+def _cases():
+    rng = np.random.default_rng(2026)
+    return [_draw(i, rng) for i in range(N_CASES)]
+
+
+_CASES = _cases()
+
+
+def _case_id(c):
+    opts = [k for k in ("fused", "stale", "ring_bf16", "sync", "unbalanced") if c[k]]
+    return "c%02d-B%d-%dq%dkv-W%d-r%s-%s-%s%s" % (
+        c["i"], c["B"], c["Hq"], c["Hkv"], c["W"], "ph" if c["bands"] else c["r"], c["kv"],
+        c["layout"][:4], ("-" + "+".join(opts)) if opts else "")
+
+
+@pytest.mark.parametrize("case", _CASES, ids=[_case_id(c) for c in _CASES])
+def test_random_configuration(gpu_lib, case):
+    import kv_reuse_amd as mac
+    import oracle
+    from gpu_harness import Lockstep
+    c = case
+    w = scaled(get_config("b16_128k"), name="sweep%02d" % c["i"], B=c["B"], Hq=c["Hq"],
+               Hkv=c["Hkv"], C=c["C"], steps=c["steps"], W=c["W"], r=c["r"], tau=c["tau"],
+               rho=("const", c["rho"]), kv=c["kv"], layout=c["layout"], seed=100 + c["i"])
+    flags = ((mac.MAC_F_FUSED_AMEND if c["fused"] else 0) |
+             (mac.MAC_F_STALE_RING if c["stale"] else 0) |
+             (mac.MAC_F_RING_BF16 if c["ring_bf16"] else 0) |
+             (mac.MAC_F_UNBALANCED_PLAN if c["unbalanced"] else 0))
+    oflags = ((oracle.F_STALE_RING if c["stale"] else 0) |
+              (oracle.F_RING_BF16 if c["ring_bf16"] else 0))
+    print("case", _case_id(c), "C", c["C"], "steps", c["steps"], "tau", c["tau"],
+          "rho %.4f" % c["rho"], "prefill", c["prefill"], "bands", c["bands"], flush=True)
+    ls = Lockstep(w, flags=flags, oracle_flags=oflags, sync_amend=c["sync"],
+                  prefill=c["prefill"], bands=c["bands"])
+    hits = forced = 0
+    try:
+        for t in range(c["steps"]):
+            info = ls.step(t)
+            hits += info["hits"]
+            forced += info["forced"]
+    finally:
+        ls.close()
+    emax = max(e for e, _ in ls.stats)
+    rmax = max(r for _, r in ls.stats)
+    print("  hits", hits, "of", c["steps"] * c["B"] * c["Hq"], "forced", forced,
+          "max-abs %.2e row-rel %.2e" % (emax, rmax), flush=True)
