@@ -68,7 +68,10 @@ enum {
      * the band [m-r+1, m], and the reduce forms AS_{1:m-r} as the stored
      * prefix merged with the part before the band and writes the ring entry
      * itself: no band re-read, no log-domain removal, no amend stream work.
-     * Same results up to rounding. */
+     * Same results up to rounding.  Where a step is short (a small batch) it
+     * is the fast form: the default hands each call's amend to the second
+     * stream through a cross-queue event, which costs tens of microseconds of
+     * host time per call on this runtime. */
     MAC_F_FUSED_AMEND = 16u,
     /* Keep the ring's pre-RoPE queries as bfloat16 (rounded to nearest, ties
      * to even) and match against those: half the match traffic, ~6x a token's
