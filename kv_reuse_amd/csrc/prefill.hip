@@ -94,16 +94,20 @@ __global__ __launch_bounds__(64 * ROW_WAVES) void prefill_rope_kernel(
 
 // =================================================================== match
 // Grid (ceil(N/64), Hq, B), 4 waves: lane l of every wave holds the query of
-// token 64 * tile + l in registers, and wave w scans candidates j = w, w + 4,
-// ... (the pre-RoPE queries of earlier tokens, rounded to bf16 with
-// MAC_F_RING_BF16).  A candidate row is the same for every lane, so it comes
-// through the scalar cache a quarter row at a time and enters the distance
-// as scalar operands, with no LDS traffic.  Distances are direct fp32 sums of
-// squared differences: the Gram form |a|^2 + |b|^2 - 2 a.b would lose about
-// 1e-5 of the distance to cancellation for the nearest rows, the size of the
-// near-tie margin.  The four partial winners of a token are then combined
-// (smaller distance, then the later token).
+// token 64 * tile + l in registers.  The candidates (the pre-RoPE queries of
+// earlier tokens, rounded to bf16 with MAC_F_RING_BF16) pass through LDS in
+// chunks of PFM_CHUNK rows, double-buffered: the block loads chunk c + 1 into
+// registers while its waves scan chunk c, wave w taking rows w, w + 4, ...; a
+// candidate row is the same for every lane, so its reads are LDS broadcasts.
+// (Rows read straight through the scalar cache ran at ~40 % of the VALU
+// rate: each quarter row waited on its scalar loads.)  Distances are direct
+// fp32 sums of squared differences: the Gram form |a|^2 + |b|^2 - 2 a.b would
+// lose about 1e-5 of the distance to cancellation for the nearest rows, the
+// size of the near-tie margin.  The four partial winners of a token are then
+// combined (smaller distance, then the later token).
 constexpr int PFM_WAVES = 4;
+constexpr int PFM_CHUNK = 16;                          // candidate rows per LDS stage
+constexpr int PFM_LOADS = PFM_CHUNK * (D / 4) / (64 * PFM_WAVES);   // float4 per thread
 
 template <bool BF16>
 __global__ __launch_bounds__(64 * PFM_WAVES) void prefill_match_kernel(
@@ -112,6 +116,7 @@ __global__ __launch_bounds__(64 * PFM_WAVES) void prefill_match_kernel(
 {
     __shared__ float bd[PFM_WAVES][64];
     __shared__ int bjs[PFM_WAVES][64];
+    __shared__ float4 rows[2][PFM_CHUNK][D / 4];
     const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     bool bad;
@@ -137,37 +142,68 @@ __global__ __launch_bounds__(64 * PFM_WAVES) void prefill_match_kernel(
     float best = INFINITY;
     int bj = -1;
     if (s.reuse) {
-        // candidate rows are wave-uniform: read through the scalar cache
+        // candidates 0 .. jend: every earlier token of the tile's last token
         const int jend = min(t0 + 63, n - 1);
-        for (int j = wv; j <= jend; j += PFM_WAVES) {
-            const float4 *crow = reinterpret_cast<const float4 *>(
-                q_pre + row3(pf, s.Hq, b, j, h) * D);
-            // four partial sums (one per float4 component) break the chain
-            // of dependent fmas; their order of addition is fixed
-            float da = 0.f, db = 0.f, dc = 0.f, dd = 0.f;
+        const int nch = (jend + PFM_CHUNK) / PFM_CHUNK;
+        float4 pre[PFM_LOADS];
+        // thread x moves float4 x, x + 256, ... of a chunk (row e / 32, column e % 32)
+        auto gload = [&](int c) {
 #pragma unroll
-            for (int k = 0; k < D / 4; ++k) {
-                if (k % 8 == 0 && k)
-                    __builtin_amdgcn_sched_barrier(0);   // keep a quarter row in SGPRs
-                float4 c = crow[k];
+            for (int i = 0; i < PFM_LOADS; ++i) {
+                const int e = threadIdx.x + i * 64 * PFM_WAVES;
+                const int j = c * PFM_CHUNK + e / (D / 4);
+                pre[i] = j <= jend ? reinterpret_cast<const float4 *>(
+                                         q_pre + row3(pf, s.Hq, b, j, h) * D)[e % (D / 4)]
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        };
+        auto lstore = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < PFM_LOADS; ++i) {
+                const int e = threadIdx.x + i * 64 * PFM_WAVES;
+                float4 c = pre[i];
                 if constexpr (BF16) {
                     c.x = __uint_as_float(bf16_rne_bits(c.x) << 16);
                     c.y = __uint_as_float(bf16_rne_bits(c.y) << 16);
                     c.z = __uint_as_float(bf16_rne_bits(c.z) << 16);
                     c.w = __uint_as_float(bf16_rne_bits(c.w) << 16);
                 }
-                const float a = q[k].x - c.x, bq = q[k].y - c.y, cq = q[k].z - c.z,
-                            dq = q[k].w - c.w;
-                da = fmaf(a, a, da);
-                db = fmaf(bq, bq, db);
-                dc = fmaf(cq, cq, dc);
-                dd = fmaf(dq, dq, dd);
+                rows[buf][e / (D / 4)][e % (D / 4)] = c;
             }
-            const float d2 = (da + db) + (dc + dd);
-            if (j < t && d2 <= best) {
-                best = d2;
-                bj = j;
+        };
+        gload(0);
+        lstore(0);
+        __syncthreads();
+        for (int c = 0; c < nch; ++c) {
+            if (c + 1 < nch)
+                gload(c + 1);   // in flight while this chunk is scanned
+            const int cur = c & 1;
+            for (int r = wv; r < PFM_CHUNK; r += PFM_WAVES) {
+                const int j = c * PFM_CHUNK + r;
+                if (j > jend)
+                    break;
+                // four partial sums (one per float4 component) break the chain
+                // of dependent fmas; their order of addition is fixed
+                float da = 0.f, db = 0.f, dc = 0.f, dd = 0.f;
+#pragma unroll
+                for (int k = 0; k < D / 4; ++k) {
+                    const float4 cv = rows[cur][r][k];
+                    const float a = q[k].x - cv.x, bq = q[k].y - cv.y, cq = q[k].z - cv.z,
+                                dq = q[k].w - cv.w;
+                    da = fmaf(a, a, da);
+                    db = fmaf(bq, bq, db);
+                    dc = fmaf(cq, cq, dc);
+                    dd = fmaf(dq, dq, dd);
+                }
+                const float d2 = (da + db) + (dc + dd);
+                if (j < t && d2 <= best) {
+                    best = d2;
+                    bj = j;
+                }
             }
+            if (c + 1 < nch)
+                lstore(cur ^ 1);   // every wave left that buffer at the last barrier
+            __syncthreads();
         }
     }
     bd[wv][lane] = best;
@@ -582,7 +618,8 @@ hipError_t launch_prefill(const Shape &s, const State &st, const KvView &kv, boo
                        seq_lens);
     float *si = pf.sa, *so = pf.sb;
     int32_t *pi = pf.pa, *po = pf.pb;
-    for (int span = 1; span < N; span *= 2) {   // ceil(log2 N) rounds
+    // ceil(log2 N) rounds; none with reuse off, where no token has a parent
+    for (int span = 1; s.reuse && span < N; span *= 2) {
         hipLaunchKernelGGL(prefill_chain_step_kernel, per_row, row_block, 0, stream, s, pf, si,
                            pi, so, po);
         float *ts = si;
