@@ -204,3 +204,44 @@ def test_prefill_host_checks(gpu_lib):
         assert ei.value.status == mac.MAC_EINVAL
     finally:
         layer.close()
+
+
+def _prefill_draw(i, rng):
+    gqa = [(8, 8), (8, 4), (16, 4), (8, 2), (32, 8), (8, 1), (32, 4)]
+    Hq, Hkv = gqa[rng.integers(len(gqa))]
+    B = int(rng.choice([1, 2, 3]))
+    N = int(rng.integers(17, 500))
+    rho = float(rng.uniform(0.93, 0.995))
+    bands = None
+    if rng.random() < 0.3:
+        bands = [int(x) for x in rng.choice([1, 16, 64, 300], size=Hq)]
+    lens = [int(x) for x in rng.integers(1, N + 1, size=B)]
+    lens[int(rng.integers(B))] = N          # one prompt fills the call
+    return dict(i=i, B=B, Hq=Hq, Hkv=Hkv, N=N, rho=rho, bands=bands, lens=lens,
+                r=int(rng.choice([1, 16, 64, 300])),
+                tau=round(float(rng.uniform(0.85, 1.4)) * np.sqrt(2 * (1 - rho)), 3),
+                kv="fp32" if rng.random() < 0.3 else "bf16",
+                layout="paged" if rng.random() < 0.6 else "contiguous",
+                ring_bf16=bool(rng.random() < 0.35))
+
+
+_PF_SWEEP = [_prefill_draw(i, rng) for rng in [np.random.default_rng(4242)] for i in range(8)]
+_PF_IDS = ["p%d-B%d-%dq%dkv-N%d" % (c["i"], c["B"], c["Hq"], c["Hkv"], c["N"]) for c in _PF_SWEEP]
+
+
+@pytest.mark.parametrize("c", _PF_SWEEP, ids=_PF_IDS)
+def test_prefill_random_configuration(gpu_lib, c):
+    """Seeded random prefill cases: shape, ragged prompt lengths (every chunk
+    and tile boundary of the match), band or per-head bands, rho with a tau
+    near the nearest earlier query's distance, KV dtype and layout, fp32 or
+    bf16 candidate queries."""
+    import kv_reuse_amd as mac
+    import oracle
+    w = _w("b16_128k", name="pfsweep%d" % c["i"], B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"],
+           steps=c["N"], r=c["r"], tau=c["tau"], rho=("const", c["rho"]), kv=c["kv"],
+           layout=c["layout"], seed=200 + c["i"])
+    flags = mac.MAC_F_RING_BF16 if c["ring_bf16"] else 0
+    oflags = oracle.F_RING_BF16 if c["ring_bf16"] else 0
+    print("tau", c["tau"], "rho %.4f" % c["rho"], "bands", c["bands"], "ring_bf16", c["ring_bf16"],
+          flush=True)
+    _prefill_case(w, lens=c["lens"], bands=c["bands"], flags=flags, oflags=oflags)
