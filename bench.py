@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "complete_kernel_b16_128k_traffic.json")
 # sources the complete kernel is built from: the counters are void once they change
 KERNEL_SRCS = [os.path.join(ROOT, "kv_reuse_amd", "csrc", f)
-               for f in ("complete.hip", "mac_device.h", "mac_internal.h")]
+               for f in ("complete.hip", "mfma_page.h", "mac_device.h", "mac_internal.h")]
 
 
 def kernel_sha16():
