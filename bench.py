@@ -527,6 +527,20 @@ def prefill_table8(args):
                                  "data": "synthetic"}}), flush=True)
 
 
+def host_cpu():
+    """The host the oracle ran on: CPU model and logical CPUs."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count()}
+
+
 def oracle_baseline(w, K, V, qs, n_req, n_steps, flags=0):
     """fp64 oracle, as it stands, on the first n_req requests for n_steps steps
     (flags: the oracle's F_* bits; F_DISABLE_REUSE gives its full-attention step)."""
@@ -775,7 +789,7 @@ def main():
         sec_full = oracle_baseline(w, host_sample[0], host_sample[1], qs, n_req, n_steps,
                                    flags=oracle.F_DISABLE_REUSE)
         cpu = {"value": sec * 1e6 * (w.B / n_req), "unit": "us/step", "cores": cores,
-               "kind": "oracle",
+               "kind": "oracle", "host": host_cpu(),
                "full_attention_value": sec_full * 1e6 * (w.B / n_req),
                "sample": "%d of %d requests (all %d heads each), first %d decode steps from an "
                          "empty ring, scaled by %d/%d to the batch" % (n_req, w.B, w.Hq, n_steps,
