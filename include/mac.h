@@ -207,9 +207,16 @@ mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv /* host */, const v
  * an equal share, and a kernel still resident when it starts would delay some
  * of its waves.  The library copies what amend needs, so the caller
  * may reuse q_pre_rope, out and seq_lens as soon as the step's work on
- * `stream` has run.  The ring slot a call writes and the events it waits on
- * are chosen on the host per call, so a decode step is not meant to be
- * captured into a HIP graph and replayed. */
+ * `stream` has run.  The ring slot a call writes comes from a call counter
+ * kept on the device (mac_stats' steps), so with MAC_F_FUSED_AMEND or
+ * MAC_F_SYNC_AMEND (and without MAC_F_STALE_RING or MAC_F_TIMING) a call
+ * enqueues only kernels whose arguments do not change from call to call: the
+ * caller may capture append + decode on one stream into a HIP graph and
+ * replay it, updating the positions, seq_lens and query buffers in place
+ * between replays (warm up and capture on the same stream).  The default
+ * form orders the amend stream with events chosen per call on the host and
+ * must not be captured; neither may the stale-by-one ring, whose buffers
+ * alternate per call on the host. */
 mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv /* host */,
                            const float *q_pre_rope, float *out, const int32_t *override_pos,
                            void *stream);

@@ -111,8 +111,7 @@ __device__ __forceinline__ void amend_finish(const Shape &s, const State &st,
 }
 
 template <typename T, int G>
-__global__ __launch_bounds__(64 * amend_waves<G>()) void amend_kernel(Shape s, State st, KvView kv,
-                                                                      int slot_new)
+__global__ __launch_bounds__(64 * amend_waves<G>()) void amend_kernel(Shape s, State st, KvView kv)
 {
     constexpr int AMEND_WAVES = amend_waves<G>();
     __shared__ float red[AMEND_WAVES][G][SUMM];
@@ -151,7 +150,7 @@ __global__ __launch_bounds__(64 * amend_waves<G>()) void amend_kernel(Shape s, S
         store_wave_summary<T, G>(acc, &red[wv][0][0]);
     }
     __syncthreads();
-    amend_finish<G, AMEND_WAVES>(s, st, red, in, b, kvh, m, lo, has_prefix, slot_new);
+    amend_finish<G, AMEND_WAVES>(s, st, red, in, b, kvh, m, lo, has_prefix, *st.step_slot);
 }
 
 // bf16 caches: the band's pages go through the MFMA page path of complete
@@ -163,7 +162,7 @@ constexpr int AMEND_MFMA_WAVES = 8;
 
 template <int G>
 __global__ __launch_bounds__(64 * AMEND_MFMA_WAVES) void amend_mfma_kernel(Shape s, State st,
-                                                                          KvView kv, int slot_new)
+                                                                          KvView kv)
 {
     constexpr int NW = AMEND_MFMA_WAVES;
     constexpr int HPL = MAcc<G>::HPL;
@@ -248,7 +247,7 @@ __global__ __launch_bounds__(64 * AMEND_MFMA_WAVES) void amend_mfma_kernel(Shape
         store_msummary<G>(acc, &red[wv][0][0]);
     }
     __syncthreads();
-    amend_finish<G, NW>(s, st, red, in, b, kvh, m, lo, has_prefix, slot_new);
+    amend_finish<G, NW>(s, st, red, in, b, kvh, m, lo, has_prefix, *st.step_slot);
 }
 
 // ================================================================= append
@@ -304,8 +303,7 @@ __global__ void reset_kernel(int32_t *ring_pos, long n_pos, unsigned long long *
 }
 
 template <typename T>
-hipError_t launch_amend_t(const Shape &s, const State &st, const KvView &kv, int slot_new,
-                          hipStream_t stream)
+hipError_t launch_amend_t(const Shape &s, const State &st, const KvView &kv, hipStream_t stream)
 {
     const dim3 grid(s.Hkv, s.B);
     switch (s.G) {
@@ -313,10 +311,10 @@ hipError_t launch_amend_t(const Shape &s, const State &st, const KvView &kv, int
     case GG:                                                                                  \
         if constexpr (sizeof(T) == 2)                                                         \
             hipLaunchKernelGGL(amend_mfma_kernel<GG>, grid, dim3(64 * AMEND_MFMA_WAVES), 0,    \
-                               stream, s, st, kv, slot_new);                                  \
+                               stream, s, st, kv);                                            \
         else                                                                                  \
             hipLaunchKernelGGL((amend_kernel<T, GG>), grid, dim3(64 * amend_waves<GG>()), 0,   \
-                               stream, s, st, kv, slot_new);                                  \
+                               stream, s, st, kv);                                            \
         break;
         MAC_CASE(1)
         MAC_CASE(2)
@@ -332,10 +330,10 @@ hipError_t launch_amend_t(const Shape &s, const State &st, const KvView &kv, int
 }  // namespace
 
 hipError_t launch_amend(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
-                        int slot_new, hipStream_t stream)
+                        hipStream_t stream)
 {
-    return kv_fp32 ? launch_amend_t<float>(s, st, kv, slot_new, stream)
-                   : launch_amend_t<uint16_t>(s, st, kv, slot_new, stream);
+    return kv_fp32 ? launch_amend_t<float>(s, st, kv, stream)
+                   : launch_amend_t<uint16_t>(s, st, kv, stream);
 }
 
 hipError_t launch_append(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,

@@ -10,6 +10,7 @@
 //   q_copy     [B][Hq][D]           this step's pre-RoPE queries (for amend)
 //   q_rot      [B][Hq][D]           this step's post-RoPE queries
 //   m_buf      [B]     int32        this step's query position (-1 idle)
+//   step_slot  [1]     int32        the ring slot this step writes (set by match)
 //   dec_slot   [B][Hq] int32        matched slot (-1 miss)
 //   dec_p      [B][Hq] int32        matched position (-1 miss)
 //   dec_start  [B][Hq] int32        first key of the head's span
@@ -20,8 +21,8 @@
 //   as_full    [B][Hq][SUMM]        AS_{1:m} of this step, input of amend
 //   band       [Hq]    int32        band r_h of each query head
 //   stats      [MAC_NSTAT] + [B*Hq][HEAD_NSTAT] + [B*Hkv][GRP_NSTAT] uint64 counters
-// With the stale-by-one ring (MAC_F_STALE_RING) q_copy, q_rot, m_buf and
-// as_full are held twice and calls alternate between the copies, so that the
+// With the stale-by-one ring (MAC_F_STALE_RING) q_copy, q_rot, m_buf,
+// step_slot and as_full are held twice and calls alternate between the copies, so that the
 // amend of call t-1, still running, reads its own while call t writes the
 // other.
 // A group's union span (the keys complete streams for it) starts at the
@@ -59,6 +60,7 @@ enum GlobalStat {
     ST_PF_HITS,
     ST_PF_KV,            // keys attended per (KV group, token)
     ST_PF_OVR_INVALID,   // prefill overrides naming no earlier token
+    ST_STEPS,            // decode calls: match takes the ring slot (ST_STEPS mod W) and advances it
     MAC_NSTAT = 8
 };
 enum HeadStat { HS_HITS = 0, HS_MISSES, HS_NEAR_TAU, HS_OVR_INVALID, HEAD_NSTAT };
@@ -91,6 +93,7 @@ struct State {
     void *ring_q;             // float, or uint16_t (bf16) when Shape::ring_bf16
     float *ring_s, *q_copy, *q_rot, *partials, *as_full, *dec_rel;
     int32_t *ring_pos, *m_buf, *dec_slot, *dec_p, *dec_start;
+    int32_t *step_slot;       // [1] ring slot of this step (match -> reduce, amend)
     int32_t *grp_parts;       // [B*Hkv*nseg][2] worker range of each segment's partials (complete -> reduce)
     unsigned long long *stats;        // [MAC_NSTAT], then the two blocks below
     unsigned long long *head_stats;   // [B*Hq][HEAD_NSTAT]
@@ -113,11 +116,10 @@ hipError_t launch_match(const Shape &s, const State &st, const KvView &kv, const
                         hipStream_t stream);
 hipError_t launch_complete(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
                            int n_blocks, hipStream_t stream);
-// slot_new: the ring slot a fused amend writes (ignored when nseg == 1).
-hipError_t launch_reduce(const Shape &s, const State &st, float *out, int slot_new,
-                         hipStream_t stream);
+// reduce (fused amend) and amend write the ring slot match chose (step_slot).
+hipError_t launch_reduce(const Shape &s, const State &st, float *out, hipStream_t stream);
 hipError_t launch_amend(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
-                        int slot_new, hipStream_t stream);
+                        hipStream_t stream);
 hipError_t launch_append(const Shape &s, const State &st, const KvView &kv, bool kv_fp32,
                          const void *k_new, const void *v_new, const int32_t *positions,
                          hipStream_t stream);

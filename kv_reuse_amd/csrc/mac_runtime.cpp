@@ -74,9 +74,10 @@ struct Sizes {
     size_t ring_q, ring_s, ring_pos, qvec, m_buf, dec_i, dec_f, grp_parts, partials, as_full,
         stats, inv_freq, band, tiles;
     size_t step_copies;   // copies of the buffers amend reads: 2 with the stale-by-one ring
+                          // (m_buf's size also holds the step's ring slot, one int)
     size_t total() const
     {
-        return ring_q + ring_s + ring_pos + step_copies * (2 * qvec + m_buf + as_full) +
+        return ring_q + ring_s + ring_pos + step_copies * (2 * qvec + 2 * m_buf + as_full) +
                3 * dec_i + dec_f + grp_parts + partials + stats + inv_freq + band + tiles;
     }
 };
@@ -384,6 +385,7 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     h->st.q_copy = (float *)take(sz.qvec);
     h->st.q_rot = (float *)take(sz.qvec);
     h->st.m_buf = (int32_t *)take(sz.m_buf);
+    h->st.step_slot = (int32_t *)take(sz.m_buf);
     h->st.dec_slot = (int32_t *)take(sz.dec_i);
     h->st.dec_p = (int32_t *)take(sz.dec_i);
     h->st.dec_start = (int32_t *)take(sz.dec_i);
@@ -402,6 +404,7 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
         h->st_odd.q_copy = (float *)take(sz.qvec);
         h->st_odd.q_rot = (float *)take(sz.qvec);
         h->st_odd.m_buf = (int32_t *)take(sz.m_buf);
+        h->st_odd.step_slot = (int32_t *)take(sz.m_buf);
         h->st_odd.as_full = (float *)take(sz.as_full);
     }
 
@@ -550,8 +553,7 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
     MAC_HIP(h, mac::launch_complete(h->shape, S, v, h->kv_fp32, h->n_blocks, st));
     if (timing)
         MAC_HIP(h, hipEventRecord(h->tm[2], st));
-    const int slot_new = (int)(h->calls % h->cfg.ring_size);
-    MAC_HIP(h, mac::launch_reduce(h->shape, S, out, slot_new, st));
+    MAC_HIP(h, mac::launch_reduce(h->shape, S, out, st));
     if (timing)
         MAC_HIP(h, hipEventRecord(h->tm[3], st));
 
@@ -563,7 +565,7 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
         }
         if (timing)
             MAC_HIP(h, hipEventRecord(h->tm[4], as));
-        MAC_HIP(h, mac::launch_amend(h->shape, S, v, h->kv_fp32, slot_new, as));
+        MAC_HIP(h, mac::launch_amend(h->shape, S, v, h->kv_fp32, as));
         if (timing)
             MAC_HIP(h, hipEventRecord(h->tm[5], as));
         if (as != st) {
@@ -636,7 +638,7 @@ mac_status mac_stats(mac_handle h, mac_stats_t *out)
             gs[k] += gp[g * mac::GRP_NSTAT + k];
     std::memset(out, 0, sizeof *out);
     const uint64_t row = 2ull * mac::D * (h->kv_fp32 ? 4 : 2);   // one key row + one value row
-    out->steps = (uint64_t)h->calls;
+    out->steps = raw[mac::ST_STEPS];   // counted on the device (graph replays included)
     out->hits = hs[mac::HS_HITS];
     out->misses = hs[mac::HS_MISSES];
     out->decisions = out->hits + out->misses;

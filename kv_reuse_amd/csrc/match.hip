@@ -316,6 +316,13 @@ __global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
             for (int k = 0; k < HEAD_NSTAT; ++k)
                 hstat[k] = old[k] + (unsigned long long)cnt[k];
         }
+        if (h == 0 && b == 0) {
+            // the ring slot of this call, from the device's own call count (so a
+            // captured step replays correctly): slot = calls mod W
+            const unsigned long long c = st.stats[ST_STEPS];
+            *st.step_slot = (int)(c % (unsigned long long)s.W);
+            st.stats[ST_STEPS] = c + 1;
+        }
         if (h == 0) {
             st.m_buf[b] = m;
             if (bad)

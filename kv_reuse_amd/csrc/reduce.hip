@@ -196,7 +196,7 @@ __device__ __forceinline__ void combine_partials(const float *part0, int n0, con
 // Five waves per SIMD (at most 102 VGPRs): a CU holds one block and the next
 // one starts while wave 0 of the last finishes its head.
 __global__ __launch_bounds__(REDUCE_THREADS) __attribute__((amdgpu_waves_per_eu(5))) void
-reduce_kernel(Shape s, State st, float *__restrict__ out, int slot_new)
+reduce_kernel(Shape s, State st, float *__restrict__ out)
 {
     __shared__ ReduceLds lds;
     const int b = blockIdx.y, h = blockIdx.x, kvh = h / s.G, hh = h % s.G;
@@ -248,6 +248,7 @@ reduce_kernel(Shape s, State st, float *__restrict__ out, int slot_new)
     } else {
         const Sum4 X = merge(S, part0);   // AS_{1:m-r}
         O = merge(X, part1);
+        const int slot_new = *st.step_slot;   // this call's ring slot (match)
         float *dst = st.ring_s + (idx * s.W + slot_new) * SUMM;
         *reinterpret_cast<float4 *>(dst + 4 * c) = X.o;
         const float4 qv = *reinterpret_cast<const float4 *>(st.q_copy + idx * D + 4 * c);
@@ -270,13 +271,12 @@ reduce_kernel(Shape s, State st, float *__restrict__ out, int slot_new)
 
 }  // namespace
 
-hipError_t launch_reduce(const Shape &s, const State &st, float *out, int slot_new,
-                         hipStream_t stream)
+hipError_t launch_reduce(const Shape &s, const State &st, float *out, hipStream_t stream)
 {
     if (!supported_group(s.G) || s.nseg < 1 || s.nseg > 2)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(reduce_kernel, dim3(s.Hq, s.B), dim3(REDUCE_THREADS), 0, stream, s, st,
-                       out, slot_new);
+                       out);
     return hipGetLastError();
 }
 
