@@ -206,8 +206,10 @@ def speedup_point(name, steps=24, warmup=40):
             prev = st
         bn.layer.close()
         res[label] = (float(np.mean(att)), float(np.sum(hits)) / (len(hits) * w.B * w.Hq))
+    graph = fused_graph_loops(w, kc, vc, paged, table, k_rows, v_rows, q_dev, warmup)
     return {"workload": name, "context": w.C, "batch": w.B,
             "mac_attention_us": res["mac"][0], "full_attention_us": res["full"][0],
+            "fused_amend_loop_us_per_step": graph,
             "head_hit_rate": res["mac"][1], "speedup": res["full"][0] / res["mac"][0],
             # the other amend forms: no second stream, so no cross-queue event
             # after the reduce (sync: amend runs inside the span)
@@ -215,6 +217,58 @@ def speedup_point(name, steps=24, warmup=40):
             "mac_sync_amend_attention_us": res["mac_sync_amend"][0],
             "speedup_fused_amend": res["full"][0] / res["mac_fused_amend"][0],
             "steps": steps, "warmup": warmup}
+
+
+def fused_graph_loops(w, kc, vc, paged, table, k_rows, v_rows, q_dev, start, steps=16):
+    """Back-to-back fused-amend decode loops (append + decode per step, each
+    step's inputs written in place first, no host synchronisation): the
+    library called eagerly, and the same step captured once into a HIP graph
+    and replayed.  Microseconds per step between two stream events."""
+    import torch
+    import kv_reuse_amd as mac
+    out = {}
+    for label in ("eager", "graph"):
+        bn = Bench(w, mac.MAC_F_FUSED_AMEND, kc, vc, paged, table)
+        s = torch.cuda.Stream()
+        k_in, v_in, q_in = k_rows[0].clone(), v_rows[0].clone(), q_dev[0].clone()
+
+        def inputs(t):
+            bn.pos.fill_(w.C + t)
+            bn.seq.fill_(w.C + t + 1)
+            k_in.copy_(k_rows[t])
+            v_in.copy_(v_rows[t])
+            q_in.copy_(q_dev[t])
+
+        def step():
+            bn.layer.append_kv(bn.view, k_in, v_in, bn.pos, s)
+            bn.layer.decode_step(bn.view, q_in, bn.out, None, s)
+
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            for t in range(start - 2):          # warm-up on the loop's stream
+                inputs(t)
+                step()
+            g = None
+            if label == "graph":
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    step()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for t in range(start - 2, start - 2 + steps):
+                inputs(t)
+                if g is None:
+                    step()
+                else:
+                    g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        out[label] = e0.elapsed_time(e1) * 1e3 / steps
+        bn.layer.close()
+    return out
 
 
 def contgen(args):
