@@ -141,7 +141,7 @@ typedef struct {
 /* Counters since mac_init / mac_reset.  Byte counts are the algorithmic bytes
  * of key/value rows streamed (each key row and value row counted once). */
 typedef struct {
-    uint64_t steps;              /* mac_decode_step calls */
+    uint64_t steps;              /* decode steps run (counted on the device: graph replays included) */
     uint64_t decisions;          /* (request, head) decisions taken by match */
     uint64_t hits;
     uint64_t misses;

@@ -38,7 +38,7 @@ struct mac_ctx {
     hipStream_t amend_on[2] = {};
     hipEvent_t tm[6] = {};
     bool timed_step = false;
-    long long calls = 0;
+    long long calls = 0;   // host-side call count: parity and hidden slot of the stale-by-one ring
     size_t aux_bytes = 0;
     void *blocks[16] = {};
     int n_alloc = 0;
