@@ -1,6 +1,7 @@
 """Parity at full size, in the configurations the benchmark times:
 - batch 16 x 131072-token context, 32q/8kv, paged bf16 KV with a permuted
-  page table (with the pages' amend, and with the fused amend);
+  page table (with the pages' amend, the fused amend, the stale-by-one ring
+  and bf16 ring queries);
 - batch 8 x 122880, 32q/4kv (8 query heads per KV head), per-head rho
   0.5..0.99, paged bf16.
 
@@ -36,11 +37,18 @@ def _sampled(w, steps, n_groups, seed, **kw):
     return hits
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_batch16_128k_paged_sampled_heads(gpu_lib, fused):
+@pytest.mark.parametrize("form", ["pages", "fused", "stale", "ring_bf16"])
+def test_batch16_128k_paged_sampled_heads(gpu_lib, form):
+    """The headline workload in the pages' form (async amend) and each option
+    the library offers for it, against the oracle with the same option."""
     import kv_reuse_amd as mac
+    import oracle
+    flags, oflags = {"pages": (0, 0),
+                     "fused": (mac.MAC_F_FUSED_AMEND, 0),
+                     "stale": (mac.MAC_F_STALE_RING, oracle.F_STALE_RING),
+                     "ring_bf16": (mac.MAC_F_RING_BF16, oracle.F_RING_BF16)}[form]
     w = get_config("b16_128k")
-    hits = _sampled(w, 24, 4, 7, flags=mac.MAC_F_FUSED_AMEND if fused else 0)
+    hits = _sampled(w, 24, 4, 7, flags=flags, oracle_flags=oflags)
     assert hits > 0
 
 
