@@ -30,7 +30,7 @@ constexpr int REDUCE_THREADS = 1024;
 constexpr int RCH = D / 4;                       // float4 chunks of a row
 constexpr int RLANES = REDUCE_THREADS / RCH;     // partials combined side by side
 constexpr int RUNROLL = 4;                       // partials per round of loads
-constexpr int RLONG = 8;                        // the same, for long lists
+constexpr int RLONG = 8;                         // the same, for long lists
 
 // A summary as threads 0..RCH-1 hold it: normalised output chunk c (o), the
 // reference max M (log2 units) and the normaliser L; EMPTY is (0, -inf, 0).
