@@ -617,8 +617,9 @@ def oracle_baseline(w, K, V, qs, n_req, n_steps, flags=0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the decode step runs on a single MI355X here and "
-              "--gpus %d is not supported (the sharding design is described in DESIGN.md)"
+        print("bench.py measures one GPU: the decode step runs on a single MI355X and "
+              "--gpus %d is not supported (requests and KV groups shard without communication "
+              "inside attention, so one GPU's share is the unit measured)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
