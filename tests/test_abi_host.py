@@ -129,3 +129,15 @@ def test_init_rejects_bad_config_before_any_device_work():
     with pytest.raises(mac.MacError) as ei:
         mac.mac_init(_cfg(band=0))
     assert ei.value.status == mac.MAC_EINVAL
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU's share: --gpus N > 1 exits with status 2 and
+    a message, before any import of the library or the GPU runtime."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "--gpus 2 is not supported" in r.stderr
+    assert r.stdout == ""
