@@ -39,14 +39,25 @@ _u8p = ctypes.POINTER(ctypes.c_uint8)
 _vp = ctypes.c_void_p
 
 
-def _load():
+def _use_library(path):
+    """Load the oracle from another build of mac_oracle.c (the mutation tests
+    build copies with a planted mistake); None returns to the default build.
+    Oracle objects created before the switch keep the library they had."""
+    global _lib
+    _lib = None
+    return _load(path)
+
+
+def _load(path=None):
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
-        from . import build as _b
-        _b.build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    if path is None:
+        path = _LIB_PATH
+        if not os.path.exists(path):
+            from . import build as _b
+            _b.build()
+    lib = ctypes.CDLL(path)
     lib.orc_rope.argtypes = [_fp, ctypes.c_int, ctypes.c_int64, ctypes.c_double, _dp]
     lib.orc_empty.argtypes = [ctypes.c_int, _dp]
     lib.orc_attend.argtypes = [_dp, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int64,

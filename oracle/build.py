@@ -11,15 +11,16 @@ SRC = os.path.join(HERE, "mac_oracle.c")
 LIB = os.path.join(HERE, "libmac_oracle.so")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, src: str = SRC, out: str = LIB) -> str:
+    """Compile `src` (the oracle, or a test's mutated copy of it) into `out`."""
     cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp",
            "-fno-fast-math", "-Wall", "-Wextra", "-Wno-unused-parameter",
-           SRC, "-o", LIB + ".tmp", "-lm"]
+           src, "-o", out + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
