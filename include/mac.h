@@ -23,7 +23,14 @@
  *    max M of the scaled logits and the normaliser l = sum exp(logit - M).
  *  - Calls are asynchronous on the stream they receive (NULL: the handle's main
  *    stream) unless stated.  A handle is one attention layer and is not
- *    thread-safe.
+ *    thread-safe.  Its calls may use different streams: a decode, prefill or
+ *    reset call on another stream than the handle's previous one waits for
+ *    that call's work (an event recorded at the end of each call; none is
+ *    recorded on a stream being captured into a graph, and calls that follow
+ *    a captured one on another stream must be ordered by the caller).
+ *  - A HIP failure part-way through mac_decode_step or mac_prefill can leave
+ *    the device state out of step with the host's; both calls then return
+ *    MAC_ESTATE until mac_reset succeeds.
  *  - No C++ exception crosses this boundary.  Every call returns mac_status;
  *    mac_last_error() gives the handle's last message.  Shape and pointer
  *    errors are caught on the host before any launch.  Device faults surface
@@ -163,6 +170,7 @@ typedef struct {
     uint64_t prefill_hits;
     uint64_t prefill_kv_tokens;  /* keys attended, per KV group and prompt token */
     uint64_t prefill_override_invalid;
+    uint64_t complete_waves;     /* waves of the complete kernel's persistent grid (the plan's workers) */
 } mac_stats_t;
 
 /* Check a configuration without touching the GPU (host only). */
@@ -238,8 +246,8 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv /* host */,
  * request b (counted in bad_input).  Honours MAC_F_DISABLE_REUSE (plain
  * causal attention) and MAC_F_RING_BF16 (earlier queries rounded to bf16
  * for the match); the other flags do not apply.  Enqueued on `stream` (NULL:
- * the main stream); its scratch (~(d + 2.6 (d + 4)) * 4 bytes per (token,
- * head)) is allocated and released stream-ordered on that stream (MAC_ENOMEM
+ * the main stream); its scratch ((5 d + 20) * 4 = 2640 bytes per (request,
+ * token, query head)) is allocated and released stream-ordered on that stream (MAC_ENOMEM
  * if that fails).  Counters: mac_stats' prefill_* fields. */
 mac_status mac_prefill(mac_handle h, const mac_kv_view *kv /* host */, int32_t num_tokens,
                        const float *q_pre, float *out, const int32_t *override_pos,

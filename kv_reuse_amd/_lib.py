@@ -64,7 +64,7 @@ class MacStats(ctypes.Structure):
                  "last_us_attention")] + \
                [(n, ctypes.c_uint64) for n in
                 ("prefill_tokens", "prefill_decisions", "prefill_hits", "prefill_kv_tokens",
-                 "prefill_override_invalid")]
+                 "prefill_override_invalid", "complete_waves")]
 
 
 _lib = None

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64 * amend_waves<G>()) void amend_kernel(Shape s, S
     __shared__ float red[AMEND_WAVES][G][SUMM];
     using K = Kv<T>;
     const int b = blockIdx.y, kvh = blockIdx.x;
-    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const int wv = threadIdx.x >> 6;
     const int m = st.m_buf[b];
     if (m < 0)
         return;

@@ -37,6 +37,17 @@ struct mac_ctx {
     // the event on this stream first (amend_on: that stream, or null)
     hipStream_t amend_on[2] = {};
     hipEvent_t tm[6] = {};
+    // Calls on different streams: the stream of the last call that enqueued
+    // work on the handle's state, and ev_done, recorded on it after that work
+    // (not recorded while the stream was being captured into a graph: then
+    // done_valid is false and the caller orders the streams).
+    hipStream_t last_stream = nullptr;
+    hipEvent_t ev_done = nullptr;
+    bool done_valid = false;
+    // A HIP call failed part-way through a decode or prefill call: device and
+    // host state may disagree (the ring slot counter), so such calls return
+    // MAC_ESTATE until mac_reset succeeds.
+    bool broken = false;
     bool timed_step = false;
     long long calls = 0;   // host-side call count: parity and hidden slot of the stale-by-one ring
     size_t aux_bytes = 0;
@@ -249,6 +260,27 @@ hipError_t wait_amend(mac_ctx *h, int i, hipStream_t st)
     return hipStreamWaitEvent(st, h->ev_amend[i], 0);
 }
 
+// Order a call on stream st after the handle's last call when that one ran
+// on another stream (its kernels read and write the same state).
+hipError_t follow(mac_ctx *h, hipStream_t st)
+{
+    if (h->last_stream && h->last_stream != st && h->done_valid)
+        return hipStreamWaitEvent(st, h->ev_done, 0);
+    return hipSuccess;
+}
+
+// Mark the end of a call's work on st (skipped while st is being captured).
+hipError_t mark_done(mac_ctx *h, hipStream_t st)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cs);
+    if (e != hipSuccess)
+        return e;
+    h->last_stream = st;
+    h->done_valid = cs == hipStreamCaptureStatusNone;
+    return h->done_valid ? hipEventRecord(h->ev_done, st) : hipSuccess;
+}
+
 mac::KvView to_view(const mac_ctx *h, const mac_kv_view *kv)
 {
     mac::KvView v{};
@@ -276,6 +308,7 @@ void release(mac_ctx *h)
     for (auto &e : h->ev_amend)
         if (e) (void)hipEventDestroy(e);
     if (h->ev_drain) (void)hipEventDestroy(h->ev_drain);
+    if (h->ev_done) (void)hipEventDestroy(h->ev_done);
     for (auto &e : h->tm)
         if (e) (void)hipEventDestroy(e);
     if (h->own_amend && h->amend_stream)
@@ -450,7 +483,8 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     if (hipEventCreateWithFlags(&h->ev_attn, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&h->ev_amend[0], hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&h->ev_amend[1], hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_drain, hipEventDisableTiming) != hipSuccess)
+        hipEventCreateWithFlags(&h->ev_drain, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_done, hipEventDisableTiming) != hipSuccess)
         return bail(MAC_EHIP, "hipEventCreate failed");
     for (auto &ev : h->tm)
         if (hipEventCreate(&ev) != hipSuccess)
@@ -478,11 +512,14 @@ mac_status mac_reset(mac_handle h)
 {
     if (!h)
         return fail(nullptr, MAC_EINVAL, "handle is NULL");
+    MAC_HIP(h, follow(h, h->main_stream));
     for (int i = 0; i < 2; ++i)
         MAC_HIP(h, wait_amend(h, i, h->main_stream));
     MAC_HIP(h, mac::launch_reset(h->shape, h->st, h->main_stream));
+    MAC_HIP(h, mark_done(h, h->main_stream));
     h->calls = 0;
     h->timed_step = false;
+    h->broken = false;
     return MAC_OK;
 }
 
@@ -504,36 +541,39 @@ mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv, const void *k_new,
     return MAC_OK;
 }
 
-mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_pre_rope, float *out,
-                           const int32_t *override_pos, void *stream)
+namespace {
+
+// The enqueue sequence of one decode call on stream st; `what` names the HIP
+// call that failed.
+hipError_t decode_enqueue(mac_ctx *h, const mac_kv_view *kv, const float *q_pre_rope, float *out,
+                          const int32_t *override_pos, hipStream_t st, const char **what)
 {
-    if (!h)
-        return fail(nullptr, MAC_EINVAL, "handle is NULL");
-    mac_status s = check_view(h, kv);
-    if (s != MAC_OK)
-        return s;
-    if (!q_pre_rope || !out)
-        return fail(h, MAC_EINVAL, "q_pre_rope and out must be non-NULL");
-    if (!aligned16(q_pre_rope) || !aligned16(out))
-        return fail(h, MAC_EINVAL, "q_pre_rope and out must be 16-byte aligned");
-    hipStream_t st = stream ? (hipStream_t)stream : h->main_stream;
+#define MAC_TRY(call)                                                                       \
+    do {                                                                                    \
+        hipError_t e_ = (call);                                                             \
+        if (e_ != hipSuccess) {                                                             \
+            *what = #call;                                                                  \
+            return e_;                                                                      \
+        }                                                                                   \
+    } while (0)
     const mac::KvView v = to_view(h, kv);
     const bool timing = h->cfg.flags & MAC_F_TIMING;
     const int cur = (int)(h->calls & 1);
 
+    MAC_TRY(follow(h, st));
     // match(t) reads the ring amend(t-1) writes.  The stale-by-one ring hides
     // that slot from match(t), which then waits only for amend(t-2); the two
     // calls also work on separate copies of the buffers amend reads.
     const bool stale = h->cfg.flags & MAC_F_STALE_RING;
     const mac::State &S = (stale && cur) ? h->st_odd : h->st;
-    MAC_HIP(h, wait_amend(h, stale ? cur : cur ^ 1, st));
+    MAC_TRY(wait_amend(h, stale ? cur : cur ^ 1, st));
     const int hidden = (stale && h->calls > 0) ? (int)((h->calls - 1) % h->cfg.ring_size) : -1;
     if (timing)
-        MAC_HIP(h, hipEventRecord(h->tm[0], st));
+        MAC_TRY(hipEventRecord(h->tm[0], st));
     if (h->shape.reuse && h->cfg.ring_size > mac::TILE_W)
-        MAC_HIP(h, mac::launch_match_tiles(h->shape, S, v, kv->seq_lens, q_pre_rope, hidden, st));
-    MAC_HIP(h, mac::launch_match(h->shape, S, v, kv->seq_lens, q_pre_rope, override_pos, out,
-                                 hidden, st));
+        MAC_TRY(mac::launch_match_tiles(h->shape, S, v, kv->seq_lens, q_pre_rope, hidden, st));
+    MAC_TRY(mac::launch_match(h->shape, S, v, kv->seq_lens, q_pre_rope, override_pos, out,
+                              hidden, st));
     // The complete kernel is a persistent grid with equal static shares per
     // wave: a kernel still holding CU slots when it launches delays some of
     // its waves and with them the whole launch (measured: +35 % when an amend
@@ -545,39 +585,67 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
     const bool fused = h->shape.nseg == 2;
     if (!h->own_amend && h->amend_stream != st && !(h->cfg.flags & MAC_F_SYNC_AMEND) &&
         h->shape.reuse && !fused) {
-        MAC_HIP(h, hipEventRecord(h->ev_drain, h->amend_stream));
-        MAC_HIP(h, hipStreamWaitEvent(st, h->ev_drain, 0));
+        MAC_TRY(hipEventRecord(h->ev_drain, h->amend_stream));
+        MAC_TRY(hipStreamWaitEvent(st, h->ev_drain, 0));
     }
     if (timing)
-        MAC_HIP(h, hipEventRecord(h->tm[1], st));
-    MAC_HIP(h, mac::launch_complete(h->shape, S, v, h->kv_fp32, h->n_blocks, st));
+        MAC_TRY(hipEventRecord(h->tm[1], st));
+    MAC_TRY(mac::launch_complete(h->shape, S, v, h->kv_fp32, h->n_blocks, st));
     if (timing)
-        MAC_HIP(h, hipEventRecord(h->tm[2], st));
-    MAC_HIP(h, mac::launch_reduce(h->shape, S, out, st));
+        MAC_TRY(hipEventRecord(h->tm[2], st));
+    MAC_TRY(mac::launch_reduce(h->shape, S, out, st));
     if (timing)
-        MAC_HIP(h, hipEventRecord(h->tm[3], st));
+        MAC_TRY(hipEventRecord(h->tm[3], st));
 
     if (h->shape.reuse && !fused) {
         hipStream_t as = (h->cfg.flags & MAC_F_SYNC_AMEND) ? st : h->amend_stream;
         if (as != st) {
-            MAC_HIP(h, hipEventRecord(h->ev_attn, st));
-            MAC_HIP(h, hipStreamWaitEvent(as, h->ev_attn, 0));
+            MAC_TRY(hipEventRecord(h->ev_attn, st));
+            MAC_TRY(hipStreamWaitEvent(as, h->ev_attn, 0));
         }
         if (timing)
-            MAC_HIP(h, hipEventRecord(h->tm[4], as));
-        MAC_HIP(h, mac::launch_amend(h->shape, S, v, h->kv_fp32, as));
+            MAC_TRY(hipEventRecord(h->tm[4], as));
+        MAC_TRY(mac::launch_amend(h->shape, S, v, h->kv_fp32, as));
         if (timing)
-            MAC_HIP(h, hipEventRecord(h->tm[5], as));
+            MAC_TRY(hipEventRecord(h->tm[5], as));
         if (as != st) {
-            MAC_HIP(h, hipEventRecord(h->ev_amend[cur], as));
+            MAC_TRY(hipEventRecord(h->ev_amend[cur], as));
             h->amend_on[cur] = nullptr;
         } else {
             h->amend_on[cur] = st;
         }
         h->amend_pending[cur] = true;
     }
+    MAC_TRY(mark_done(h, st));
     h->timed_step = timing;
     h->calls += 1;
+    return hipSuccess;
+#undef MAC_TRY
+}
+
+}  // namespace
+
+mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_pre_rope, float *out,
+                           const int32_t *override_pos, void *stream)
+{
+    if (!h)
+        return fail(nullptr, MAC_EINVAL, "handle is NULL");
+    if (h->broken)
+        return fail(h, MAC_ESTATE, "an earlier call failed part-way; call mac_reset first");
+    mac_status s = check_view(h, kv);
+    if (s != MAC_OK)
+        return s;
+    if (!q_pre_rope || !out)
+        return fail(h, MAC_EINVAL, "q_pre_rope and out must be non-NULL");
+    if (!aligned16(q_pre_rope) || !aligned16(out))
+        return fail(h, MAC_EINVAL, "q_pre_rope and out must be 16-byte aligned");
+    hipStream_t st = stream ? (hipStream_t)stream : h->main_stream;
+    const char *what = "";
+    const hipError_t e = decode_enqueue(h, kv, q_pre_rope, out, override_pos, st, &what);
+    if (e != hipSuccess) {
+        h->broken = true;
+        return fail_hip(h, what, e);
+    }
     return MAC_OK;
 }
 
@@ -587,6 +655,8 @@ mac_status mac_prefill(mac_handle h, const mac_kv_view *kv, int32_t num_tokens,
 {
     if (!h)
         return fail(nullptr, MAC_EINVAL, "handle is NULL");
+    if (h->broken)
+        return fail(h, MAC_ESTATE, "an earlier call failed part-way; call mac_reset first");
     mac_status s = check_view(h, kv);
     if (s != MAC_OK)
         return s;
@@ -597,20 +667,26 @@ mac_status mac_prefill(mac_handle h, const mac_kv_view *kv, int32_t num_tokens,
     if (!aligned16(q_pre) || !aligned16(out))
         return fail(h, MAC_EINVAL, "q_pre and out must be 16-byte aligned");
     hipStream_t st = stream ? (hipStream_t)stream : h->main_stream;
+    hipError_t e = follow(h, st);
+    if (e != hipSuccess) {
+        h->broken = true;
+        return fail_hip(h, "follow", e);
+    }
     const size_t bytes = mac::prefill_scratch_bytes(h->shape, num_tokens);
     void *scratch = nullptr;
     if (hipMallocAsync(&scratch, bytes, st) != hipSuccess || !scratch) {
         (void)hipGetLastError();
         return fail(h, MAC_ENOMEM, "stream-ordered allocation of the prefill scratch failed");
     }
-    const hipError_t e = mac::launch_prefill(h->shape, h->st, to_view(h, kv), h->kv_fp32,
-                                             kv->seq_lens, num_tokens, q_pre, out, override_pos,
-                                             p_out, scratch, st);
+    e = mac::launch_prefill(h->shape, h->st, to_view(h, kv), h->kv_fp32, kv->seq_lens, num_tokens,
+                            q_pre, out, override_pos, p_out, scratch, st);
     const hipError_t ef = hipFreeAsync(scratch, st);
-    if (e != hipSuccess)
-        return fail_hip(h, "launch_prefill", e);
-    if (ef != hipSuccess)
-        return fail_hip(h, "hipFreeAsync", ef);
+    const hipError_t ed = e == hipSuccess && ef == hipSuccess ? mark_done(h, st) : hipSuccess;
+    if (e != hipSuccess || ef != hipSuccess || ed != hipSuccess) {
+        h->broken = true;
+        return e != hipSuccess ? fail_hip(h, "launch_prefill", e)
+               : ef != hipSuccess ? fail_hip(h, "hipFreeAsync", ef) : fail_hip(h, "mark_done", ed);
+    }
     return MAC_OK;
 }
 
@@ -649,6 +725,7 @@ mac_status mac_stats(mac_handle h, mac_stats_t *out)
     out->kv_bytes_critical = gs[mac::GS_TOK_CRIT] * row;
     out->kv_bytes_amend = gs[mac::GS_TOK_AMEND] * row;
     out->aux_bytes = h->aux_bytes;
+    out->complete_waves = (uint64_t)h->st.n_workers;
     out->bad_input = raw[mac::ST_BAD_INPUT];
     out->prefill_tokens = raw[mac::ST_PF_TOKENS];
     out->prefill_decisions = raw[mac::ST_PF_DECISIONS];

@@ -1,13 +1,16 @@
 """Lockstep runner: the HIP library (through the C ABI) beside the fp64 oracle.
 
 Per decode step the oracle decides first; heads whose relative distance lies
-within 1e-4 of tau, or whose two nearest ring entries are within a relative
-1e-5, are forced to the oracle's decision through the override array (both
-decisions are correct there).  The GPU then runs and must reproduce every
-decision bit for bit and every output within max-abs 2e-3 and per-row
-relative 1e-2.  Cache rows that have not been appended yet hold NaN (per
-request, for ragged prefill lengths), so a kernel that reads past a request's
-query position fails loudly.
+within 1e-4 of tau (near-threshold), or whose two nearest ring entries are
+within a relative 1e-5 (near-tie), are forced to the oracle's decision
+through the override array (both decisions are correct there: fp32 distance
+rounding reaches that far).  The two kinds are counted apart, and the forced
+share of all decisions must stay small (at most 1 %, or 3 decisions in a tiny
+run), so a slip that widened the exemption would fail.  The GPU then runs
+and must reproduce every decision bit for bit and every output within
+max-abs 2e-3 and per-row relative 1e-2.  Cache rows that have not been
+appended yet hold NaN (per request, for ragged prefill lengths), so a kernel
+that reads past a request's query position fails loudly.
 """
 import numpy as np
 import torch
@@ -18,6 +21,27 @@ from workloads import bf16_bits, kv_logical, page_table, queries, to_paged
 
 MAX_ABS = 2e-3
 ROW_REL = 1e-2
+FORCED_FRAC = 0.01      # forced decisions allowed, as a share of all decisions
+FORCED_MIN = 3          # ... but at least this many in a short run
+
+
+def force_near(res, override=None):
+    """The override array that forces the oracle's decision on its near-tau
+    and near-tie heads (those not already overridden), and the counts of each
+    kind (a head both near tau and near a tie counts as near tau)."""
+    shape = res["hit"].shape
+    forced = np.full(shape, -2, np.int32) if override is None else np.array(override, np.int32)
+    free = forced == -2
+    tau = res["near_tau"].astype(bool) & free
+    tie = res["near_tie"].astype(bool) & free & ~tau
+    flag = tau | tie
+    forced[flag] = np.where(res["hit"][flag] != 0, res["p"][flag], -1)
+    return forced, flag, int(tau.sum()), int(tie.sum())
+
+
+def check_forced_share(n_forced, n_decisions, what=""):
+    bound = max(FORCED_MIN, FORCED_FRAC * n_decisions)
+    assert n_forced <= bound, ("too many forced decisions", what, n_forced, n_decisions)
 
 
 def _kv_nan(dtype):
@@ -27,8 +51,12 @@ def _kv_nan(dtype):
 class Lockstep:
     def __init__(self, w, flags=0, track=None, device="cuda", oracle_flags=0, tau=None, r=None,
                  W=None, sync_amend=False, layer=0, amend_stream=None, prefill=None,
-                 bands=None):
+                 bands=None, force=True):
+        """force=False passes overrides through unchanged: for runs whose
+        decisions are exact in fp32 (distances of exactly zero), where
+        forcing would hide the decision under test."""
         self.w = w
+        self.force = force
         # per-request prefill length (ragged batches); request b decodes
         # position prefill[b] + t at step t
         self.prefill = (np.full(w.B, w.C, np.int32) if prefill is None
@@ -90,6 +118,9 @@ class Lockstep:
                                  kv_fp32=(w.kv == "fp32"), flags=oracle_flags)
         self.out = torch.empty((B, w.Hq, d), dtype=torch.float32, device=device)
         self.stats = []
+        self.n_decisions = 0      # (request, head) decisions of active requests so far
+        self.n_forced_tau = 0
+        self.n_forced_tie = 0
 
     def step(self, t, seq_lens=None, override=None, compare=True, q=None):
         return self.finish(self.launch(t, seq_lens, override, q), compare)
@@ -112,14 +143,21 @@ class Lockstep:
         self.layer.append_kv(self.view, k_new, v_new, self.pos)
         self.seq.copy_(torch.as_tensor(seq_h))
         res = self.orc.step(self.Kg, self.Vg, seq_h, q_h, override=override, track=self.track)
-        forced = np.full((B, w.Hq), -2, np.int32) if override is None else override.copy()
-        flag = (res["near_tau"] | res["near_tie"]).astype(bool) & (forced == -2)
-        forced[flag] = np.where(res["hit"][flag] != 0, res["p"][flag], -1)
+        if self.force:
+            forced, flag, n_tau, n_tie = force_near(res, override)
+        else:
+            forced = (np.full((B, w.Hq), -2, np.int32) if override is None
+                      else np.array(override, np.int32))
+            flag, n_tau, n_tie = np.zeros((B, w.Hq), bool), 0, 0
+        self.n_decisions += int((seq_h > 0).sum()) * w.Hq
+        self.n_forced_tau += n_tau
+        self.n_forced_tie += n_tie
         ov = torch.as_tensor(forced, device=self.dev)
         qd = torch.as_tensor(q_h, device=self.dev)
         self.layer.decode_step(self.view, qd, self.out, ov)
         # keep the step's device inputs alive until it has run
-        return {"t": t, "res": res, "flag": flag, "keep": (k_new, v_new, ov, qd)}
+        return {"t": t, "res": res, "flag": flag, "n_tau": n_tau, "n_tie": n_tie,
+                "keep": (k_new, v_new, ov, qd)}
 
     def finish(self, pending, compare=True):
         """Synchronise and compare the step launched by launch()."""
@@ -127,11 +165,72 @@ class Lockstep:
         res, t = pending["res"], pending["t"]
         p_g, hit_g, rel_g = self.layer.debug_last()
         out_g = self.out.cpu().numpy().astype(np.float64)
-        info = {"t": t, "forced": int(pending["flag"].sum()), "hits": int(res["hit"].sum()),
+        info = {"t": t, "forced": int(pending["flag"].sum()), "forced_tau": pending["n_tau"],
+                "forced_tie": pending["n_tie"], "hits": int(res["hit"].sum()),
                 "p_gpu": p_g, "hit_gpu": hit_g, "res": res, "out_gpu": out_g}
         if compare:
             self.check(res, p_g, hit_g, out_g, t)
+            check_forced_share(self.n_forced_tau + self.n_forced_tie, self.n_decisions,
+                               "step %d" % t)
         return info
+
+    def run_unsynced(self, t0, steps, streams):
+        """Steps t0 .. t0+steps-1 enqueued back to back, step t's append and
+        decode on streams[t % len(streams)], with no host synchronisation
+        between them: the oracle decides every step first, each step gets its
+        own input and output buffers, and all outputs are compared after one
+        final synchronisation.  Returns the number of head hits."""
+        w, B = self.w, self.w.B
+        staged = []
+        for t in range(t0, t0 + steps):
+            seq_h = (self.prefill + t + 1).astype(np.int32)
+            pos_h = (self.prefill + t).astype(np.int32)
+            res = self.orc.step(self.Kg, self.Vg, seq_h, self.q[t], track=self.track)
+            forced, _, n_tau, n_tie = force_near(res)
+            self.n_decisions += int((seq_h > 0).sum()) * w.Hq
+            self.n_forced_tau += n_tau
+            self.n_forced_tie += n_tie
+            m_idx = torch.as_tensor(pos_h, device=self.dev, dtype=torch.long)
+            bi = torch.arange(B, device=self.dev)
+            seq = torch.as_tensor(seq_h, device=self.dev)
+            view = mac.make_kv_view(self.kc, self.vc, seq, self.table,
+                                    num_pages=self.kc.shape[0] if self.paged else 0)
+            staged.append({"res": res, "seq": seq, "view": view,
+                           "pos": torch.as_tensor(pos_h, device=self.dev),
+                           "k": self.K[bi, :, m_idx].contiguous(),
+                           "v": self.V[bi, :, m_idx].contiguous(),
+                           "q": torch.as_tensor(self.q[t], device=self.dev),
+                           "ov": torch.as_tensor(forced, device=self.dev),
+                           "out": torch.full_like(self.out, float("nan"))})
+        torch.cuda.synchronize()
+        for i, x in enumerate(staged):
+            s = streams[(t0 + i) % len(streams)]
+            self.layer.append_kv(x["view"], x["k"], x["v"], x["pos"], s)
+            self.layer.decode_step(x["view"], x["q"], x["out"], x["ov"], s)
+        torch.cuda.synchronize()
+        hits = 0
+        mask = np.ones((B, w.Hq), bool) if self.track is None else self.track.astype(bool)
+        for i, x in enumerate(staged):
+            res, g = x["res"], x["out"].cpu().numpy().astype(np.float64)
+            o = res["out"][mask]
+            err = np.abs(g[mask] - o)
+            assert np.all(np.isfinite(g[mask])), ("non-finite output", t0 + i)
+            assert err.max() <= MAX_ABS, ("max-abs", t0 + i, float(err.max()))
+            rel = np.linalg.norm(g[mask] - o, axis=-1) / np.maximum(np.linalg.norm(o, axis=-1),
+                                                                    1e-30)
+            assert rel.max() <= ROW_REL, ("row-rel", t0 + i, float(rel.max()))
+            self.stats.append((float(err.max()), float(rel.max())))
+            hits += int(res["hit"].sum())
+        p_g, hit_g, _ = self.layer.debug_last()
+        last = staged[-1]["res"]
+        assert np.array_equal(hit_g, last["hit"]) and np.array_equal(p_g, last["p"])
+        check_forced_share(self.n_forced_tau + self.n_forced_tie, self.n_decisions, "unsynced")
+        return hits
+
+    def forced_summary(self):
+        return "forced %d (near tau %d, near tie %d) of %d decisions" % (
+            self.n_forced_tau + self.n_forced_tie, self.n_forced_tau, self.n_forced_tie,
+            self.n_decisions)
 
     def check(self, res, p_g, hit_g, out_g, t):
         assert np.array_equal(hit_g, res["hit"]), ("decision mismatch", t,

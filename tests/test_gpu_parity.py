@@ -18,17 +18,16 @@ def _run(w, steps, **kw):
     print("case", w.name, "B", w.B, "Hq", w.Hq, "Hkv", w.Hkv, "C", w.C, "steps", steps,
           w.kv, w.layout, kw, flush=True)
     ls = Lockstep(w, **kw)
-    hits = forced = 0
+    hits = 0
     try:
         for t in range(steps):
             info = ls.step(t)
             hits += info["hits"]
-            forced += info["forced"]
     finally:
         ls.close()
     emax = max(e for e, _ in ls.stats)
     rmax = max(r for _, r in ls.stats)
-    print("  hits", hits, "of", steps * w.B * w.Hq, "forced", forced,
+    print("  hits", hits, "of", steps * w.B * w.Hq, ls.forced_summary(),
           "max-abs %.2e row-rel %.2e" % (emax, rmax), flush=True)
     return hits, ls
 

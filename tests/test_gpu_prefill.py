@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_harness import MAX_ABS, ROW_REL
+from gpu_harness import MAX_ABS, ROW_REL, check_forced_share, force_near
 from workloads import bf16_bits, get_config, kv_logical, page_table, queries, scaled, to_paged
 
 pytestmark = pytest.mark.gpu
@@ -39,12 +39,13 @@ def _prefill_case(w, lens=None, bands=None, flags=0, oflags=0):
     ov = np.full((B, N, Hq), -2, np.int32)
     want_p = np.full((B, N, Hq), -1, np.int32)
     want_o = np.zeros((B, N, Hq, d))
-    keys = 0
+    keys = n_tau = n_tie = 0
     for t in range(N):
         seq = np.where(t < lens, t + 1, 0).astype(np.int32)
         res = orc.step(Kg, Vg, seq, q[t])
-        flag = (res["near_tau"] | res["near_tie"]).astype(bool)
-        ov[:, t][flag] = np.where(res["hit"][flag] != 0, res["p"][flag], -1)
+        ov[:, t], _, a, b = force_near(res)
+        n_tau += a
+        n_tie += b
         want_p[:, t] = np.where(res["hit"] != 0, res["p"], -1)
         want_o[:, t] = res["out"]
         keys += int(res["kv_tokens"].sum())
@@ -76,7 +77,9 @@ def _prefill_case(w, lens=None, bands=None, flags=0, oflags=0):
     rel = np.linalg.norm(g - o, axis=-1) / np.maximum(np.linalg.norm(o, axis=-1), 1e-30)
     hits = int((want_p >= 0).sum())
     print("  hits", hits, "of", int(lens.sum()) * Hq, "forced", int((ov != -2).sum()),
+          "(near tau %d, near tie %d)" % (n_tau, n_tie),
           "max-abs %.2e row-rel %.2e" % (err.max(), rel.max()), flush=True)
+    check_forced_share(n_tau + n_tie, int(lens.sum()) * Hq, w.name)
     assert err.max() <= MAX_ABS and rel.max() <= ROW_REL
     assert st["prefill_tokens"] == lens.sum()
     assert st["prefill_decisions"] == lens.sum() * Hq

@@ -202,10 +202,12 @@ def test_all_requests_idle_then_resume():
 
 def test_tau_zero_hits_only_exact_repeats():
     """tau = 0: a hit needs distance exactly 0.  Repeating the previous step's
-    query hits it (span [m-1-r+1, m]); a fresh query misses."""
+    query hits it (span [m-1-r+1, m]); a fresh query misses.  Distances of
+    exactly zero are exact in fp32, so nothing is forced: every decision,
+    exact ties included, is the GPU's own."""
     from gpu_harness import Lockstep
     w = _case(steps=10)
-    ls = Lockstep(w, tau=0.0)
+    ls = Lockstep(w, tau=0.0, force=False)
     try:
         q = ls.q
         # steps 4 and 5 repeat step 3's query, step 8 repeats step 7's
@@ -302,3 +304,28 @@ def test_misaligned_pointers_rejected_on_host():
     torch.cuda.synchronize()
     assert torch.isfinite(out).all() and out.abs().sum() > 0
     assert pl.layer.stats()["steps"] == 1
+
+
+@pytest.mark.parametrize("form", ["async", "fused", "stale", "sync"])
+def test_alternating_streams_match_oracle(form):
+    """Calls of one handle on two streams, enqueued back to back with no host
+    synchronisation: each call must wait for the previous one's work on the
+    other stream (its match rewrites the decisions and partials the previous
+    reduce reads), in every amend form; all outputs against the oracle."""
+    from gpu_harness import Lockstep
+    flags, oflags = {"async": (0, 0), "fused": (mac.MAC_F_FUSED_AMEND, 0),
+                     "stale": (mac.MAC_F_STALE_RING, oracle.F_STALE_RING),
+                     "sync": (mac.MAC_F_SYNC_AMEND, 0)}[form]
+    w = _case(B=4, C=3000, steps=24, rho=("const", 0.985 if form == "stale" else 0.965))
+    ls = Lockstep(w, flags=flags, oracle_flags=oflags)
+    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    try:
+        hits = 0
+        for t in range(4):                      # warm the ring up, synchronised
+            hits += ls.step(t)["hits"]
+        hits += ls.run_unsynced(4, w.steps - 4, [s0, s1])
+    finally:
+        torch.cuda.synchronize()
+        ls.close()
+    print("  hits", hits, ls.forced_summary(), flush=True)
+    assert hits > 0

@@ -94,15 +94,14 @@ def test_random_configuration(gpu_lib, case):
           "rho %.4f" % c["rho"], "prefill", c["prefill"], "bands", c["bands"], flush=True)
     ls = Lockstep(w, flags=flags, oracle_flags=oflags, sync_amend=c["sync"],
                   prefill=c["prefill"], bands=c["bands"])
-    hits = forced = 0
+    hits = 0
     try:
         for t in range(c["steps"]):
             info = ls.step(t)
             hits += info["hits"]
-            forced += info["forced"]
     finally:
         ls.close()
     emax = max(e for e, _ in ls.stats)
     rmax = max(r for _, r in ls.stats)
-    print("  hits", hits, "of", c["steps"] * c["B"] * c["Hq"], "forced", forced,
+    print("  hits", hits, "of", c["steps"] * c["B"] * c["Hq"], ls.forced_summary(),
           "max-abs %.2e row-rel %.2e" % (emax, rmax), flush=True)
