@@ -253,6 +253,21 @@ mac_status mac_prefill(mac_handle h, const mac_kv_view *kv /* host */, int32_t n
                        const float *q_pre, float *out, const int32_t *override_pos,
                        int32_t *p_out, void *stream);
 
+/* mac_prefill for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same operation, arguments, results and counters, but the scratch lives in
+ * a static device array of 64 MiB per GPU, held by the library until the
+ * process ends, and the call allocates and frees nothing.  The scratch takes
+ * (5 d + 20) * 4 = 2640 bytes per (request, token, query head): calls whose
+ * batch * num_tokens * num_q_heads rows need more than 64 MiB (25,420 rows,
+ * e.g. 1 x 780 x 32) return MAC_EINVAL before any GPU work.  Every call on a
+ * GPU, from any handle, shares that GPU's array: calls that may overlap on
+ * one GPU (other streams, other host threads) race and must be ordered by
+ * the caller. */
+mac_status mac_prefill_noalloc(mac_handle h, const mac_kv_view *kv /* host */, int32_t num_tokens,
+                               const float *q_pre, float *out, const int32_t *override_pos,
+                               int32_t *p_out, void *stream);
+
 /* Synchronise the handle's streams and copy the counters (host). */
 mac_status mac_stats(mac_handle h, mac_stats_t *out /* host */);
 

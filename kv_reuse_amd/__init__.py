@@ -10,7 +10,7 @@ from ._lib import (EXPORTS, LIB_PATH, MAC_BF16, MAC_EHIP, MAC_EINVAL, MAC_ENOMEM
                    MAC_F_TIMING, MAC_FP32, MAC_KV_CONTIGUOUS, MAC_KV_PAGED, MAC_OK, MacConfig,
                    MacError, MacKvView, MacStats, load, mac_append_kv, mac_aux_bytes,
                    mac_config_validate, mac_debug_last, mac_decode_step, mac_destroy, mac_init,
-                   mac_last_error, mac_prefill, mac_reset, mac_stats, mac_status_string, make_config,
+                   mac_last_error, mac_prefill, mac_prefill_noalloc, mac_reset, mac_stats, mac_status_string, make_config,
                    make_kv_view)
 from .layer import MacLayer
 

@@ -24,7 +24,7 @@ MAC_F_UNBALANCED_PLAN = 128
 
 EXPORTS = ["mac_config_validate", "mac_aux_bytes", "mac_init", "mac_destroy", "mac_reset",
            "mac_append_kv", "mac_decode_step", "mac_stats", "mac_debug_last", "mac_last_error",
-           "mac_status_string", "mac_prefill"]
+           "mac_status_string", "mac_prefill", "mac_prefill_noalloc"]
 
 
 class MacError(RuntimeError):
@@ -97,6 +97,8 @@ def load():
     lib.mac_stats.restype = st
     lib.mac_prefill.argtypes = [vp, ctypes.POINTER(MacKvView), i32, vp, vp, vp, vp, vp]
     lib.mac_prefill.restype = st
+    lib.mac_prefill_noalloc.argtypes = [vp, ctypes.POINTER(MacKvView), i32, vp, vp, vp, vp, vp]
+    lib.mac_prefill_noalloc.restype = st
     lib.mac_debug_last.argtypes = [vp, vp, vp, vp]
     lib.mac_debug_last.restype = st
     lib.mac_last_error.argtypes = [vp]
@@ -192,6 +194,13 @@ def mac_decode_step(h, kv, q_pre_rope, out, override_pos=None, stream=None):
 def mac_prefill(h, kv, num_tokens, q_pre, out, override_pos=None, p_out=None, stream=None):
     _check(load().mac_prefill(h, ctypes.byref(kv), int(num_tokens), _ptr(q_pre), _ptr(out),
                               _ptr(override_pos), _ptr(p_out), _stream(stream)), h)
+
+
+def mac_prefill_noalloc(h, kv, num_tokens, q_pre, out, override_pos=None, p_out=None,
+                        stream=None):
+    _check(load().mac_prefill_noalloc(h, ctypes.byref(kv), int(num_tokens), _ptr(q_pre),
+                                      _ptr(out), _ptr(override_pos), _ptr(p_out),
+                                      _stream(stream)), h)
 
 
 def mac_stats(h):

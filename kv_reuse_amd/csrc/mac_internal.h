@@ -131,6 +131,12 @@ hipError_t launch_prefill(const Shape &s, const State &st, const KvView &kv, boo
                           const int32_t *seq_lens, int N, const float *q_pre, float *out,
                           const int32_t *override_pos, int32_t *p_out, void *scratch,
                           hipStream_t stream);
+// Allocation-free prefill: a static device array of PREFILL_STATIC_BYTES per
+// GPU.  prefill_static_scratch_init takes its address on `device` (which must
+// be current), once; prefill_static_scratch returns it (null before init).
+constexpr size_t PREFILL_STATIC_BYTES = size_t(64) << 20;
+hipError_t prefill_static_scratch_init(int device);
+void *prefill_static_scratch(int device);
 // Workgroups of the complete kernel resident per CU (occupancy query).
 int complete_blocks_per_cu(bool kv_fp32, int G, size_t plan_lds_bytes);
 bool supported_group(int G);

@@ -378,6 +378,9 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     hipError_t e = hipGetDevice(&h->device);
     if (e != hipSuccess)
         return bail(MAC_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    e = mac::prefill_static_scratch_init(h->device);
+    if (e != hipSuccess)
+        return bail(MAC_EHIP, std::string("static prefill scratch: ") + hipGetErrorString(e));
     int n_cu = 0;
     e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, h->device);
     if (e != hipSuccess || n_cu < 1)
@@ -686,6 +689,46 @@ mac_status mac_prefill(mac_handle h, const mac_kv_view *kv, int32_t num_tokens,
         h->broken = true;
         return e != hipSuccess ? fail_hip(h, "launch_prefill", e)
                : ef != hipSuccess ? fail_hip(h, "hipFreeAsync", ef) : fail_hip(h, "mark_done", ed);
+    }
+    return MAC_OK;
+}
+
+mac_status mac_prefill_noalloc(mac_handle h, const mac_kv_view *kv, int32_t num_tokens,
+                               const float *q_pre, float *out, const int32_t *override_pos,
+                               int32_t *p_out, void *stream)
+{
+    if (!h)
+        return fail(nullptr, MAC_EINVAL, "handle is NULL");
+    if (h->broken)
+        return fail(h, MAC_ESTATE, "an earlier call failed part-way; call mac_reset first");
+    mac_status s = check_view(h, kv);
+    if (s != MAC_OK)
+        return s;
+    if (num_tokens < 1 || num_tokens > 32768)
+        return fail(h, MAC_EINVAL, "num_tokens must be in [1, 32768]");
+    if (!q_pre || !out)
+        return fail(h, MAC_EINVAL, "q_pre and out must be non-NULL");
+    if (!aligned16(q_pre) || !aligned16(out))
+        return fail(h, MAC_EINVAL, "q_pre and out must be 16-byte aligned");
+    const size_t bytes = mac::prefill_scratch_bytes(h->shape, num_tokens);
+    if (bytes > mac::PREFILL_STATIC_BYTES)
+        return fail(h, MAC_EINVAL, "mac_prefill_noalloc: batch * num_tokens * num_q_heads needs " +
+                                       std::to_string(bytes) + " bytes of scratch, over the " +
+                                       std::to_string(mac::PREFILL_STATIC_BYTES) +
+                                       "-byte static array (use mac_prefill)");
+    void *scratch = mac::prefill_static_scratch(h->device);
+    if (!scratch)
+        return fail(h, MAC_ESTATE, "static prefill scratch not set up on this device");
+    hipStream_t st = stream ? (hipStream_t)stream : h->main_stream;
+    hipError_t e = follow(h, st);
+    if (e == hipSuccess)
+        e = mac::launch_prefill(h->shape, h->st, to_view(h, kv), h->kv_fp32, kv->seq_lens,
+                                num_tokens, q_pre, out, override_pos, p_out, scratch, st);
+    if (e == hipSuccess)
+        e = mark_done(h, st);
+    if (e != hipSuccess) {
+        h->broken = true;
+        return fail_hip(h, "mac_prefill_noalloc", e);
     }
     return MAC_OK;
 }

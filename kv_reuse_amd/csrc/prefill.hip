@@ -21,9 +21,49 @@
 //   prefill_count   counters (tokens, decisions, hits, keys), one atomic
 //                   per (request, KV head) block
 //   prefill_chain_init / _step / prefill_out   the scan and O
+#include <mutex>
+
 #include "mac_device.h"
 
 namespace mac {
+
+// Scratch of mac_prefill_noalloc: one array per GPU, held from the library's
+// load until the process ends.  Host code never passes `scratch` itself to a
+// kernel (on the host the name is a stand-in, not a device address): it takes
+// the device address once per device, at mac_init, and uses that.
+static __device__ __align__(256) unsigned char scratch[PREFILL_STATIC_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+
+}  // namespace
+
+hipError_t prefill_static_scratch_init(int device)
+{
+    if (device < 0 || device >= MAX_DEVICES)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[device])
+        return hipSuccess;
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess)
+        return e;
+    g_scratch_ptr[device] = p;
+    return hipSuccess;
+}
+
+void *prefill_static_scratch(int device)
+{
+    if (device < 0 || device >= MAX_DEVICES)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_ptr[device];
+}
+
 namespace {
 
 // Scratch of one prefill call (device memory; rows = B * N * Hq, row index

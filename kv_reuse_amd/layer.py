@@ -32,6 +32,10 @@ class MacLayer:
     def prefill(self, kv, num_tokens, q_pre, out, override_pos=None, p_out=None, stream=None):
         _lib.mac_prefill(self.h, kv, num_tokens, q_pre, out, override_pos, p_out, stream)
 
+    def prefill_noalloc(self, kv, num_tokens, q_pre, out, override_pos=None, p_out=None,
+                        stream=None):
+        _lib.mac_prefill_noalloc(self.h, kv, num_tokens, q_pre, out, override_pos, p_out, stream)
+
     def stats(self):
         return _lib.mac_stats(self.h)
 
