@@ -244,6 +244,13 @@ class Lockstep:
         assert np.all(np.isfinite(g)), ("non-finite output", t)
         assert err.max() <= MAX_ABS, ("max-abs", t, float(err.max()))
         rel = np.linalg.norm(g - o, axis=-1) / np.maximum(np.linalg.norm(o, axis=-1), 1e-30)
+        if rel.max() > ROW_REL:
+            rel_all = np.full(p_g.shape, 0.0)
+            rel_all[mask] = rel
+            bad = np.argwhere(rel_all > ROW_REL)
+            print("rows over tolerance (b, h, hit, p, row-rel):",
+                  [(int(b), int(h), int(res["hit"][b, h]), int(res["p"][b, h]),
+                    round(float(rel_all[b, h]), 4)) for b, h in bad[:16]], flush=True)
         assert rel.max() <= ROW_REL, ("row-rel", t, float(rel.max()))
         self.stats.append((float(err.max()), float(rel.max())))
 
