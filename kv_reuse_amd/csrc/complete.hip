@@ -25,7 +25,11 @@ __global__ __launch_bounds__(BLOCK) void complete_kernel(Shape s, State st, KvVi
     if (P == 0)
         return;
     const int nW = s.unbalanced ? st.n_workers : active_workers(st.n_workers, P);
-    if (blockIdx.x == 0)
+    // the plan is published by the last block when its waves have no pages
+    // (a small step), else by block 0 (the first dispatch round, whose waves
+    // end first; the last round sets the end of a full launch)
+    const int pub = nW <= ((int)gridDim.x - 1) * WAVES ? (int)gridDim.x - 1 : 0;
+    if ((int)blockIdx.x == pub)
         publish_plan(s, st, s_off, nW);
     const int w = blockIdx.x * WAVES + (threadIdx.x >> 6);
     if (w >= nW)
@@ -38,7 +42,7 @@ __global__ __launch_bounds__(BLOCK) void complete_kernel(Shape s, State st, KvVi
         while (s_off[sg + 1] <= x)
             ++sg;
         const long send = min((long)s_off[sg + 1], x1);
-        const Seg sd = segment(s, st, sg);
+        const Seg sd = plan_segment(s, st, s_off, sg);
         const int b = sd.b, kvh = sd.kvh, hi = sd.hi;
         // head h attends keys [max(start_h, lo), hi] of this segment
         int hs[G];
@@ -143,7 +147,11 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
     if (P == 0)
         return;
     const int nW = s.unbalanced ? st.n_workers : active_workers(st.n_workers, P);
-    if (blockIdx.x == 0)
+    // the plan is published by the last block when its waves have no pages
+    // (a small step), else by block 0 (the first dispatch round, whose waves
+    // end first; the last round sets the end of a full launch)
+    const int pub = nW <= ((int)gridDim.x - 1) * WAVES ? (int)gridDim.x - 1 : 0;
+    if ((int)blockIdx.x == pub)
         publish_plan(s, st, s_off, nW);
     const int wv = threadIdx.x >> 6, lane = lane_id();
     const int w = blockIdx.x * WAVES + wv;
@@ -161,7 +169,7 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
         const long send = min((long)s_off[sg + 1], x1);
         float4 qf[8];   // issued before the segment's bounds are read
         load_qa_rows<G>(s, st, (sg / s.nseg) / s.Hkv, (sg / s.nseg) % s.Hkv, qf);
-        const Seg sd = segment(s, st, sg);
+        const Seg sd = plan_segment(s, st, s_off, sg);
         const int b = sd.b, kvh = sd.kvh, hi = sd.hi;
         constexpr int HPL = MAcc<G>::HPL;
         const unsigned long long half_mask = G > 4 ? __ballot((lane >> 4) & 1) : 0ULL;
@@ -174,6 +182,8 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
             hmax = max(hmax, hs[h]);
         }
         const int first_page = sd.lo / PAGE;
+        int page = first_page + (int)(x - s_off[sg]);
+        const int last = first_page + (int)(send - s_off[sg]) - 1;
         int hsl[HPL];
 #pragma unroll
         for (int v = 0; v < HPL; ++v) {
@@ -182,6 +192,12 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
             else
                 hsl[v] = hs[v];
         }
+        // the segment's first page id is looked up before the A operands are
+        // built, so it arrives together with the queries (G > 4: from the
+        // lane-gathered table rows)
+        PageWalker pw(kv, b, kvh, s.Hkv, page, last);
+        const long off0 = G > 4 ? pw.offset(page, bad)
+                                : kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad) - kb;
         {
             uint4 qa[8];
             build_qa(qf, s.scale_log2, qa);
@@ -189,6 +205,7 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
             for (int i = 0; i < 8; ++i)
                 qlds[wv][i][lane] = qa[i];
         }
+        MPage cur;
         MAcc<G> acc;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -202,17 +219,11 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
             acc.L[v] = 0.f;
             acc.Ml[v] = NEG_INF;
         }
-        int page = first_page + (int)(x - s_off[sg]);
-        const int last = first_page + (int)(send - s_off[sg]) - 1;
         if constexpr (G > 4) {
-            PageWalker pw(kv, b, kvh, s.Hkv, page, last);
             // two waves per SIMD (G = 8 needs ~220 VGPRs): the next page's
             // loads are issued before the current page is computed
-            MPage cur, nxt;
-            {
-                const long off = pw.offset(page, bad);
-                load_mpage(cur, kb + off, vb + off);
-            }
+            MPage nxt;
+            load_mpage(cur, kb + off0, vb + off0);
             kstore_page(cur, klds[wv]);
             while (true) {
                 if (page + 1 <= last) {
@@ -236,16 +247,17 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
             // buffering (which needs more registers than that) does (measured)
             // (the page id comes from a wave-uniform scalar load here: with one
             // page in flight the lane-fetched ids of PageWalker measured slower)
-            MPage cur;
+            (void)pw;
+            long off = off0;
             while (true) {
-                load_mpage(cur, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad),
-                           kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page, bad));
+                load_mpage(cur, kb + off, vb + off);
                 kstore_page(cur, klds[wv]);
                 const int tok0 = page * PAGE;
                 compute_mpage<G>(klds[wv], cur.v, &qlds[wv][0][0], plds[wv], tok0, hi, hsl,
                                  tok0 < hmax || tok0 + PAGE - 1 > hi, half_mask, acc);
                 if (++page > last)
                     break;
+                off = kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad) - kb;
             }
         }
         store_msummary<G>(acc, st.partials + ((long)w + sg) * G * SUMM);

@@ -457,14 +457,59 @@ __device__ __forceinline__ int segment_pages(const Seg &sg)
 }
 
 // Page offsets of every segment in the flattened work list: off[i] = pages
-// of the segments before i, off[nS] = all pages of the step.
+// of the segments before i, off[nS] = all pages of the step.  With
+// s.plan_bounds the plan also keeps each segment's first key (off[nS + 1 +
+// i]) and each request's query position (off[2 nS + 1 + b]), so a wave sets
+// up its first segment from LDS and its first page-table lookup goes out
+// with its query loads.
 __device__ inline void build_plan(const Shape &s, const State &st, int *off)
 {
     const int nS = s.B * s.Hkv * s.nseg;
-    for (int i = threadIdx.x; i < nS; i += blockDim.x)
-        off[i] = segment_pages(segment(s, st, i));
+    for (int i = threadIdx.x; i < nS; i += blockDim.x) {
+        const Seg sd = segment(s, st, i);
+        off[i] = segment_pages(sd);
+        if (s.plan_bounds)
+            off[nS + 1 + i] = sd.lo;
+    }
+    if (s.plan_bounds)
+        for (int b = threadIdx.x; b < s.B; b += blockDim.x)
+            off[2 * nS + 1 + b] = st.m_buf[b];
     __syncthreads();
     block_exclusive_scan(off, nS);
+}
+
+// Segment seg as the plan holds it (LDS) or, for long work lists, as
+// segment() reads it from the decisions.
+__device__ __forceinline__ Seg plan_segment(const Shape &s, const State &st, const int *off, int seg)
+{
+    if (!s.plan_bounds)
+        return segment(s, st, seg);
+    const int nS = s.B * s.Hkv * s.nseg;
+    const int g = seg / s.nseg, part = seg % s.nseg;
+    Seg r;
+    r.b = g / s.Hkv;
+    r.kvh = g % s.Hkv;
+    r.m = off[2 * nS + 1 + r.b];
+    r.lo = off[nS + 1 + seg];
+    // a fused group's part 0 ends where its band part starts
+    r.hi = (s.nseg == 2 && part == 0) ? off[nS + 1 + seg + 1] - 1 : r.m;
+    if (r.m < 0) {
+        r.lo = 0;
+        r.hi = -1;
+    }
+    return r;
+}
+
+// floor(a / b) for 0 <= a < 2^53, b > 0: the fp64 quotient, corrected by one
+// where its rounding crossed an integer.
+__device__ __forceinline__ long div_floor(long a, int b)
+{
+    long q = (long)((double)a / (double)b);
+    if (q * b > a)
+        --q;
+    else if ((q + 1) * b <= a)
+        ++q;
+    return q;
 }
 
 // Waves that take part: every worker gets at least MIN_PAGES_PER_WORKER pages.
@@ -476,7 +521,7 @@ __device__ __forceinline__ int active_workers(int n_workers, int P)
 // Worker w owns flattened pages [w*P/nW, (w+1)*P/nW); owner of page x:
 __device__ __forceinline__ int page_owner(long x, int nW, int P)
 {
-    return (int)(((x + 1) * (long)nW - 1) / P);
+    return (int)div_floor((x + 1) * (long)nW - 1, P);
 }
 
 // Dispatch-round weights.  The grid holds `slots` blocks per CU, dispatched
@@ -510,7 +555,7 @@ __device__ __forceinline__ long long cum_weight(int w, int Nk, int S)
 __device__ __forceinline__ long share_start(const State &st, int w, int nW, int P)
 {
     if (!tilted_plan(st, nW, P))
-        return (long)w * P / nW;
+        return div_floor((long)w * P, nW);
     const int S = st.slots, Nk = nW / S;
     return (long)((long long)P * cum_weight(w, Nk, S) / cum_weight(nW, Nk, S));
 }
@@ -565,10 +610,21 @@ __device__ __forceinline__ void worker_share(const Shape &s, const State &st, co
     x1 = off[sg] + (long)(j + 1) * n / kk;
 }
 
-// Last segment i with off[i] <= x (segments with no pages are skipped by the
-// caller).
+// Last segment i with off[i] <= x, which holds page x (x < off[nS]): up to
+// 4096 segments a two-level wave ballot over the LDS offsets (two LDS reads
+// per lane), beyond that a binary search.  Called by whole waves.
 __device__ __forceinline__ int find_segment(const int *off, int nS, long x)
 {
+    if (nS <= 64 * 64) {
+        const int lane = lane_id();
+        const int step = (nS + 63) / 64;
+        const int j = lane * step;
+        const unsigned long long b1 = __ballot(j < nS && off[j] <= x);   // off[0] = 0 <= x
+        const int i0 = (63 - __clzll(b1)) * step;
+        const int j2 = i0 + lane;
+        const unsigned long long b2 = __ballot(lane < step && j2 < nS && off[j2] <= x);
+        return i0 + 63 - __clzll(b2);
+    }
     int lo = 0, hi = nS - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
@@ -608,7 +664,11 @@ __device__ inline void publish_plan(const Shape &s, const State &st, const int *
 }
 
 // Bytes of LDS the plan (one int per segment, plus the total) occupies.
-inline size_t plan_lds_bytes(const Shape &s) { return (size_t)(s.B * s.Hkv * s.nseg + 1) * sizeof(int); }
+inline size_t plan_lds_bytes(const Shape &s)
+{
+    const size_t nS = (size_t)s.B * s.Hkv * s.nseg;
+    return (s.plan_bounds ? 2 * nS + 1 + s.B : nS + 1) * sizeof(int);
+}
 
 }  // namespace
 }  // namespace mac

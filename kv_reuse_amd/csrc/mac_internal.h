@@ -87,6 +87,8 @@ struct Shape {
     int32_t nseg;           // work-list segments per group: 1, or 2 when amend is fused
     int32_t ring_bf16;      // ring queries stored as bf16 (rounded to nearest, ties to even)
     int32_t unbalanced;     // plan: the same number of waves per segment (measurement baseline)
+    int32_t plan_bounds;    // the complete kernel's LDS plan also keeps each segment's first
+                            // key and each request's position (small work lists)
 };
 
 struct State {

@@ -387,8 +387,14 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
         return bail(MAC_EHIP, "cannot query the compute-unit count");
 
     const int G = cfg->num_q_heads / cfg->num_kv_heads;
+    // The complete kernel's LDS plan: one offset per work-list segment, and
+    // for short lists each segment's first key and each request's position
+    // too (while that keeps the plan within 3 KB, so three blocks of the
+    // kernel still fit a CU's 160 KB of LDS).
+    const long n_plan = (long)cfg->batch * cfg->num_kv_heads * segments_per_group(*cfg);
+    const bool plan_bounds = (2 * n_plan + 1 + cfg->batch) * (long)sizeof(int) <= 3072;
     const size_t plan_lds =
-        (size_t)(cfg->batch * cfg->num_kv_heads * segments_per_group(*cfg) + 1) * sizeof(int);
+        (size_t)(plan_bounds ? 2 * n_plan + 1 + cfg->batch : n_plan + 1) * sizeof(int);
     h->st.slots = mac::complete_blocks_per_cu(h->kv_fp32, G, plan_lds);
     h->n_blocks = n_cu * h->st.slots;
     h->st.n_workers = h->n_blocks * mac::WAVES;
@@ -474,6 +480,7 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     h->shape.nseg = segments_per_group(*cfg);
     h->shape.ring_bf16 = (cfg->flags & MAC_F_RING_BF16) ? 1 : 0;
     h->shape.unbalanced = (cfg->flags & MAC_F_UNBALANCED_PLAN) ? 1 : 0;
+    h->shape.plan_bounds = plan_bounds ? 1 : 0;
 
     if (amend_stream) {
         h->amend_stream = (hipStream_t)amend_stream;
