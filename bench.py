@@ -18,7 +18,13 @@ kernel.
 Prints one JSON line.  `value` is the attention-phase microseconds per decode
 step (lower is better); the line also carries achieved HBM GB/s, tokens/s, the
 roofline of the dominant kernel (complete), the in-house full-attention kernel
-on the same cache and the fp64 oracle timed on a bounded sample.
+on the same cache and the fp64 oracle timed on a bounded sample.  Each timed
+step starts from an idle GPU (the counters are read between steps), so `value`
+includes the decode call's own launch latency; `loop_us_per_step` gives the
+back-to-back figures.  With the default workload the line also carries
+`workloads`: compact records of the other shapes (the CPU-sized 4K workload
+over all 256 steps, the 32q/4kv MoE shape at r = 64, 256 and 1024, continuous
+generation over 32 layers), each MAC against full attention on its own cache.
 """
 import argparse
 import json
@@ -32,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+CPU_WARM, CPU_STEPS = 8, 16      # oracle sample at the headline shape: warm-up, timed steps
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "complete_kernel_b16_128k_traffic.json")
 # sources the complete kernel is built from: the counters are void once they change
 KERNEL_SRCS = [os.path.join(ROOT, "kv_reuse_amd", "csrc", f)
@@ -67,6 +74,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline-kernel", action="store_true")
     ap.add_argument("--no-32k", action="store_true", help="skip the 32K speedup point")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other workloads' sub-records (CPU-sized 4K, MoE 122K at "
+                         "r = 64/256/1024, continuous generation)")
     ap.add_argument("--figures", nargs="?", const="fig4,fig5,fig8a,fig8b", default=None,
                     help="synthetic analogs of the pages' Figures 4, 5 and 8 (one JSON line); "
                          "optionally a comma list of fig4, fig5, fig8a, fig8b")
@@ -206,6 +216,22 @@ def speedup_point(name, steps=24, warmup=40):
             prev = st
         bn.layer.close()
         res[label] = (float(np.mean(att)), float(np.sum(hits)) / (len(hits) * w.B * w.Hq))
+    # per-kernel HIP events (MAC_F_TIMING), the same steps and scrub
+    kernels = {}
+    for label, flags in (("mac", 0), ("full", mac.MAC_F_DISABLE_REUSE)):
+        bn = Bench(w, flags | mac.MAC_F_TIMING, kc, vc, paged, table)
+        kern, toks, prev = {}, 0, None
+        for t in range(total):
+            st = bn.step(t, q_dev[t], k_rows[t], v_rows[t], scrub)
+            if t >= warmup:
+                for k in ("match", "complete", "reduce", "amend"):
+                    kern.setdefault(k, []).append(st["last_us_" + k])
+                toks += st["kv_tokens_critical"] - prev["kv_tokens_critical"]
+            prev = st
+        bn.layer.close()
+        kv = toks * 2 * w.d * w.kv_elem_bytes / steps
+        kernels[label] = kernel_rates(w, {k: float(np.mean(v)) for k, v in kern.items()}, kv)
+        kernels[label]["kv_bytes_per_step"] = kv
     graph = fused_graph_loops(w, kc, vc, paged, table, k_rows, v_rows, q_dev, warmup)
     return {"workload": name, "context": w.C, "batch": w.B,
             "mac_attention_us": res["mac"][0], "full_attention_us": res["full"][0],
@@ -216,7 +242,7 @@ def speedup_point(name, steps=24, warmup=40):
             "mac_fused_amend_attention_us": res["mac_fused_amend"][0],
             "mac_sync_amend_attention_us": res["mac_sync_amend"][0],
             "speedup_fused_amend": res["full"][0] / res["mac_fused_amend"][0],
-            "steps": steps, "warmup": warmup}
+            "kernels": kernels, "steps": steps, "warmup": warmup}
 
 
 def fused_graph_loops(w, kc, vc, paged, table, k_rows, v_rows, q_dev, start, steps=16):
@@ -271,21 +297,149 @@ def fused_graph_loops(w, kc, vc, paged, table, k_rows, v_rows, q_dev, start, ste
     return out
 
 
-def contgen(args):
+def workload_cache(w, total):
+    """K/V of a workload in HBM (paged or contiguous) and the rows appended
+    during `total` steps, and its queries, all on the GPU."""
+    import torch
+    from workloads import kv_logical, page_table, queries, to_paged
+    K, V = kv_logical(w, "cuda")
+    idx = torch.arange(w.C, w.C + total, device="cuda")
+    k_rows = K[:, :, idx].permute(2, 0, 1, 3).contiguous()
+    v_rows = V[:, :, idx].permute(2, 0, 1, 3).contiguous()
+    q_dev = torch.as_tensor(queries(w, steps=total), device="cuda")
+    paged = w.layout == "paged"
+    if paged:
+        tab = page_table(w)
+        cache = (to_paged(K, tab), to_paged(V, tab), True, torch.as_tensor(tab, device="cuda"))
+        del K, V
+    else:
+        cache = (K, V, False, None)
+    return cache, k_rows, v_rows, q_dev
+
+
+def measure(w, flags, cache, k_rows, v_rows, q_dev, warm, steps):
+    """Two passes over the same steps from a fresh ring: the attention phase
+    between two stream events per step (with the per-head decisions read
+    after each step), then the library's per-kernel HIP events."""
+    import kv_reuse_amd as mac
+    G = w.Hq // w.Hkv
+    out = {}
+    for timing in (False, True):
+        fl = flags | (mac.MAC_F_TIMING if timing else mac.MAC_F_RECORD_DEBUG)
+        bn = Bench(w, fl, *cache)
+        span, hits, toks, grp, kern, prev = [], 0, 0, 0, {}, None
+        for t in range(warm + steps):
+            st = bn.step(t, q_dev[t], k_rows[t], v_rows[t])
+            if t >= warm:
+                if timing:
+                    for k in ("match", "complete", "reduce", "amend"):
+                        kern.setdefault(k, []).append(st["last_us_" + k])
+                else:
+                    span.append(st["span_us"])
+                    hit = bn.layer.debug_last()[1].reshape(w.B, w.Hkv, G)
+                    grp += int(hit.all(axis=-1).sum())
+                hits += st["hits"] - (prev["hits"] if prev else 0)
+                toks += st["kv_tokens_critical"] - (prev["kv_tokens_critical"] if prev else 0)
+            prev = st
+        bn.layer.close()
+        if timing:
+            assert toks == out["kv_tokens"], "the instrumented pass streamed different bytes"
+            out["kernel_us"] = {k: float(np.mean(v)) for k, v in kern.items()}
+        else:
+            out.update({"attention_us": float(np.mean(span)), "kv_tokens": toks,
+                        "head_hit_rate": hits / (steps * w.B * w.Hq),
+                        "groups_all_hit_rate": grp / (steps * w.B * w.Hkv)})
+    return out
+
+
+def kernel_rates(w, kernel_us, kv_bytes, ring_bytes_per_elem=4):
+    """Achieved GB/s (and fraction of 8 TB/s) of the two streaming kernels from
+    their HIP-event durations: match on the ring queries it scans (plus this
+    step's queries in and the two query copies out), complete on the K/V rows
+    of the union spans plus the post-RoPE queries."""
+    q = w.B * w.Hq * w.d * 4
+    match_bytes = w.B * w.Hq * w.W * w.d * ring_bytes_per_elem + w.B * w.W * 4 + 3 * q
+    out = {}
+    for k, nbytes in (("match", match_bytes), ("complete", kv_bytes + q)):
+        us = kernel_us[k]
+        gbps = nbytes / (us * 1e-6) / 1e9 if us > 0 else None
+        out[k] = {"us": us, "bytes": nbytes, "gbps": gbps,
+                  "frac": gbps / PEAK_HBM_GBS if gbps else None}
+    for k in ("reduce", "amend"):
+        if k in kernel_us:
+            out[k] = {"us": kernel_us[k]}
+    return out
+
+
+def workload_record(name, warm, steps, bands=(None,), loop=True):
+    """Compact record of one workload: MAC (async amend) against the in-house
+    full-attention kernel on the same cache, `steps` steps after `warm`
+    warm-up steps from a fresh ring.  With several bands, one MAC record per
+    band (full attention does not depend on it).  Per record: attention-phase
+    µs/step (synchronised step), tokens/s, KV bytes per step, the complete
+    kernel's achieved GB/s and fraction of 8 TB/s, head-hit and all-hit-group
+    shares, the back-to-back loop µs/step (amend included) and MAC vs full."""
+    import torch
+    import kv_reuse_amd as mac
+    from workloads import get_config, scaled
+    w0 = get_config(name)
+    total = warm + steps
+    assert total <= w0.steps
+    cache, k_rows, v_rows, q_dev = workload_cache(w0, total)
+    row_bytes = 2 * w0.d * w0.kv_elem_bytes
+    q_bytes = w0.B * w0.Hq * w0.d * 4
+
+    def summarise(w, flags):
+        m = measure(w, flags, cache, k_rows, v_rows, q_dev, warm, steps)
+        kv = m.pop("kv_tokens") * row_bytes / steps
+        gbps = (kv + q_bytes) / (m["kernel_us"]["complete"] * 1e-6) / 1e9
+        m.update({"tokens_per_s": w.B / (m["attention_us"] * 1e-6), "kv_bytes_per_step": kv,
+                  "complete_gbps": gbps, "complete_frac": gbps / PEAK_HBM_GBS})
+        if loop:
+            m["loop_us_per_step"] = loop_us(w, flags, cache, q_dev, k_rows, v_rows, min(warm, 8),
+                                            min(steps, 16))
+        return m
+
+    full = summarise(w0, mac.MAC_F_DISABLE_REUSE)
+    recs = []
+    for r in bands:
+        w = w0 if r is None else scaled(w0, r=r)
+        m = summarise(w, 0)
+        m["band"] = w.r
+        m["speedup_vs_full"] = full["attention_us"] / m["attention_us"]
+        if loop:
+            m["loop_speedup_vs_full"] = full["loop_us_per_step"] / m["loop_us_per_step"]
+        recs.append(m)
+    del cache, k_rows, v_rows, q_dev
+    torch.cuda.empty_cache()
+    rec = {"workload": name, "batch": w0.B, "context": w0.C, "q_heads": w0.Hq,
+           "kv_heads": w0.Hkv, "kv_dtype": w0.kv, "kv_layout": w0.layout, "ring": w0.W,
+           "tau": w0.tau, "rho": list(w0.rho), "warmup": warm, "steps": steps,
+           "full_attention": full}
+    if len(recs) == 1:
+        rec["mac"] = recs[0]
+    else:
+        rec["mac_by_band"] = recs
+    return rec
+
+
+def contgen_run(warm, steps, decisions=True):
     """Continuous generation: 32 layers x batch 32, 16384-token prompt then
     generated tokens, K/V appended every step and amend overlapping the next
     layers on a shared stream.  Steady state is measured at the mid-run context
     (position 16384 + 8192): the ring remembers only its last W steps, so the
-    window starts there with a fresh ring, warms up, then times the steps."""
+    window starts there with a fresh ring, warms up, then times the steps.
+    With `decisions`, one more untimed MAC pass over the same steps reads
+    every layer's per-head decisions (share of all-hit KV groups)."""
     import torch
     import kv_reuse_amd as mac
     from workloads import get_config, kv_logical, page_table, queries, scaled, to_paged
     base = get_config("contgen")
-    warm, steps = args.warmup if args.warmup >= base.W + 8 else base.W + 8, args.steps
     total = warm + steps
     ctx0 = base.C + base.steps // 2
     w = scaled(base, C=ctx0, steps=total)
     L = w.layers
+    G = w.Hq // w.Hkv
     t0 = time.perf_counter()
     tab_np = page_table(w)
     table = torch.as_tensor(tab_np, device="cuda")
@@ -307,14 +461,18 @@ def contgen(args):
     main = torch.cuda.current_stream()
     amend = torch.cuda.Stream()
     res = {}
-    for label, flags in (("mac", 0), ("mac_fused_amend", mac.MAC_F_FUSED_AMEND),
-                         ("full", mac.MAC_F_DISABLE_REUSE)):
+    passes = [("mac", 0), ("mac_fused_amend", mac.MAC_F_FUSED_AMEND),
+              ("full", mac.MAC_F_DISABLE_REUSE)]
+    if decisions:
+        passes.append(("decisions", mac.MAC_F_RECORD_DEBUG))
+    for label, flags in passes:
         cfg = mac.make_config(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, ring_size=w.W,
                               band=w.r, tau=w.tau, rope_theta=w.theta, layout=mac.MAC_KV_PAGED,
                               kv_dtype=mac.MAC_BF16, max_seq_len=w.n_cap, flags=flags)
         layers = [mac.MacLayer(cfg, main_stream=main, amend_stream=amend) for _ in range(L)]
         views = [mac.make_kv_view(kcs[i], vcs[i], seq, table, num_pages=kcs[i].shape[0])
                  for i in range(L)]
+        all_hit = []
 
         def run(t):
             pos.fill_(w.C + t)
@@ -322,6 +480,9 @@ def contgen(args):
             for i in range(L):
                 layers[i].append_kv(views[i], krows[i][t], vrows[i][t], pos, main)
                 layers[i].decode_step(views[i], qs[i][t], out, None, main)
+                if label == "decisions" and t >= warm:
+                    hit = layers[i].debug_last()[1].reshape(w.B, w.Hkv, G)
+                    all_hit.append(float(hit.all(axis=-1).mean()))
 
         for t in range(warm):
             run(t)
@@ -338,27 +499,45 @@ def contgen(args):
         toks = sum(x["kv_tokens_critical"] for x in st) - k0
         for l in layers:
             l.close()
+        if label == "decisions":
+            res["mac"]["groups_all_hit_rate"] = float(np.mean(all_hit))
+            continue
         res[label] = {"tokens_per_s": w.B * steps / wall, "ms_per_step": wall * 1e3 / steps,
                       "head_hit_rate": hits / (steps * L * w.B * w.Hq),
                       "kv_bytes_per_step": toks * 2 * w.d * 2 / steps,
                       "hbm_gbps": toks * 2 * w.d * 2 / wall / 1e9}
+        res[label]["hbm_frac"] = res[label]["hbm_gbps"] / PEAK_HBM_GBS
+    del kcs, vcs, krows, vrows, qs
+    torch.cuda.empty_cache()
+    return {"workload": "contgen", "batch": w.B, "layers": L, "context_at_window": ctx0,
+            "q_heads": w.Hq, "kv_heads": w.Hkv, "ring": w.W, "band": w.r, "tau": w.tau,
+            "rho": list(base.rho), "jump_every": base.jump_every, "warmup": warm,
+            "steps": steps, "mac": res["mac"], "mac_fused_amend": res["mac_fused_amend"],
+            "full_attention": res["full"],
+            "speedup_vs_full": res["mac"]["tokens_per_s"] / res["full"]["tokens_per_s"],
+            "speedup_vs_full_fused_amend": (res["mac_fused_amend"]["tokens_per_s"] /
+                                            res["full"]["tokens_per_s"]),
+            "setup_s": setup,
+            "note": "attention path only (append, match, complete, reduce, amend on a second "
+                    "stream shared by the layers); wall clock over the timed steps, no FFN"}
+
+
+def contgen(args):
+    """`--config contgen`: the continuous-generation record as its own line."""
+    from workloads import get_config
+    W = get_config("contgen").W
+    rec = contgen_run(max(args.warmup, W + 8), args.steps)
     line = {
         "metric": "steady-state tokens/s, continuous generation (32 layers, batch 32, GQA 32q/8kv)",
-        "value": res["mac"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps,
-        "warmup": warm, "ms_per_step": res["mac"]["ms_per_step"], "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "contgen", "batch": w.B, "layers": L, "context_at_window": ctx0,
-                   "q_heads": w.Hq, "kv_heads": w.Hkv, "ring": w.W, "band": w.r, "tau": w.tau,
-                   "rho": list(base.rho), "jump_every": base.jump_every,
-                   "note": "attention path only (append, match, complete, reduce, amend on a "
-                           "second stream shared by the layers); no FFN"},
-        "mac": res["mac"], "mac_fused_amend": res["mac_fused_amend"],
-        "full_attention_kernel": res["full"],
-        "speedup_vs_full": res["mac"]["tokens_per_s"] / res["full"]["tokens_per_s"],
-        "speedup_vs_full_fused_amend": (res["mac_fused_amend"]["tokens_per_s"] /
-                                        res["full"]["tokens_per_s"]),
-        "setup_s": setup,
+        "value": rec["mac"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": rec["steps"], "warmup": rec["warmup"], "ms_per_step": rec["mac"]["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {k: rec[k] for k in ("workload", "batch", "layers", "context_at_window",
+                                       "q_heads", "kv_heads", "ring", "band", "tau", "rho",
+                                       "jump_every", "note")},
     }
+    line.update({k: v for k, v in rec.items() if k not in line["config"]})
     print(json.dumps(line), flush=True)
 
 
@@ -595,23 +774,69 @@ def host_cpu():
     return {"model": model, "logical_cpus": os.cpu_count()}
 
 
-def oracle_baseline(w, K, V, qs, n_req, n_steps, flags=0):
-    """fp64 oracle, as it stands, on the first n_req requests for n_steps steps
-    (flags: the oracle's F_* bits; F_DISABLE_REUSE gives its full-attention step)."""
+def oracle_baseline(w, K, V, qs, n_req, n_steps, flags=0, warm=0):
+    """fp64 oracle, as it stands, on the first n_req requests: `warm` untimed
+    steps, then n_steps timed ones; seconds per timed step (flags: the
+    oracle's F_* bits; F_DISABLE_REUSE gives its full-attention step)."""
     import oracle
     from workloads import bf16_bits
     Kg, Vg = [], []
     for b in range(n_req):
         for g in range(w.Hkv):
-            Kg.append(bf16_bits(K[b, g, :w.C + n_steps]))
-            Vg.append(bf16_bits(V[b, g, :w.C + n_steps]))
+            Kg.append(bf16_bits(K[b, g, :w.C + warm + n_steps]))
+            Vg.append(bf16_bits(V[b, g, :w.C + warm + n_steps]))
     orc = oracle.Oracle(n_req, w.Hq, w.Hkv, w.d, w.W, w.r, w.tau, w.theta,
                         kv_fp32=(w.kv == "fp32"), flags=flags)
+    for t in range(warm):
+        orc.step(Kg, Vg, np.full(n_req, w.C + t + 1, np.int32), qs[t, :n_req])
     t0 = time.perf_counter()
-    for t in range(n_steps):
+    for t in range(warm, warm + n_steps):
         orc.step(Kg, Vg, np.full(n_req, w.C + t + 1, np.int32), qs[t, :n_req])
     dt = time.perf_counter() - t0
     return dt / n_steps
+
+
+def cpu_baseline(w, host_sample):
+    """The fp64 oracle on the host cores: the headline shape on a bounded
+    sample (n_req requests, CPU_WARM warm-up steps so the ring holds entries,
+    CPU_STEPS timed, scaled to the batch; full attention on 4 steps), and the
+    CPU-sized 4K workload over all its 256 steps with every thread and with
+    one."""
+    import torch
+    import oracle
+    from workloads import get_config, kv_logical, queries
+    K, V, qs = host_sample
+    n_req = K.shape[0]
+    # the host's threads (OMP_NUM_THREADS when set): the OpenMP runtime is
+    # shared with torch, whose own setting must not decide the oracle's
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    oracle.set_threads(threads)
+    threads = oracle.set_threads(0)
+    sec = oracle_baseline(w, K, V, qs, n_req, CPU_STEPS, warm=CPU_WARM)
+    sec_full = oracle_baseline(w, K, V, qs, n_req, 4, flags=oracle.F_DISABLE_REUSE)
+    w1 = get_config("cpu4k")
+    K1, V1 = kv_logical(w1, "cuda")
+    K1, V1 = K1.cpu(), V1.cpu()
+    q1 = queries(w1)
+    c4k = {"threads": threads,
+           "us_per_step": oracle_baseline(w1, K1, V1, q1, w1.B, w1.steps) * 1e6}
+    oracle.set_threads(1)
+    try:
+        c4k["single_thread_us_per_step"] = oracle_baseline(w1, K1, V1, q1, w1.B, w1.steps) * 1e6
+    finally:
+        oracle.set_threads(threads)
+    c4k["full_attention_us_per_step"] = oracle_baseline(
+        w1, K1, V1, q1, w1.B, 16, flags=oracle.F_DISABLE_REUSE) * 1e6
+    c4k["sample"] = ("the whole CPU-sized workload: 1 request, 8q/2kv fp32, 4096 + 256 steps "
+                     "from an empty ring (full attention: its first 16 steps)")
+    return {"value": sec * 1e6 * (w.B / n_req), "unit": "us/step", "cores": threads,
+            "kind": "oracle", "host": host_cpu(),
+            "full_attention_value": sec_full * 1e6 * (w.B / n_req),
+            "sample": "%d of %d requests (all %d heads each): %d untimed steps fill the ring, "
+                      "then %d timed steps (full attention: 4 steps), scaled by %d/%d to the "
+                      "batch; OpenMP over (request, head), %d threads"
+                      % (n_req, w.B, w.Hq, CPU_WARM, CPU_STEPS, w.B, n_req, threads),
+            "cpu4k": c4k}
 
 
 def main():
@@ -668,7 +893,9 @@ def main():
     host_sample = None
     if not args.no_cpu_baseline:
         n_req = min(2, w.B)
-        host_sample = (K[:n_req, :, :w.C + 8].clone(), V[:n_req, :, :w.C + 8].clone())
+        n_cpu = CPU_WARM + CPU_STEPS
+        host_sample = (K[:n_req, :, :w.C + n_cpu].cpu(), V[:n_req, :, :w.C + n_cpu].cpu(),
+                       queries(w, steps=n_cpu)[:, :n_req].copy())
     if paged:
         del K, V
     torch.cuda.synchronize()
@@ -775,29 +1002,26 @@ def main():
     allhit = loops = None
     if (not args.no_baseline_kernel and args.config == "b16_128k" and not args.set and not args.r
             and not args.band_per_head):
-        wa = scaled(w, rho=("const", 0.97))
-        qa = torch.as_tensor(queries(wa, steps=total), device="cuda")
-        ab = Bench(wa, mac_flags, kc, vc, paged, table)
-        aa, ah, at, prev = [], [], [], None
-        for t in range(min(total, 4 + 16)):
-            st = ab.step(t, qa[t], k_rows[t], v_rows[t])
-            if t >= 4:
-                aa.append(st["span_us"])
-                ah.append(st["hits"] - prev["hits"])
-                at.append(st["kv_tokens_critical"] - prev["kv_tokens_critical"])
-            prev = st
-        ab.layer.close()
         cache = (kc, vc, paged, table)
-        allhit = {"rho": 0.97, "attention_us": float(np.mean(aa)),
-                  "head_hit_rate": float(np.sum(ah)) / (heads * len(ah)),
-                  "kv_bytes_per_step": float(np.mean(at)) * row_bytes,
-                  "speedup_vs_full": (base["attention_us"] / float(np.mean(aa))) if base else None,
-                  "loop_us_per_step": {
-                      "mac": loop_us(wa, 0, cache, qa, k_rows, v_rows, 4, 16),
-                      "mac_fused_amend": loop_us(wa, mac.MAC_F_FUSED_AMEND, cache, qa, k_rows,
-                                                 v_rows, 4, 16),
-                      "mac_sync_amend": loop_us(wa, mac.MAC_F_SYNC_AMEND, cache, qa, k_rows,
-                                                v_rows, 4, 16)}}
+        row_bytes_ = 2 * w.d * w.kv_elem_bytes
+
+        def reuse_point(rho):
+            wa = scaled(w, rho=("const", rho))
+            qa = torch.as_tensor(queries(wa, steps=total), device="cuda")
+            m = measure(wa, mac_flags, cache, k_rows, v_rows, qa, 4, 16)
+            kv = m.pop("kv_tokens") * row_bytes_ / 16
+            m.update({"rho": rho, "kv_bytes_per_step": kv,
+                      "speedup_vs_full": (base["attention_us"] / m["attention_us"]) if base
+                      else None,
+                      "kernels": kernel_rates(wa, m["kernel_us"], kv,
+                                              2 if args.ring_bf16 else 4)})
+            return wa, qa, m
+
+        wa, qa, allhit = reuse_point(0.97)
+        allhit["loop_us_per_step"] = {
+            "mac": loop_us(wa, 0, cache, qa, k_rows, v_rows, 4, 16),
+            "mac_fused_amend": loop_us(wa, mac.MAC_F_FUSED_AMEND, cache, qa, k_rows, v_rows, 4, 16),
+            "mac_sync_amend": loop_us(wa, mac.MAC_F_SYNC_AMEND, cache, qa, k_rows, v_rows, 4, 16)}
         # the mixed workload's decode loop, amend included, for every amend form
         lh = {}
         loops = {"mac": loop_us(w, 0, cache, q_dev, k_rows, v_rows, 4, 16, lh),
@@ -813,42 +1037,44 @@ def main():
         # the stale-by-one ring matches two calls back: at rho = 0.99 the
         # queries of the previous-but-one step are still within tau, so both
         # ring forms hit everywhere and the loops differ by the overlap
-        ws = scaled(w, rho=("const", 0.99))
-        qsd = torch.as_tensor(queries(ws, steps=total), device="cuda")
+        ws, qsd, stale = reuse_point(0.99)
         sh = {}
-        stale = {"rho": 0.99,
-                 "loop_us_per_step": {
-                     "mac": loop_us(ws, 0, cache, qsd, k_rows, v_rows, 4, 16, sh),
-                     "mac_stale_ring": loop_us(ws, mac.MAC_F_STALE_RING, cache, qsd, k_rows,
-                                               v_rows, 4, 16, sh),
-                     "mac_fused_amend": loop_us(ws, mac.MAC_F_FUSED_AMEND, cache, qsd, k_rows,
-                                                v_rows, 4, 16),
-                     "mac_sync_amend": loop_us(ws, mac.MAC_F_SYNC_AMEND, cache, qsd, k_rows,
-                                               v_rows, 4, 16)},
-                 "head_hit_rate": {"mac": sh[0], "mac_stale_ring": sh[mac.MAC_F_STALE_RING]}}
-        allhit["stale_ring_point"] = stale
+        stale.update({
+            "loop_us_per_step": {
+                "mac": loop_us(ws, 0, cache, qsd, k_rows, v_rows, 4, 16, sh),
+                "mac_stale_ring": loop_us(ws, mac.MAC_F_STALE_RING, cache, qsd, k_rows, v_rows,
+                                          4, 16, sh),
+                "mac_fused_amend": loop_us(ws, mac.MAC_F_FUSED_AMEND, cache, qsd, k_rows, v_rows,
+                                           4, 16),
+                "mac_sync_amend": loop_us(ws, mac.MAC_F_SYNC_AMEND, cache, qsd, k_rows, v_rows,
+                                          4, 16)},
+            "loop_head_hit_rate": {"mac": sh[0], "mac_stale_ring": sh[mac.MAC_F_STALE_RING]}})
+        allhit["rho99_point"] = stale
 
     point_32k = None
     if not args.no_32k and args.config == "b16_128k" and not args.set and not args.r:
-        del bench
+        bench = None
         point_32k = speedup_point("llama32k")
+
+    sub = None
+    if (not args.no_workloads and args.config == "b16_128k" and not args.set and not args.r
+            and not args.band_per_head):
+        bench = kc = vc = table = k_rows = v_rows = q_dev = None
+        torch.cuda.empty_cache()
+        from workloads import get_config as _gc
+        sub = {
+            # the CPU-sized workload: all 256 steps from an empty ring
+            "cpu4k": workload_record("cpu4k", 0, 256),
+            # the MoE shape, band swept; W + 8 warm-up steps
+            "moe_122k": workload_record("moe_122k", _gc("moe_122k").W + 8, 16,
+                                        bands=(64, 256, 1024)),
+            # continuous generation at mid-run context, W + 8 warm-up steps
+            "contgen": contgen_run(_gc("contgen").W + 8, 16),
+        }
 
     cpu = None
     if host_sample is not None:
-        n_req = host_sample[0].shape[0]
-        n_steps = 4
-        torch.set_num_threads(1)
-        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        sec = oracle_baseline(w, host_sample[0], host_sample[1], qs, n_req, n_steps)
-        import oracle
-        sec_full = oracle_baseline(w, host_sample[0], host_sample[1], qs, n_req, n_steps,
-                                   flags=oracle.F_DISABLE_REUSE)
-        cpu = {"value": sec * 1e6 * (w.B / n_req), "unit": "us/step", "cores": cores,
-               "kind": "oracle", "host": host_cpu(),
-               "full_attention_value": sec_full * 1e6 * (w.B / n_req),
-               "sample": "%d of %d requests (all %d heads each), first %d decode steps from an "
-                         "empty ring, scaled by %d/%d to the batch" % (n_req, w.B, w.Hq, n_steps,
-                                                                       w.B, n_req)}
+        cpu = cpu_baseline(w, host_sample)
 
     # a measured HBM rate beside the published peak: a plain device copy of
     # 2 GiB (2 GiB read + 2 GiB written)
@@ -910,7 +1136,12 @@ def main():
         "allhit_128k": allhit,
         "speedup_32k": point_32k,
         "cpu_baseline": cpu,
+        "workloads": sub,
         "setup_s": t_setup,
+        "timing_note": ("value: mean over the timed steps of the decode call's span on the "
+                        "decode stream, each step launched onto an idle GPU (launch latency "
+                        "included); warm-up steps as given by --warmup (the AR(1) queries' "
+                        "nearest ring entry is the newest, so a few steps fill what matches)"),
         "bad_input": int(st1["bad_input"]),
     }
     print(json.dumps(line), flush=True)

@@ -79,6 +79,8 @@ def _load(path=None):
     lib.orc_step.argtypes = [_vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32p, _fp, _i32p,
                              _u8p, _dp, _dp, _u8p, _i32p, _dp, _u8p, _u8p, _i32p, _i64p]
     lib.orc_step.restype = ctypes.c_int
+    lib.orc_set_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_threads.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -95,6 +97,11 @@ def _kv(a):
     if a.dtype == np.uint16:
         return a, 0
     raise TypeError("key/value rows must be float32 or bf16 bits (uint16), got %s" % a.dtype)
+
+
+def set_threads(n):
+    """OpenMP threads of Oracle.step (timing only); returns the previous count."""
+    return int(_load().orc_set_threads(int(n)))
 
 
 def rope(x, m, theta):

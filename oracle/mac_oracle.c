@@ -27,6 +27,7 @@
  * EMPTY = (o = 0, M = -inf, l = 0).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -239,6 +240,16 @@ int orc_nearest(const float *qt, const float *ring_q, const int32_t *ring_pos,
     *d1 = b1;
     *d2 = b2;
     return best;
+}
+
+/* Threads of the batched decode call (OpenMP over (request, head)); returns
+ * the count in use before.  Timing only: results do not depend on it. */
+int orc_set_threads(int n)
+{
+    int before = omp_get_max_threads();
+    if (n > 0)
+        omp_set_num_threads(n);
+    return before;
 }
 
 /* ------------------------------------------------------------ the policy */
