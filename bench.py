@@ -86,6 +86,9 @@ def parse():
                     help="MAC passes with MAC_F_RING_BF16 (ring queries kept as bfloat16)")
     ap.add_argument("--stale-ring", action="store_true",
                     help="MAC passes with MAC_F_STALE_RING (match skips the previous call's entry)")
+    ap.add_argument("--table5", action="store_true",
+                    help="Table 5 analog: match / complete / reduce / attention-phase us at a "
+                         "1024-entry window, batch 1, 32K and 60K context, KV 1-20 %% (one JSON line)")
     ap.add_argument("--prefill", action="store_true",
                     help="Table 8 analog: MAC over a prompt (mac_prefill, unbounded window) vs "
                          "the same engine with reuse off (one JSON line)")
@@ -317,7 +320,7 @@ def workload_cache(w, total):
     return cache, k_rows, v_rows, q_dev
 
 
-def measure(w, flags, cache, k_rows, v_rows, q_dev, warm, steps):
+def measure(w, flags, cache, k_rows, v_rows, q_dev, warm, steps, scrub=None):
     """Two passes over the same steps from a fresh ring: the attention phase
     between two stream events per step (with the per-head decisions read
     after each step), then the library's per-kernel HIP events."""
@@ -329,7 +332,7 @@ def measure(w, flags, cache, k_rows, v_rows, q_dev, warm, steps):
         bn = Bench(w, fl, *cache)
         span, hits, toks, grp, kern, prev = [], 0, 0, 0, {}, None
         for t in range(warm + steps):
-            st = bn.step(t, q_dev[t], k_rows[t], v_rows[t])
+            st = bn.step(t, q_dev[t], k_rows[t], v_rows[t], scrub)
             if t >= warm:
                 if timing:
                     for k in ("match", "complete", "reduce", "amend"):
@@ -539,6 +542,53 @@ def contgen(args):
     }
     line.update({k: v for k, v in rec.items() if k not in line["config"]})
     print(json.dumps(line), flush=True)
+
+
+def table5(args):
+    """Synthetic analog of the pages' Table 5: the attention path at a fixed
+    1024-entry match window, batch 1, 32q/8kv, contiguous bf16 K/V at 32K and
+    60K context.  The queries (AR(1), rho = 0.99) make every head hit its
+    previous step, so each group reads its band plus the tail; the band r
+    sets the share of the context read, KV % = (r + 1) / context, at the
+    pages' 1, 5, 10 and 20 %.  Each step follows a 1 GiB read scrub (the
+    cache fits the 256 MB Infinity Cache); per-kernel HIP events (match;
+    complete, whose plan is the load balancer; reduce) and the attention-phase
+    span, against the in-house full-attention kernel on the same cache.
+    Prints one JSON line."""
+    import torch
+    import kv_reuse_amd as mac
+    from workloads import get_config, scaled
+    warm, steps = 8, 16
+    scrub = [torch.ones(1 << 28, dtype=torch.float32, device="cuda"),
+             torch.zeros((), dtype=torch.float32, device="cuda")]
+    rows = []
+    for C in (32768, 61440):
+        w0 = scaled(get_config("llama32k"), C=C, W=1024, rho=("const", 0.99), steps=warm + steps)
+        cache, k_rows, v_rows, q_dev = workload_cache(w0, warm + steps)
+        full_tok = sum(w0.B * w0.Hkv * (C + t + 1) for t in range(warm, warm + steps))
+        f = measure(w0, mac.MAC_F_DISABLE_REUSE, cache, k_rows, v_rows, q_dev, warm, steps, scrub)
+        for kvp in (1, 5, 10, 20):
+            r = max(1, int(round(kvp / 100.0 * C)) - 1)
+            w = scaled(w0, r=r)
+            m = measure(w, 0, cache, k_rows, v_rows, q_dev, warm, steps, scrub)
+            rows.append({"context": C, "kv_pct_target": kvp, "band": r,
+                         "kv_pct": 100.0 * m["kv_tokens"] / full_tok,
+                         "head_hit_rate": m["head_hit_rate"],
+                         "full_attention_us": f["attention_us"],
+                         "full_attention_complete_us": f["kernel_us"]["complete"],
+                         "match_us": m["kernel_us"]["match"],
+                         "complete_us": m["kernel_us"]["complete"],
+                         "reduce_us": m["kernel_us"]["reduce"],
+                         "amend_us_second_stream": m["kernel_us"]["amend"],
+                         "attention_us": m["attention_us"],
+                         "speedup_vs_full": f["attention_us"] / m["attention_us"]})
+        del cache, k_rows, v_rows, q_dev
+        torch.cuda.empty_cache()
+    print(json.dumps({"table5": rows,
+                      "config": {"workload": "llama32k-shaped, batch 1", "q_heads": 32,
+                                 "kv_heads": 8, "ring": 1024, "tau": 0.3, "rho": 0.99,
+                                 "kv_layout": "contiguous", "warmup": warm, "steps": steps,
+                                 "data": "synthetic"}}), flush=True)
 
 
 def figures(args):
@@ -857,6 +907,9 @@ def main():
         return
     if args.prefill:
         prefill_table8(args)
+        return
+    if args.table5:
+        table5(args)
         return
     if args.figures:
         figures(args)

@@ -13,7 +13,8 @@ namespace {
 // before the band when amend is fused) in LDS; the step's pages, segment
 // after segment, are split into equal contiguous shares, one per active wave.
 // A worker writes one partial summary per segment it touches, into slot
-// (worker + segment), which is unique along the flattened list.
+// (worker + segment), which is unique along the flattened list.  Vector
+// units only: the fp32 cache, and the bf16 cache at G = 1.
 template <typename T, int G>
 __global__ __launch_bounds__(BLOCK) void complete_kernel(Shape s, State st, KvView kv)
 {
@@ -89,8 +90,8 @@ __global__ __launch_bounds__(BLOCK) void complete_kernel(Shape s, State st, KvVi
 }
 
 // ========================================================== complete (MFMA)
-// bf16 cache: the page machinery (MFMA Q.K^T, swizzled K tile, lazy rescale)
-// is in mfma_page.h.
+// bf16 cache, G >= 2: the page machinery (MFMA Q.K^T, swizzled K tile, lazy
+// rescale) is in mfma_page.h.
 
 // Element offsets of the (page, KV head) blocks a wave walks in one segment.
 // Paged caches: the page ids are fetched 64 at a time, one per lane, and each
@@ -271,9 +272,12 @@ hipError_t launch_complete_t(const Shape &s, const State &st, const KvView &kv, 
 {
     const size_t lds = plan_lds_bytes(s);
     if constexpr (std::is_same<T, uint16_t>::value) {
+        // G = 1: one query row is no matrix tile; the vector worker is as fast
+        // on streaming steps and faster on short ones (measured), so the
+        // matrix cores start at G = 2
         switch (s.G) {
-        case 1: hipLaunchKernelGGL(complete_mfma_kernel<1>, dim3(n_blocks), dim3(BLOCK), lds,
-                                   stream, s, st, kv); break;
+        case 1: hipLaunchKernelGGL((complete_kernel<uint16_t, 1>), dim3(n_blocks), dim3(BLOCK),
+                                   lds, stream, s, st, kv); break;
         case 2: hipLaunchKernelGGL(complete_mfma_kernel<2>, dim3(n_blocks), dim3(BLOCK), lds,
                                    stream, s, st, kv); break;
         case 4: hipLaunchKernelGGL(complete_mfma_kernel<4>, dim3(n_blocks), dim3(BLOCK), lds,
@@ -323,7 +327,8 @@ int complete_blocks_per_cu(bool kv_fp32, int G, size_t lds)
         else if (G == 4) MAC_OCC(float, 4); else MAC_OCC(float, 8);
     } else {
         if (G == 1)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_mfma_kernel<1>, BLOCK, lds);
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_kernel<uint16_t, 1>,
+                                                             BLOCK, lds);
         else if (G == 2)
             e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, complete_mfma_kernel<2>, BLOCK, lds);
         else if (G == 4)

@@ -15,8 +15,8 @@
 //   dec_p      [B][Hq] int32        matched position (-1 miss)
 //   dec_start  [B][Hq] int32        first key of the head's span
 //   dec_rel    [B][Hq]              relative distance of the nearest entry
+//   tile_best  [B][Hq][W/64][3]     W > 64, few heads: nearest entry of each 64-slot tile
 //   grp_parts  [B][Hkv][nseg][2] int32  first and last worker whose partial covers a segment
-//   tile_best  [B][Hq][W/64][3]     W > 64: nearest entry of each 64-slot tile
 //   partials   [NW + B*Hkv*nseg][G][SUMM] per-(worker, segment) unnormalised summaries
 //   as_full    [B][Hq][SUMM]        AS_{1:m} of this step, input of amend
 //   band       [Hq]    int32        band r_h of each query head
@@ -43,7 +43,7 @@ constexpr int PAGE = 16;        // tokens per page
 constexpr int BLOCK = 256;      // threads per workgroup (4 waves of 64)
 constexpr int WAVES = BLOCK / 64;
 constexpr int MAX_W = 2048;     // ring slots per (request, head)
-constexpr int TILE_W = 64;      // ring slots one wave scans (the whole ring, or one tile of it)
+constexpr int TILE_W = 64;      // longest ring one match wave holds whole (longer: several waves)
 constexpr int MAX_GROUPS = 4096;  // B * Hkv
 constexpr int MIN_PAGES_PER_WORKER = 1;
 
@@ -108,11 +108,7 @@ struct State {
 };
 
 // Launchers (enqueue only; return the launch status).
-// W > TILE_W: per-tile nearest entries, read by launch_match's kernel.
 // `hidden` is a ring slot this call's match and override ignore (-1: none).
-hipError_t launch_match_tiles(const Shape &s, const State &st, const KvView &kv,
-                              const int32_t *seq_lens, const float *q_pre, int hidden,
-                              hipStream_t stream);
 hipError_t launch_match(const Shape &s, const State &st, const KvView &kv, const int32_t *seq_lens,
                         const float *q_pre, const int32_t *override_pos, float *out, int hidden,
                         hipStream_t stream);

@@ -580,8 +580,6 @@ hipError_t decode_enqueue(mac_ctx *h, const mac_kv_view *kv, const float *q_pre_
     const int hidden = (stale && h->calls > 0) ? (int)((h->calls - 1) % h->cfg.ring_size) : -1;
     if (timing)
         MAC_TRY(hipEventRecord(h->tm[0], st));
-    if (h->shape.reuse && h->cfg.ring_size > mac::TILE_W)
-        MAC_TRY(mac::launch_match_tiles(h->shape, S, v, kv->seq_lens, q_pre_rope, hidden, st));
     MAC_TRY(mac::launch_match(h->shape, S, v, kv->seq_lens, q_pre_rope, override_pos, out,
                               hidden, st));
     // The complete kernel is a persistent grid with equal static shares per

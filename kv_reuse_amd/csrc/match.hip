@@ -58,7 +58,13 @@ struct RingTile {
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
             const int sl = PER * u + sub;
-            v[u] = sl < nslot ? rq[(long)sl * VPR + c] : Vec{};
+            if (sl < nslot) {
+                // read once per step: streaming hint
+                const uint4 t = load_stream(rq + (long)sl * VPR + c);
+                v[u] = *reinterpret_cast<const Vec *>(&t);
+            } else {
+                v[u] = Vec{};
+            }
         }
     }
 
@@ -135,12 +141,174 @@ struct RingTile {
     }
 };
 
-// =========================================================== match tiles
-// Rings longer than one 64-slot tile (the pages' windows of 512-2048 entries,
-// Figure 6, Tables 5 and 7).  Grid (tiles, Hq, B), one wave per tile: the
-// wave loads the tile's 64 pre-RoPE queries (32 KB fp32, 16 KB bf16) and
-// records the tile's nearest entry; the match kernel then reduces the tiles
-// of each head.
+// ================================================================== match
+// One (request, query head) per block.  The head's decision is taken by one
+// wave once the nearest valid ring entry is known; the kernels differ in how
+// they find it.  The match step is latency-bound, so every load that does not
+// depend on the query position (query, angles, stamps, override, the head's
+// counters) is issued before any of them is waited on.  The head then takes
+// its decision (hit iff the relative L2 distance of the nearest valid entry is
+// within tau, compared squared), applies an override, rotates its query
+// (rotate-half RoPE, angle in fp64) and records its key span:
+// [max(p - r + 1, 0), m] on a hit, [0, m] on a miss.
+
+// The head's inputs other than the ring, loaded by the deciding wave.
+struct HeadIn {
+    float qa, qb;      // pre-RoPE query, elements lane and lane + 64
+    double inv;        // inverse frequency of the lane's rotation pair
+    int ov, band, pos_l;
+    unsigned long long old[HEAD_NSTAT];
+};
+
+__device__ __forceinline__ void load_head(const Shape &s, const State &st, const float *q_pre,
+                                          const int32_t *ovr, int b, int h, int hidden,
+                                          HeadIn &in)
+{
+    const long idx = (long)b * s.Hq + h;
+    const int lane = lane_id();
+    in.qa = q_pre[idx * D + lane];
+    in.qb = q_pre[idx * D + lane + 64];
+    in.inv = st.inv_freq[lane];
+    in.ov = ovr ? ovr[idx] : -2;
+    in.band = st.band[h];
+    in.pos_l = (s.reuse && lane < s.W && lane != hidden) ? st.ring_pos[(long)b * s.W + lane] : -1;
+#pragma unroll
+    for (int k = 0; k < HEAD_NSTAT; ++k)
+        in.old[k] = 0;
+    if (lane == 0) {
+        const unsigned long long *hstat = st.head_stats + idx * HEAD_NSTAT;
+#pragma unroll
+        for (int k = 0; k < HEAD_NSTAT; ++k)
+            in.old[k] = hstat[k];
+    }
+}
+
+// This step's query copies: pre-RoPE (for amend) and rotated (for complete);
+// an idle request's output is zero (no group of it gets work).
+__device__ __forceinline__ void store_queries(const State &st, long idx, int m, const HeadIn &in,
+                                              float *out)
+{
+    const int lane = lane_id();
+    if (m >= 0) {
+        st.q_copy[idx * D + lane] = in.qa;
+        st.q_copy[idx * D + lane + 64] = in.qb;
+        float ra, rb;
+        rope_pair(in.qa, in.qb, m, in.inv, ra, rb);
+        st.q_rot[idx * D + lane] = ra;
+        st.q_rot[idx * D + lane + 64] = rb;
+    } else {
+        out[idx * D + lane] = 0.f;
+        out[idx * D + lane + 64] = 0.f;
+    }
+}
+
+// The decision from the nearest valid entry (kd, kp, kj; kp < 0: none), the
+// override, the span and the counters; one wave.
+__device__ __forceinline__ void decide(const Shape &s, const State &st, int b, int h, int m,
+                                       bool bad, const HeadIn &in, float kd, int kp, int kj,
+                                       int hidden)
+{
+    const long idx = (long)b * s.Hq + h;
+    const int lane = lane_id();
+    int slot = -1, p = -1, start = 0;
+    float rel = NAN;
+    int cnt[HEAD_NSTAT] = {0, 0, 0, 0};
+    const bool act = m >= 0;
+    if (act && s.reuse) {
+        const float q2 = wave_sum(in.qa * in.qa + in.qb * in.qb);
+        if (kp >= 0) {
+            rel = q2 > 0.f ? sqrtf(kd / q2) : (kd == 0.f ? 0.f : INFINITY);
+            // relative-L2 test compared squared: D <= tau^2 |q~|^2
+            if (s.tau >= 0.f && kd <= s.tau * s.tau * q2) {
+                slot = kj;
+                p = kp;
+            }
+            if (fabsf(rel - s.tau) < 1e-4f)
+                cnt[HS_NEAR_TAU] = 1;
+        }
+        if (in.ov != -2) {
+            slot = -1;
+            p = -1;
+            if (in.ov >= 0) {
+                // the largest slot holding position ov, 64 slots at a time
+                for (int c0 = 0; c0 < s.W; c0 += 64) {
+                    const int sl = c0 + lane;
+                    const int ps = c0 == 0 ? in.pos_l
+                                           : (sl < s.W ? st.ring_pos[(long)b * s.W + sl] : -1);
+                    const bool mine = sl < s.W && sl != hidden && in.ov <= m && ps == in.ov;
+                    const unsigned long long bal = __ballot(mine);
+                    if (bal) {
+                        slot = c0 + 63 - __clzll(bal);
+                        p = in.ov;
+                    }
+                }
+                if (slot < 0)
+                    cnt[HS_OVR_INVALID] = 1;
+            }
+        }
+        if (slot >= 0)
+            start = max(p - in.band + 1, 0);
+    }
+    if (lane == 0) {
+        st.dec_slot[idx] = slot;
+        st.dec_p[idx] = p;
+        st.dec_start[idx] = start;
+        st.dec_rel[idx] = rel;
+        if (act) {
+            // this wave owns the head's counters: no atomics
+            cnt[slot >= 0 ? HS_HITS : HS_MISSES] = 1;
+            unsigned long long *hstat = st.head_stats + idx * HEAD_NSTAT;
+#pragma unroll
+            for (int k = 0; k < HEAD_NSTAT; ++k)
+                hstat[k] = in.old[k] + (unsigned long long)cnt[k];
+        }
+        if (h == 0 && b == 0) {
+            // the ring slot of this call, from the device's own call count (so a
+            // captured step replays correctly): slot = calls mod W
+            const unsigned long long c = st.stats[ST_STEPS];
+            *st.step_slot = (int)(c % (unsigned long long)s.W);
+            st.stats[ST_STEPS] = c + 1;
+        }
+        if (h == 0) {
+            st.m_buf[b] = m;
+            if (bad)
+                atomicAdd(&st.stats[ST_BAD_INPUT], 1ULL);
+        }
+    }
+}
+
+// Rings of up to 64 entries: one wave, the whole ring in registers
+// (RingTile), loaded with the head's other inputs.
+template <int SLOTS, bool BF16>
+__global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
+                                                   const int32_t *__restrict__ seq_lens,
+                                                   const float *__restrict__ q_pre,
+                                                   const int32_t *__restrict__ ovr,
+                                                   float *__restrict__ out, int hidden)
+{
+    const int h = blockIdx.x, b = blockIdx.y;
+    const long idx = (long)b * s.Hq + h;
+    RingTile<SLOTS, BF16> ring;
+    if (s.reuse)
+        ring.load(s, st, idx, 0, s.W);
+    const int seq = seq_lens[b];
+    HeadIn in;
+    load_head(s, st, q_pre, ovr, b, h, hidden, in);
+    bool bad;
+    const int m = query_position(kv, seq, bad);
+    store_queries(st, idx, m, in, out);
+    float kd = INFINITY;
+    int kp = INT_MIN, kj = -1;
+    if (m >= 0 && s.reuse)
+        ring.scan(q_pre + idx * D, 0, s.W, in.pos_l, m, kd, kp, kj);
+    decide(s, st, b, h, m, bad, in, kd, kp, kj, hidden);
+}
+
+// Rings longer than one 64-slot tile, few heads (too few to give every CU a
+// block of the one-launch kernel below): grid (tiles, Hq, B), one wave per
+// 64-slot tile loads the tile's pre-RoPE queries (32 KB fp32, 16 KB bf16) and
+// records the tile's nearest entry; match_tiled_kernel then reduces the
+// tiles of each head.
 template <bool BF16>
 __global__ __launch_bounds__(64) void match_tiles_kernel(Shape s, State st, KvView kv,
                                                          const int32_t *__restrict__ seq_lens,
@@ -172,189 +340,188 @@ __global__ __launch_bounds__(64) void match_tiles_kernel(Shape s, State st, KvVi
     }
 }
 
-// ================================================================== match
-// Grid (Hq, B), one wave per (request, query head).  A ring of up to 64
-// entries is held in registers (RingTile); a longer one arrives as
-// per-tile nearest entries from match_tiles_kernel.  The kernel is
-// latency-bound, so every load that does not depend on the query position
-// (query, angles, ring, stamps, override, the head's counters) is issued
-// before any of them is waited on.  The head then takes its decision (hit iff
-// the relative L2 distance of the nearest valid entry is within tau, compared
-// squared), applies an override, rotates its query (rotate-half RoPE, angle in
-// fp64) and records its key span: [max(p - r + 1, 0), m] on a hit, [0, m] on
-// a miss.
-template <int SLOTS, bool BF16>
-__global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
-                                                   const int32_t *__restrict__ seq_lens,
-                                                   const float *__restrict__ q_pre,
-                                                   const int32_t *__restrict__ ovr,
-                                                   float *__restrict__ out, int hidden)
+template <int OFF>
+__device__ __forceinline__ void argmin_step(float &kd, int &kp, int &kj)
+{
+    const float d2 = xor_lanes<OFF>(kd);
+    const int p2 = xor_lanes_i<OFF>(kp);
+    const int j2 = xor_lanes_i<OFF>(kj);
+    if (nearer(d2, p2, j2, kd, kp, kj)) {
+        kd = d2;
+        kp = p2;
+        kj = j2;
+    }
+}
+
+// One wave per head: the nearest of the head's tile entries (lane t holds
+// tile t's), then the decision.
+__global__ __launch_bounds__(64) void match_tiled_kernel(Shape s, State st, KvView kv,
+                                                         const int32_t *__restrict__ seq_lens,
+                                                         const float *__restrict__ q_pre,
+                                                         const int32_t *__restrict__ ovr,
+                                                         float *__restrict__ out, int hidden)
 {
     const int h = blockIdx.x, b = blockIdx.y;
     const long idx = (long)b * s.Hq + h;
     const int lane = lane_id();
-    const bool tiled = s.W > TILE_W;
     const int ntiles = (s.W + TILE_W - 1) / TILE_W;
-    unsigned long long *hstat = st.head_stats + idx * HEAD_NSTAT;
-
-    // ---- loads independent of the position
-    RingTile<SLOTS, BF16> ring;
-    if (s.reuse && !tiled)
-        ring.load(s, st, idx, 0, s.W);
-    const int seq = seq_lens[b];
-    const float qa = q_pre[idx * D + lane], qb = q_pre[idx * D + lane + 64];
-    const double inv = st.inv_freq[lane];
-    const int ov = ovr ? ovr[idx] : -2;
-    const int band = st.band[h];
-    const int pos_l =
-        (s.reuse && lane < s.W && lane != hidden) ? st.ring_pos[(long)b * s.W + lane] : -1;
-    unsigned long long old[HEAD_NSTAT] = {};
-    if (lane == 0) {
-#pragma unroll
-        for (int k = 0; k < HEAD_NSTAT; ++k)
-            old[k] = hstat[k];
-    }
-    float td = INFINITY;
-    int tp = INT_MIN, tj = -1;
-    if (s.reuse && tiled && lane < ntiles) {
+    float kd = INFINITY;
+    int kp = INT_MIN, kj = -1;
+    if (s.reuse && lane < ntiles) {
         const float *tb = st.tile_best + (idx * ntiles + lane) * 3;
-        td = tb[0];
-        tp = __float_as_int(tb[1]);
-        tj = __float_as_int(tb[2]);
+        kd = tb[0];
+        kp = __float_as_int(tb[1]);
+        kj = __float_as_int(tb[2]);
     }
-
+    const int seq = seq_lens[b];
+    HeadIn in;
+    load_head(s, st, q_pre, ovr, b, h, hidden, in);
     bool bad;
     const int m = query_position(kv, seq, bad);
-    const bool act = m >= 0;
-    int slot = -1, p = -1, start = 0;
-    float rel = NAN;
-    int cnt[HEAD_NSTAT] = {0, 0, 0, 0};
-    if (act) {
-        st.q_copy[idx * D + lane] = qa;
-        st.q_copy[idx * D + lane + 64] = qb;
-        float ra, rb;
-        rope_pair(qa, qb, m, inv, ra, rb);
-        st.q_rot[idx * D + lane] = ra;
-        st.q_rot[idx * D + lane + 64] = rb;
-    } else {
-        // idle request: its output is zero (no group of it gets work)
-        out[idx * D + lane] = 0.f;
-        out[idx * D + lane + 64] = 0.f;
-    }
-    if (act && s.reuse) {
-        float kd;
-        int kp, kj;
-        if (!tiled) {
-            ring.scan(q_pre + idx * D, 0, s.W, pos_l, m, kd, kp, kj);
-        } else {
-            // nearest entry over the head's tiles
-            kd = td;
-            kp = tp;
-            kj = tj;
-#define MAC_ARGMIN_STEP(OFF)                                                                 \
-    {                                                                                       \
-        const float d2 = xor_lanes<OFF>(kd);                                                \
-        const int p2 = xor_lanes_i<OFF>(kp);                                                \
-        const int j2 = xor_lanes_i<OFF>(kj);                                                \
-        if (nearer(d2, p2, j2, kd, kp, kj)) {                                               \
-            kd = d2;                                                                        \
-            kp = p2;                                                                        \
-            kj = j2;                                                                        \
-        }                                                                                   \
-    }
-            MAC_ARGMIN_STEP(1)
-            MAC_ARGMIN_STEP(2)
-            MAC_ARGMIN_STEP(4)
-            MAC_ARGMIN_STEP(8)
-            MAC_ARGMIN_STEP(16)
-            MAC_ARGMIN_STEP(32)
-#undef MAC_ARGMIN_STEP
-        }
-        const float q2 = wave_sum(qa * qa + qb * qb);
-        if (kp >= 0) {
-            rel = q2 > 0.f ? sqrtf(kd / q2) : (kd == 0.f ? 0.f : INFINITY);
-            // relative-L2 test compared squared: D <= tau^2 |q~|^2
-            if (s.tau >= 0.f && kd <= s.tau * s.tau * q2) {
-                slot = kj;
-                p = kp;
+    store_queries(st, idx, m, in, out);
+    argmin_step<1>(kd, kp, kj);
+    argmin_step<2>(kd, kp, kj);
+    argmin_step<4>(kd, kp, kj);
+    argmin_step<8>(kd, kp, kj);
+    argmin_step<16>(kd, kp, kj);
+    argmin_step<32>(kd, kp, kj);
+    if (m < 0)
+        kp = INT_MIN;
+    decide(s, st, b, h, m, bad, in, kd, kp, kj, hidden);
+}
+
+// Longer rings (the pages' windows of 512-2048 entries, Figure 6, Tables 5
+// and 7) with enough heads for two blocks per CU: up to MATCH_WAVES waves per
+// head, wave w scanning sub-tiles w, w + waves, ... of SUB = 16 slots (in
+// RingTile's layouts, so each slot's distance is summed as in the one-wave
+// kernel), two sub-tiles in flight per wave; the waves' nearest entries meet
+// in LDS and wave 0 decides.  One launch streams the whole ring, and at <= 128
+// registers two blocks share a CU, so one block's deciding wave overlaps the
+// other's scan.
+constexpr int MATCH_WAVES = 8;
+
+template <bool BF16>
+__global__ __launch_bounds__(64 * MATCH_WAVES) __attribute__((amdgpu_waves_per_eu(4))) void
+match_wide_kernel(
+    Shape s, State st, KvView kv, const int32_t *__restrict__ seq_lens,
+    const float *__restrict__ q_pre, const int32_t *__restrict__ ovr, float *__restrict__ out,
+    int hidden)
+{
+    constexpr int SUB = 16;
+    __shared__ float s_d[MATCH_WAVES];
+    __shared__ int s_p[MATCH_WAVES], s_j[MATCH_WAVES];
+    const int h = blockIdx.x, b = blockIdx.y;
+    const long idx = (long)b * s.Hq + h;
+    const int lane = lane_id(), wv = threadIdx.x >> 6, nwv = blockDim.x >> 6;
+    const int nsub = (s.W + SUB - 1) / SUB;
+    const int seq = seq_lens[b];
+    bool bad;
+    const int m = query_position(kv, seq, bad);
+    float kd = INFINITY;
+    int kp = INT_MIN, kj = -1;
+    if (m >= 0 && s.reuse) {
+        // two sub-tiles per wave in flight: the next one's loads are issued
+        // before the current one is scanned
+        RingTile<SUB, BF16> ring[2];
+        int pos_l[2];
+        auto fetch = [&](int k, int j) {
+            const int base = j * SUB, nslot = min(SUB, s.W - base);
+            ring[k].load(s, st, idx, base, nslot);
+            pos_l[k] = (lane < nslot && base + lane != hidden)
+                           ? st.ring_pos[(long)b * s.W + base + lane]
+                           : -1;
+        };
+        auto scan = [&](int k, int j) {
+            const int base = j * SUB, nslot = min(SUB, s.W - base);
+            float d;
+            int p, jj;
+            ring[k].scan(q_pre + idx * D, base, nslot, pos_l[k], m, d, p, jj);
+            if (nearer(d, p, jj, kd, kp, kj)) {
+                kd = d;
+                kp = p;
+                kj = jj;
             }
-            if (fabsf(rel - s.tau) < 1e-4f)
-                cnt[HS_NEAR_TAU] = 1;
+        };
+        int j = wv;
+        if (j < nsub)
+            fetch(0, j);
+        while (j < nsub) {
+            if (j + nwv < nsub)
+                fetch(1, j + nwv);
+            scan(0, j);
+            j += nwv;
+            if (j >= nsub)
+                break;
+            if (j + nwv < nsub)
+                fetch(0, j + nwv);
+            scan(1, j);
+            j += nwv;
         }
-        if (ov != -2) {
-            slot = -1;
-            p = -1;
-            if (ov >= 0) {
-                // the largest slot holding position ov, 64 slots at a time
-                for (int c0 = 0; c0 < s.W; c0 += 64) {
-                    const int sl = c0 + lane;
-                    const int ps = c0 == 0 ? pos_l
-                                           : (sl < s.W ? st.ring_pos[(long)b * s.W + sl] : -1);
-                    const bool mine = sl < s.W && sl != hidden && ov <= m && ps == ov;
-                    const unsigned long long bal = __ballot(mine);
-                    if (bal) {
-                        slot = c0 + 63 - __clzll(bal);
-                        p = ov;
-                    }
-                }
-                if (slot < 0)
-                    cnt[HS_OVR_INVALID] = 1;
-            }
-        }
-        if (slot >= 0)
-            start = max(p - band + 1, 0);
     }
     if (lane == 0) {
-        st.dec_slot[idx] = slot;
-        st.dec_p[idx] = p;
-        st.dec_start[idx] = start;
-        st.dec_rel[idx] = rel;
-        if (act) {
-            // this wave owns the head's counters: no atomics
-            cnt[slot >= 0 ? HS_HITS : HS_MISSES] = 1;
-#pragma unroll
-            for (int k = 0; k < HEAD_NSTAT; ++k)
-                hstat[k] = old[k] + (unsigned long long)cnt[k];
-        }
-        if (h == 0 && b == 0) {
-            // the ring slot of this call, from the device's own call count (so a
-            // captured step replays correctly): slot = calls mod W
-            const unsigned long long c = st.stats[ST_STEPS];
-            *st.step_slot = (int)(c % (unsigned long long)s.W);
-            st.stats[ST_STEPS] = c + 1;
-        }
-        if (h == 0) {
-            st.m_buf[b] = m;
-            if (bad)
-                atomicAdd(&st.stats[ST_BAD_INPUT], 1ULL);
+        s_d[wv] = kd;
+        s_p[wv] = kp;
+        s_j[wv] = kj;
+    }
+    __syncthreads();
+    if (wv != 0)
+        return;
+    // the head's other inputs: loaded after the scan, whose ring tiles take
+    // the registers (two blocks per CU: at most 128 per lane)
+    HeadIn in;
+    load_head(s, st, q_pre, ovr, b, h, hidden, in);
+    store_queries(st, idx, m, in, out);
+    // nearest over the waves (a strict total order: the result does not
+    // depend on the order of the comparisons)
+    for (int k = 1; k < nwv; ++k) {
+        if (nearer(s_d[k], s_p[k], s_j[k], kd, kp, kj)) {
+            kd = s_d[k];
+            kp = s_p[k];
+            kj = s_j[k];
         }
     }
+    decide(s, st, b, h, m, bad, in, kd, kp, kj, hidden);
 }
 
 }  // namespace
-
-hipError_t launch_match_tiles(const Shape &s, const State &st, const KvView &kv,
-                              const int32_t *seq_lens, const float *q_pre, int hidden,
-                              hipStream_t stream)
-{
-    const dim3 grid((s.W + TILE_W - 1) / TILE_W, s.Hq, s.B);
-    if (s.ring_bf16)
-        hipLaunchKernelGGL(match_tiles_kernel<true>, grid, dim3(64), 0, stream, s, st, kv,
-                           seq_lens, q_pre, hidden);
-    else
-        hipLaunchKernelGGL(match_tiles_kernel<false>, grid, dim3(64), 0, stream, s, st, kv,
-                           seq_lens, q_pre, hidden);
-    return hipGetLastError();
-}
 
 hipError_t launch_match(const Shape &s, const State &st, const KvView &kv, const int32_t *seq_lens,
                         const float *q_pre, const int32_t *override_pos, float *out, int hidden,
                         hipStream_t stream)
 {
-    // ring slots held in registers: the whole ring up to 64 (a longer one is
-    // read by match_tiles_kernel)
-    const int slots = s.W > 32 ? 64 : s.W > 16 ? 32 : 16;
     const dim3 grid(s.Hq, s.B);
+    if (s.W > TILE_W) {
+        const int n_cu = st.n_workers / (st.slots * WAVES);
+        if ((long)s.B * s.Hq < 2L * n_cu) {
+            // too few heads for one block per CU: one wave per 64-slot tile,
+            // then one per head (measured faster there: a head's ring is
+            // spread over many CUs)
+            if (s.reuse) {
+                const dim3 tgrid((s.W + TILE_W - 1) / TILE_W, s.Hq, s.B);
+                if (s.ring_bf16)
+                    hipLaunchKernelGGL(match_tiles_kernel<true>, tgrid, dim3(64), 0, stream, s,
+                                       st, kv, seq_lens, q_pre, hidden);
+                else
+                    hipLaunchKernelGGL(match_tiles_kernel<false>, tgrid, dim3(64), 0, stream, s,
+                                       st, kv, seq_lens, q_pre, hidden);
+            }
+            hipLaunchKernelGGL(match_tiled_kernel, grid, dim3(64), 0, stream, s, st, kv, seq_lens,
+                               q_pre, override_pos, out, hidden);
+            return hipGetLastError();
+        }
+        // sub-tiles of 16 slots, at most MATCH_WAVES waves per head
+        const int sub = 16;
+        const int waves = s.reuse ? min((s.W + sub - 1) / sub, MATCH_WAVES) : 1;
+        if (s.ring_bf16)
+            hipLaunchKernelGGL(match_wide_kernel<true>, grid, dim3(64 * waves), 0, stream, s, st,
+                               kv, seq_lens, q_pre, override_pos, out, hidden);
+        else
+            hipLaunchKernelGGL(match_wide_kernel<false>, grid, dim3(64 * waves), 0, stream, s,
+                               st, kv, seq_lens, q_pre, override_pos, out, hidden);
+        return hipGetLastError();
+    }
+    // the whole ring in registers
+    const int slots = s.W > 32 ? 64 : s.W > 16 ? 32 : 16;
 #define MAC_MATCH(SL, BF)                                                                      \
     hipLaunchKernelGGL((match_kernel<SL, BF>), grid, dim3(64), 0, stream, s, st, kv, seq_lens,  \
                        q_pre, override_pos, out, hidden)

@@ -113,6 +113,34 @@ def test_large_windows(gpu_lib, W, steps):
     assert hits > 0
 
 
+_WIDE_CASES = {
+    # (B, W, steps, ring queries, stale-by-one ring); B x 32 query heads
+    "b16_w200": (16, 200, 60, "fp32", False),
+    "b16_w1000_bf16": (16, 1000, 24, "bf16", False),
+    "b32_w100_wraps": (32, 100, 130, "fp32", False),
+    "b32_w300_bf16_stale": (32, 300, 40, "bf16", True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_WIDE_CASES))
+def test_large_windows_many_heads(gpu_lib, case):
+    """Rings over one 64-slot tile with enough heads to give every CU two
+    blocks (512 and 1024 query heads): one launch per step whose waves (up to
+    8 per head) split each ring into 16-slot sub-tiles and meet in LDS; a
+    ragged last sub-tile (W = 100, 200, 300, 1000), the ring wrapping (W = 100
+    over 130 steps), both ring precisions and the slot the stale-by-one ring
+    hides."""
+    import kv_reuse_amd as mac
+    import oracle
+    B, W, steps, ring, stale = _WIDE_CASES[case]
+    w = scaled(get_config("b16_128k"), B=B, C=300, steps=steps, W=W,
+               rho=("const", 0.985 if stale else 0.96))
+    flags = (mac.MAC_F_RING_BF16 if ring == "bf16" else 0) | (mac.MAC_F_STALE_RING if stale else 0)
+    oflags = (oracle.F_RING_BF16 if ring == "bf16" else 0) | (oracle.F_STALE_RING if stale else 0)
+    hits, _ = _run(w, w.steps, flags=flags, oracle_flags=oflags)
+    assert hits > 0
+
+
 _FUSED_CASES = {
     "cpu4k_fp32": (lambda: scaled(get_config("cpu4k"), steps=120), {}),
     "paged_mixed": (lambda: scaled(get_config("b16_128k"), B=4, C=3000, steps=48), {}),
