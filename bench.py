@@ -465,6 +465,7 @@ def contgen_run(warm, steps, decisions=True):
     amend = torch.cuda.Stream()
     res = {}
     passes = [("mac", 0), ("mac_fused_amend", mac.MAC_F_FUSED_AMEND),
+              ("mac_fused_amend_ring_bf16", mac.MAC_F_FUSED_AMEND | mac.MAC_F_RING_BF16),
               ("full", mac.MAC_F_DISABLE_REUSE)]
     if decisions:
         passes.append(("decisions", mac.MAC_F_RECORD_DEBUG))
@@ -516,10 +517,13 @@ def contgen_run(warm, steps, decisions=True):
             "q_heads": w.Hq, "kv_heads": w.Hkv, "ring": w.W, "band": w.r, "tau": w.tau,
             "rho": list(base.rho), "jump_every": base.jump_every, "warmup": warm,
             "steps": steps, "mac": res["mac"], "mac_fused_amend": res["mac_fused_amend"],
+            "mac_fused_amend_ring_bf16": res["mac_fused_amend_ring_bf16"],
             "full_attention": res["full"],
             "speedup_vs_full": res["mac"]["tokens_per_s"] / res["full"]["tokens_per_s"],
             "speedup_vs_full_fused_amend": (res["mac_fused_amend"]["tokens_per_s"] /
                                             res["full"]["tokens_per_s"]),
+            "speedup_vs_full_fused_amend_ring_bf16": (
+                res["mac_fused_amend_ring_bf16"]["tokens_per_s"] / res["full"]["tokens_per_s"]),
             "setup_s": setup,
             "note": "attention path only (append, match, complete, reduce, amend on a second "
                     "stream shared by the layers); wall clock over the timed steps, no FFN"}

@@ -7,7 +7,7 @@ namespace mac {
 namespace {
 
 // ================================================================== reduce
-// Grid (Hq, B), 1024 threads: one block per (request, query head).  Each
+// Grid (Hq, B), REDUCE_THREADS threads: one block per (request, query head).  Each
 // segment of the head's group has n partial summaries (slots w + segment for
 // the worker range the complete kernel published); n is a few dozen when
 // most groups stream their whole context and reaches the thousands when one
@@ -26,7 +26,7 @@ namespace {
 //                 of this step together with the pre-RoPE query and m;
 //                 O = X (+) band.
 // out receives O's normalised output.
-constexpr int REDUCE_THREADS = 1024;
+constexpr int REDUCE_THREADS = 512;
 constexpr int RCH = D / 4;                       // float4 chunks of a row
 constexpr int RLANES = REDUCE_THREADS / RCH;     // partials combined side by side
 constexpr int RUNROLL = 4;                       // partials per round of loads
@@ -193,9 +193,10 @@ __device__ __forceinline__ void combine_partials(const float *part0, int n0, con
     }
 }
 
-// Five waves per SIMD (at most 102 VGPRs): a CU holds one block and the next
-// one starts while wave 0 of the last finishes its head.
-__global__ __launch_bounds__(REDUCE_THREADS) __attribute__((amdgpu_waves_per_eu(5))) void
+// 512 threads at <= 128 VGPRs: two blocks per CU, so a CU works on two heads
+// at once (1024-thread blocks, one per CU, took two rounds over the CUs for
+// 512 heads and measured ~2 us slower on short steps).
+__global__ __launch_bounds__(REDUCE_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void
 reduce_kernel(Shape s, State st, float *__restrict__ out)
 {
     __shared__ ReduceLds lds;
