@@ -111,7 +111,14 @@ struct RingTile {
                 d = fmaf(t3, t3, d);
                 d = half_sum(d);
             }
-            const int pos = __shfl(pos_l, sl & 63, 64);
+            // the slots' stamps by wave-uniform lane reads (no LDS round trip),
+            // then each lane group takes its own slot's
+            int pos = __builtin_amdgcn_readlane(pos_l, PER * u);
+#pragma unroll
+            for (int g = 1; g < PER; ++g) {
+                const int pg = __builtin_amdgcn_readlane(pos_l, PER * u + g);
+                pos = sub == g ? pg : pos;
+            }
             const bool valid = sl < nslot && pos >= 0 && pos <= m;
             if (valid && nearer(d, pos, base + sl, kd, kp, kj)) {
                 kd = d;
