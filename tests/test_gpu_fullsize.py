@@ -5,10 +5,11 @@
   stale-by-one ring and bf16 ring queries on sampled groups;
 - batch 8 x 122880, 32q/4kv (8 query heads per KV head), per-head rho
   0.5..0.99, paged bf16, sampled groups;
-- batch 16 x 8192, 32q/8kv: every group for 16 steps at a size where the
-  complete kernel's plan weights its shares by dispatch round (the step's
-  pages reach 16 per wave of the persistent grid), asserted through the
-  grid size the library reports.
+- batch 16 x 8192, 32q/8kv, and batch 8 x 16384 with one query head per KV
+  head (the vector worker): every group at a size where the complete
+  kernel's plan weights its shares by dispatch round (the step's pages reach
+  16 per wave of the persistent grid), asserted through the grid size the
+  library reports.
 
 Decisions are checked for every head (the oracle's match is cheap); where a
 sample of whole GQA groups is tracked, each head's state is independent of
@@ -116,4 +117,19 @@ def test_dispatch_round_weighted_plan_every_group(gpu_lib, form):
     weighted = sum(p >= 16 * waves for p in pages)
     print("steps with a round-weighted plan:", weighted, "of", len(pages), flush=True)
     assert weighted == len(pages)
+    assert hits > 0
+
+
+def test_g1_vector_worker_weighted_plan_every_group(gpu_lib):
+    """One query head per KV head (G = 1; bf16 runs the vector worker there):
+    8 x 16384 with 8 heads gives 64 groups of ~1025 pages, over 16 per wave of
+    three dispatch rounds, so every step takes the round-weighted split;
+    every group is output-checked."""
+    import torch
+    w = scaled(get_config("b16_128k"), B=8, Hq=8, Hkv=8, C=16384, steps=12)
+    hits, pages, st = _run(w, w.steps)
+    waves = st["complete_waves"]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert waves >= 3 * 4 * n_cu, "fewer than three dispatch rounds of 4-wave blocks"
+    assert all(p >= 16 * waves for p in pages)
     assert hits > 0
