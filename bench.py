@@ -153,6 +153,34 @@ class Bench:
         self.layer.decode_step(self.view, q, self.out, None, self.stream)
 
 
+def pipelined_us(w, flags, cache, q_dev, k_rows, v_rows, warmup, steps, scrub=None):
+    """Attention phase with the launches queued ahead, as a serving loop
+    issues them: after `warmup` synchronised steps from a fresh ring, `steps`
+    steps are enqueued back to back (the optional scrub read, append, then
+    the decode call between two stream events) and the host synchronises once
+    at the end.  The mean of the event spans is the decode call's device time
+    without the host's launch latency; it includes any wait for the previous
+    step's amend."""
+    import torch
+    bn = Bench(w, flags, *cache)
+    for t in range(warmup):
+        bn.step(t, q_dev[t], k_rows[t], v_rows[t], scrub)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i, t in enumerate(range(warmup, warmup + steps)):
+        if scrub is not None:
+            scrub[1].copy_(scrub[0].sum())
+        bn.pos.fill_(w.C + t)
+        bn.seq.fill_(w.C + t + 1)
+        bn.layer.append_kv(bn.view, k_rows[t], v_rows[t], bn.pos, bn.stream)
+        ev[i][0].record(bn.stream)
+        bn.layer.decode_step(bn.view, q_dev[t], bn.out, None, bn.stream)
+        ev[i][1].record(bn.stream)
+    bn.layer.stats()                        # synchronises every stream of the handle
+    bn.layer.close()
+    return float(np.mean([a.elapsed_time(b) * 1e3 for a, b in ev]))
+
+
 def loop_us(w, flags, cache, q_dev, k_rows, v_rows, warmup, steps, hit_rate=None):
     """Microseconds per step of a decode loop run back to back (append and
     decode enqueued with no host synchronisation, as a serving loop runs):
@@ -235,6 +263,10 @@ def speedup_point(name, steps=24, warmup=40):
         kv = toks * 2 * w.d * w.kv_elem_bytes / steps
         kernels[label] = kernel_rates(w, {k: float(np.mean(v)) for k, v in kern.items()}, kv)
         kernels[label]["kv_bytes_per_step"] = kv
+    cache = (kc, vc, paged, table)
+    piped = {label: pipelined_us(w, flags, cache, q_dev, k_rows, v_rows, warmup, steps, scrub)
+             for label, flags in (("mac", 0), ("mac_fused_amend", mac.MAC_F_FUSED_AMEND),
+                                  ("full", mac.MAC_F_DISABLE_REUSE))}
     graph = fused_graph_loops(w, kc, vc, paged, table, k_rows, v_rows, q_dev, warmup)
     return {"workload": name, "context": w.C, "batch": w.B,
             "mac_attention_us": res["mac"][0], "full_attention_us": res["full"][0],
@@ -245,7 +277,9 @@ def speedup_point(name, steps=24, warmup=40):
             "mac_fused_amend_attention_us": res["mac_fused_amend"][0],
             "mac_sync_amend_attention_us": res["mac_sync_amend"][0],
             "speedup_fused_amend": res["full"][0] / res["mac_fused_amend"][0],
-            "kernels": kernels, "steps": steps, "warmup": warmup}
+            "kernels": kernels, "attention_us_pipelined": piped,
+            "speedup_pipelined": piped["full"] / piped["mac"],
+            "steps": steps, "warmup": warmup}
 
 
 def fused_graph_loops(w, kc, vc, paged, table, k_rows, v_rows, q_dev, start, steps=16):
@@ -1056,7 +1090,7 @@ def main():
 
     # the reuse path's own speedup at this context: the same cache, queries
     # with rho = 0.97 (nearly every head hits its previous step)
-    allhit = loops = None
+    allhit = loops = piped = None
     if (not args.no_baseline_kernel and args.config == "b16_128k" and not args.set and not args.r
             and not args.band_per_head):
         cache = (kc, vc, paged, table)
@@ -1067,6 +1101,10 @@ def main():
             qa = torch.as_tensor(queries(wa, steps=total), device="cuda")
             m = measure(wa, mac_flags, cache, k_rows, v_rows, qa, 4, 16)
             kv = m.pop("kv_tokens") * row_bytes_ / 16
+            m["attention_us_pipelined"] = {
+                "mac": pipelined_us(wa, mac_flags, cache, qa, k_rows, v_rows, 4, 16),
+                "mac_fused_amend": pipelined_us(wa, mac_flags | mac.MAC_F_FUSED_AMEND, cache, qa,
+                                                k_rows, v_rows, 4, 16)}
             m.update({"rho": rho, "kv_bytes_per_step": kv,
                       "speedup_vs_full": (base["attention_us"] / m["attention_us"]) if base
                       else None,
@@ -1081,6 +1119,9 @@ def main():
             "mac_sync_amend": loop_us(wa, mac.MAC_F_SYNC_AMEND, cache, qa, k_rows, v_rows, 4, 16)}
         # the mixed workload's decode loop, amend included, for every amend form
         lh = {}
+        piped = {"mac": pipelined_us(w, mac_flags, cache, q_dev, k_rows, v_rows, 4, 16),
+                 "full": pipelined_us(w, mac.MAC_F_DISABLE_REUSE, cache, q_dev, k_rows, v_rows,
+                                      4, 16)}
         loops = {"mac": loop_us(w, 0, cache, q_dev, k_rows, v_rows, 4, 16, lh),
                  "mac_fused_amend": loop_us(w, mac.MAC_F_FUSED_AMEND, cache, q_dev, k_rows,
                                             v_rows, 4, 16, lh),
@@ -1190,6 +1231,7 @@ def main():
         "attention_phase_bytes_per_step": att_bytes,
         "full_attention_kernel": base,
         "loop_us_per_step": loops,
+        "attention_us_pipelined": piped,
         "allhit_128k": allhit,
         "speedup_32k": point_32k,
         "cpu_baseline": cpu,
@@ -1197,8 +1239,10 @@ def main():
         "setup_s": t_setup,
         "timing_note": ("value: mean over the timed steps of the decode call's span on the "
                         "decode stream, each step launched onto an idle GPU (launch latency "
-                        "included); warm-up steps as given by --warmup (the AR(1) queries' "
-                        "nearest ring entry is the newest, so a few steps fill what matches)"),
+                        "included); attention_us_pipelined: the same span with the launches "
+                        "queued ahead (one synchronisation after 16 steps); warm-up steps as "
+                        "given by --warmup (the AR(1) queries' nearest ring entry is the "
+                        "newest, so a few steps fill what matches)"),
         "bad_input": int(st1["bad_input"]),
     }
     print(json.dumps(line), flush=True)
