@@ -9,7 +9,9 @@ namespace mac {
 namespace {
 
 // ================================================================== amend
-// fp32 caches (bf16 ones take amend_mfma_kernel below).
+// fp32 caches, and bf16 ones at G = 1 (one query row is no matrix tile; the
+// vector worker measured as fast there); bf16 at G >= 2 takes
+// amend_mfma_kernel below.
 // Grid (Hkv, B), 8 waves (4 for 8 query heads per KV head, whose VALU worker
 // needs more than the 256 VGPRs two waves per SIMD allow): the waves share the
 // band [m-r+1, m] page by page (two to five pages each at r = 256), combine in
@@ -153,9 +155,9 @@ __global__ __launch_bounds__(64 * amend_waves<G>()) void amend_kernel(Shape s, S
     amend_finish<G, AMEND_WAVES>(s, st, red, in, b, kvh, m, lo, has_prefix, *st.step_slot);
 }
 
-// bf16 caches: the band's pages go through the MFMA page path of complete
-// (mfma_page.h), 8 waves per group for every G (G = 8 fits two waves per SIMD
-// there).  The waves share one copy of the group's A operands in LDS; wave w
+// bf16 caches, G >= 2: the band's pages go through the MFMA page path of
+// complete (mfma_page.h), 8 waves per group for every G (G = 8 fits two waves
+// per SIMD there).  The waves share one copy of the group's A operands in LDS; wave w
 // takes pages lo/16 + w, + 8, ..., the next page's loads in flight while one
 // is computed; the epilogue is amend_finish.
 constexpr int AMEND_MFMA_WAVES = 8;
@@ -309,7 +311,7 @@ hipError_t launch_amend_t(const Shape &s, const State &st, const KvView &kv, hip
     switch (s.G) {
 #define MAC_CASE(GG)                                                                          \
     case GG:                                                                                  \
-        if constexpr (sizeof(T) == 2)                                                         \
+        if constexpr (sizeof(T) == 2 && GG > 1)                                               \
             hipLaunchKernelGGL(amend_mfma_kernel<GG>, grid, dim3(64 * AMEND_MFMA_WAVES), 0,    \
                                stream, s, st, kv);                                            \
         else                                                                                  \
