@@ -531,10 +531,13 @@ __device__ __forceinline__ int page_owner(long x, int nW, int P)
 // waves and sets the end of the launch (wave ends at 128K x 16 per round,
 // median / max: 967 / 1004, 998 / 1025, 1025 / 1054 us), so with many pages
 // per wave the balanced plan gives round k the weight
-// 1000 + SLOT_TILT * (slots - 1 - 2k) per mille (complete 1081 -> 1070 us).
+// 1000 + SLOT_TILT * (slots - 1 - 2k) per mille: 1120 / 1000 / 880 at three
+// rounds.  Complete at 128K x 16 (mean of 3-4 runs per setting, two boxes):
+// +-6 % 1081-1088 us, +-9 % 1079, +-12 % 1071-1072, +-16 % 1070; full
+// attention 1322-1328 us at +-6 %, 1318-1323 at +-12 %.
 // At two rounds (G = 8) the rounds' slowest waves end together (310 / 312 us
 // of 8 x 122880) and the weights only lengthened the first round (+2.8 %).
-constexpr int SLOT_TILT = 30;
+constexpr int SLOT_TILT = 60;
 
 __device__ __forceinline__ bool tilted_plan(const State &st, int nW, int P)
 {
