@@ -149,12 +149,11 @@ struct RingTile {
 };
 
 // ================================================================== match
-// One (request, query head) per block.  The head's decision is taken by one
-// wave once the nearest valid ring entry is known; the kernels differ in how
-// they find it.  The match step is latency-bound, so every load that does not
-// depend on the query position (query, angles, stamps, override, the head's
-// counters) is issued before any of them is waited on.  The head then takes
-// its decision (hit iff the relative L2 distance of the nearest valid entry is
+// The head's decision is taken by one wave once the nearest valid ring entry
+// is known; the kernels below differ in how they find it.  The match step is
+// latency-bound, so the one-wave kernel issues every load that does not depend
+// on the query position (query, angles, ring, stamps, override, the head's
+// counters) before it waits on any of them.  The head then takes its decision (hit iff the relative L2 distance of the nearest valid entry is
 // within tau, compared squared), applies an override, rotates its query
 // (rotate-half RoPE, angle in fp64) and records its key span:
 // [max(p - r + 1, 0), m] on a hit, [0, m] on a miss.
