@@ -415,7 +415,8 @@ def workload_record(name, warm, steps, bands=(None,), loop=True):
     band (full attention does not depend on it).  Per record: attention-phase
     µs/step (synchronised step), tokens/s, KV bytes per step, the complete
     kernel's achieved GB/s and fraction of 8 TB/s, head-hit and all-hit-group
-    shares, the back-to-back loop µs/step (amend included) and MAC vs full."""
+    shares, the back-to-back loop µs/step (amend included) and MAC vs full;
+    and the same MAC step with fused amend (no second stream)."""
     import torch
     import kv_reuse_amd as mac
     from workloads import get_config, scaled
@@ -446,6 +447,15 @@ def workload_record(name, warm, steps, bands=(None,), loop=True):
         m["speedup_vs_full"] = full["attention_us"] / m["attention_us"]
         if loop:
             m["loop_speedup_vs_full"] = full["loop_us_per_step"] / m["loop_us_per_step"]
+        # the fused amend form (no second stream): attention phase and loop only
+        f = measure(w, mac.MAC_F_FUSED_AMEND, cache, k_rows, v_rows, q_dev, warm, steps)
+        m["fused_amend"] = {"attention_us": f["attention_us"],
+                            "speedup_vs_full": full["attention_us"] / f["attention_us"]}
+        if loop:
+            fl = loop_us(w, mac.MAC_F_FUSED_AMEND, cache, q_dev, k_rows, v_rows, min(warm, 8),
+                         min(steps, 16))
+            m["fused_amend"].update({"loop_us_per_step": fl,
+                                     "loop_speedup_vs_full": full["loop_us_per_step"] / fl})
         recs.append(m)
     del cache, k_rows, v_rows, q_dev
     torch.cuda.empty_cache()
