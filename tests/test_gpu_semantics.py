@@ -9,7 +9,9 @@
 - mac_reset empties the rings; idle requests produce zeros and store nothing;
 - sequence lengths and page ids out of range are caught on the device;
 - the counters agree with the oracle's decisions and key counts;
-- misaligned device pointers are refused on the host.
+- misaligned device pointers are refused on the host;
+- overrides of every kind through both long-ring match forms;
+- calls moving between two streams with no host synchronisation.
 """
 import numpy as np
 import pytest
@@ -329,3 +331,31 @@ def test_alternating_streams_match_oracle(form):
         ls.close()
     print("  hits", hits, ls.forced_summary(), flush=True)
     assert hits > 0
+
+
+@pytest.mark.parametrize("B", [2, 16])
+def test_overrides_with_long_rings_match_oracle(B):
+    """Overrides (forced reuse of a named position, a forced miss, a position
+    not in the ring) with a 200-entry ring, through both long-ring match forms:
+    the tile kernel (2 x 32 heads) and the one-launch kernel (16 x 32 heads).
+    Every decision and output against the oracle given the same overrides."""
+    from gpu_harness import Lockstep
+    w = _case(B=B, C=400, steps=36, W=200)
+    rng = np.random.default_rng(11 + B)
+    ls = Lockstep(w)
+    try:
+        for t in range(w.steps):
+            ov = None
+            if t >= 12:
+                m = w.C + t
+                ov = np.full((w.B, w.Hq), -2, np.int32)
+                kind = rng.integers(0, 4, size=(w.B, w.Hq))
+                back = rng.integers(1, t + 1, size=(w.B, w.Hq))   # steps 0 .. t-1 are stored
+                ov[kind == 1] = (m - back)[kind == 1]
+                ov[kind == 2] = -1
+                ov[kind == 3] = m + 3                              # never stored
+            info = ls.step(t, override=ov)
+            if ov is not None:
+                assert info["res"]["override_invalid"] == int((ov == w.C + t + 3).sum())
+    finally:
+        ls.close()
