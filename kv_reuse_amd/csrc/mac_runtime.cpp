@@ -43,6 +43,7 @@ struct mac_ctx {
     // done_valid is false and the caller orders the streams).
     hipStream_t last_stream = nullptr;
     hipEvent_t ev_done = nullptr;
+    hipEvent_t done_ev = nullptr;   // ev_done, or an event the call already recorded at its end
     bool done_valid = false;
     // A HIP call failed part-way through a decode or prefill call: device and
     // host state may disagree (the ring slot counter), so such calls return
@@ -265,12 +266,14 @@ hipError_t wait_amend(mac_ctx *h, int i, hipStream_t st)
 hipError_t follow(mac_ctx *h, hipStream_t st)
 {
     if (h->last_stream && h->last_stream != st && h->done_valid)
-        return hipStreamWaitEvent(st, h->ev_done, 0);
+        return hipStreamWaitEvent(st, h->done_ev, 0);
     return hipSuccess;
 }
 
 // Mark the end of a call's work on st (skipped while st is being captured).
-hipError_t mark_done(mac_ctx *h, hipStream_t st)
+// `recorded`: an event the call has just recorded on st after its last work
+// (the hand-off to the amend stream), which then serves as the end mark.
+hipError_t mark_done(mac_ctx *h, hipStream_t st, hipEvent_t recorded = nullptr)
 {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     hipError_t e = hipStreamIsCapturing(st, &cs);
@@ -278,7 +281,14 @@ hipError_t mark_done(mac_ctx *h, hipStream_t st)
         return e;
     h->last_stream = st;
     h->done_valid = cs == hipStreamCaptureStatusNone;
-    return h->done_valid ? hipEventRecord(h->ev_done, st) : hipSuccess;
+    if (!h->done_valid)
+        return hipSuccess;
+    if (recorded) {
+        h->done_ev = recorded;
+        return hipSuccess;
+    }
+    h->done_ev = h->ev_done;
+    return hipEventRecord(h->ev_done, st);
 }
 
 mac::KvView to_view(const mac_ctx *h, const mac_kv_view *kv)
@@ -605,11 +615,13 @@ hipError_t decode_enqueue(mac_ctx *h, const mac_kv_view *kv, const float *q_pre_
     if (timing)
         MAC_TRY(hipEventRecord(h->tm[3], st));
 
+    hipEvent_t end_mark = nullptr;   // an event recorded on st after this call's last work
     if (h->shape.reuse && !fused) {
         hipStream_t as = (h->cfg.flags & MAC_F_SYNC_AMEND) ? st : h->amend_stream;
         if (as != st) {
             MAC_TRY(hipEventRecord(h->ev_attn, st));
             MAC_TRY(hipStreamWaitEvent(as, h->ev_attn, 0));
+            end_mark = h->ev_attn;
         }
         if (timing)
             MAC_TRY(hipEventRecord(h->tm[4], as));
@@ -624,7 +636,7 @@ hipError_t decode_enqueue(mac_ctx *h, const mac_kv_view *kv, const float *q_pre_
         }
         h->amend_pending[cur] = true;
     }
-    MAC_TRY(mark_done(h, st));
+    MAC_TRY(mark_done(h, st, end_mark));
     h->timed_step = timing;
     h->calls += 1;
     return hipSuccess;
