@@ -7,17 +7,20 @@ namespace mac {
 namespace {
 
 // ================================================================== reduce
-// Grid (Hq, B), REDUCE_THREADS threads: one block per (request, query head).  Each
-// segment of the head's group has n partial summaries (slots w + segment for
-// the worker range the complete kernel published); n is a few dozen when
-// most groups stream their whole context and reaches the thousands when one
-// long span shares the workers with short ones.  The block is laid out as
-// RLANES partials x RCH float4 column chunks: thread (k, c) folds chunk c of
-// partials k, k + RLANES, ... into an online-softmax state (running max,
-// rescaled sums), RUNROLL partials per round with all their loads in flight
-// (RLONG per round while a whole such round is left: a list of thousands
-// takes a handful of round trips, not dozens);
-// the RLANES states are then combined in LDS.
+// Grid (Hq, B, slices), REDUCE_THREADS threads: each (request, query head) is
+// combined by `slices` blocks, block z taking the row's float4 column chunks
+// [z CH, (z + 1) CH) of every partial (CH = 32 / slices) together with the
+// partials' (M, l), which every slice reads, so all slices agree on the
+// scales.  Each segment of the head's group has n partial summaries (slots
+// w + segment for the worker range the complete kernel published); n is a
+// few dozen when most groups stream their whole context and reaches the
+// thousands when one long span shares the workers with short ones.  A block
+// is laid out as 512 / CH partial lanes x CH chunks: thread (k, c) folds
+// chunk c of partials k, k + lanes, ... into an online-softmax state (running
+// max, rescaled sums), RUNROLL partials per round with all their loads in
+// flight (RLONG per round while a whole such round is left), and the lanes'
+// states are then combined in LDS.  Narrower slices give a long list more
+// lanes, so fewer dependent rounds of loads.
 //
 // Then, per head, with the matched entry's stored prefix S = AS_{1:p-r}
 // (EMPTY on a miss) and (+) the log-domain merge:
@@ -28,11 +31,10 @@ namespace {
 // out receives O's normalised output.
 constexpr int REDUCE_THREADS = 512;
 constexpr int RCH = D / 4;                       // float4 chunks of a row
-constexpr int RLANES = REDUCE_THREADS / RCH;     // partials combined side by side
 constexpr int RUNROLL = 4;                       // partials per round of loads
 constexpr int RLONG = 8;                         // the same, for long lists
 
-// A summary as threads 0..RCH-1 hold it: normalised output chunk c (o), the
+// A summary as threads 0..CH-1 hold it: normalised output chunk c (o), the
 // reference max M (log2 units) and the normaliser L; EMPTY is (0, -inf, 0).
 struct Sum4 {
     float4 o;
@@ -90,23 +92,27 @@ __device__ __forceinline__ void fold(float4 &a, float &L, float &M, const float4
     }
 }
 
+template <int CH>
 struct ReduceLds {
-    float4 o[RLANES][RCH];
-    float l[RLANES], m[RLANES];
+    static constexpr int LANES = REDUCE_THREADS / CH;   // partials combined side by side
+    float4 o[LANES][CH];
+    float l[LANES], m[LANES];
 };
 
 // Combine NSETS (1 or 2) sets of partials -- set j: n_j rows at part_j,
-// part_j + pstride, ... (this head's rows) -- into normalised summaries r0,
-// r1, valid in threads 0..RCH-1 (EMPTY for a set with no rows).  The block's
-// RLANES partial lanes are split evenly between the sets, so both are read in
-// the same rounds.  Every thread of the block calls it (one barrier).
-template <int NSETS>
+// part_j + pstride, ... (this head's rows) -- over the CH chunks starting at
+// float `col0` into normalised summaries r0, r1, valid in threads 0..CH-1
+// (EMPTY for a set with no rows).  The block's partial lanes are split evenly
+// between the sets, so both are read in the same rounds.  Every thread of the
+// block calls it (one barrier).
+template <int NSETS, int CH>
 __device__ __forceinline__ void combine_partials(const float *part0, int n0, const float *part1,
-                                                 int n1, long pstride, ReduceLds &lds, Sum4 &r0,
-                                                 Sum4 &r1)
+                                                 int n1, long pstride, int col0,
+                                                 ReduceLds<CH> &lds, Sum4 &r0, Sum4 &r1)
 {
-    constexpr int PER = RLANES / NSETS;   // partial lanes per set
-    const int t = threadIdx.x, c = t % RCH, k = t / RCH;
+    constexpr int LANES = ReduceLds<CH>::LANES;
+    constexpr int PER = LANES / NSETS;   // partial lanes per set
+    const int t = threadIdx.x, c = t % CH, k = t / CH;
     const int set = k / PER, kk = k % PER;
     const float *part = set == 0 ? part0 : part1;
     const int n = set == 0 ? n0 : n1;
@@ -119,7 +125,7 @@ __device__ __forceinline__ void combine_partials(const float *part0, int n0, con
 #pragma unroll
         for (int u = 0; u < RLONG; ++u) {
             const float *pi = part + (long)(i + u * PER) * pstride;
-            ov[u] = *reinterpret_cast<const float4 *>(pi + 4 * c);
+            ov[u] = *reinterpret_cast<const float4 *>(pi + col0 + 4 * c);
             const float2 ml = *reinterpret_cast<const float2 *>(pi + D);
             mv[u] = ml.x;
             lv[u] = ml.y;
@@ -134,7 +140,7 @@ __device__ __forceinline__ void combine_partials(const float *part0, int n0, con
         for (int u = 0; u < RUNROLL; ++u) {
             if (u < cnt) {
                 const float *pi = part + (long)(i + u * PER) * pstride;
-                ov[u] = *reinterpret_cast<const float4 *>(pi + 4 * c);
+                ov[u] = *reinterpret_cast<const float4 *>(pi + col0 + 4 * c);
                 mv[u] = pi[D];
                 lv[u] = pi[D + 1];
             }
@@ -149,36 +155,49 @@ __device__ __forceinline__ void combine_partials(const float *part0, int n0, con
     __syncthreads();
     if (t >= 64)
         return;
-    // wave 0: lanes 32j .. 32j+31 finish set j (set 0 only when NSETS == 1)
+    // wave 0: lanes [j TPS, (j + 1) TPS) finish set j; lane jj CH + c of a
+    // set folds chunk c of lanes jj, jj + J, ..., then the J folds of a chunk
+    // meet by lane exchanges (lanes CH, 2 CH, ... apart, inside the set)
+    constexpr int TPS = 64 / NSETS;
+    constexpr int J = TPS / CH;
+    static_assert(J >= 1 && J * CH == TPS, "chunk count must divide the set's lanes");
+    const int q0 = (t / TPS) * PER, jj = (t % TPS) / CH;
+    float Mx = NEG_INF;
+#pragma unroll
+    for (int q = jj; q < PER; q += J)
+        Mx = fmaxf(Mx, lds.m[q0 + q]);
+#pragma unroll
+    for (int off = CH; off < TPS; off <<= 1)
+        Mx = fmaxf(Mx, __shfl_xor(Mx, off, 64));
+    const float base = Mx == NEG_INF ? 0.f : Mx;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float Lt = 0.f;
+#pragma unroll
+    for (int q = jj; q < PER; q += J) {
+        const float sc = exp2f(lds.m[q0 + q] - base);   // 0 for a lane that saw no partial
+        const float4 x = lds.o[q0 + q][c];
+        o.x = fmaf(x.x, sc, o.x);
+        o.y = fmaf(x.y, sc, o.y);
+        o.z = fmaf(x.z, sc, o.z);
+        o.w = fmaf(x.w, sc, o.w);
+        Lt = fmaf(lds.l[q0 + q], sc, Lt);
+    }
+#pragma unroll
+    for (int off = CH; off < TPS; off <<= 1) {
+        o.x += __shfl_xor(o.x, off, 64);
+        o.y += __shfl_xor(o.y, off, 64);
+        o.z += __shfl_xor(o.z, off, 64);
+        o.w += __shfl_xor(o.w, off, 64);
+        Lt += __shfl_xor(Lt, off, 64);
+    }
     Sum4 r;
     r.o = make_float4(0.f, 0.f, 0.f, 0.f);
     r.M = NEG_INF;
     r.L = 0.f;
-    const int mine = t / RCH;
-    if (mine < NSETS) {
-        const int q0 = mine * PER;
-        float Mx = lds.m[q0];
-#pragma unroll
-        for (int q = 1; q < PER; ++q)
-            Mx = fmaxf(Mx, lds.m[q0 + q]);
-        const float base = Mx == NEG_INF ? 0.f : Mx;
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        float Lt = 0.f;
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            const float sc = exp2f(lds.m[q0 + q] - base);   // 0 for a lane that saw no partial
-            const float4 x = lds.o[q0 + q][c];
-            o.x = fmaf(x.x, sc, o.x);
-            o.y = fmaf(x.y, sc, o.y);
-            o.z = fmaf(x.z, sc, o.z);
-            o.w = fmaf(x.w, sc, o.w);
-            Lt = fmaf(lds.l[q0 + q], sc, Lt);
-        }
-        if (Lt > 0.f) {
-            r.o = make_float4(o.x / Lt, o.y / Lt, o.z / Lt, o.w / Lt);
-            r.M = Mx;
-            r.L = Lt;
-        }
+    if (Lt > 0.f) {
+        r.o = make_float4(o.x / Lt, o.y / Lt, o.z / Lt, o.w / Lt);
+        r.M = Mx;
+        r.L = Lt;
     }
     r0 = r;
     if constexpr (NSETS == 2) {
@@ -196,24 +215,26 @@ __device__ __forceinline__ void combine_partials(const float *part0, int n0, con
 // 512 threads at <= 128 VGPRs: two blocks per CU, so a CU works on two heads
 // at once (1024-thread blocks, one per CU, took two rounds over the CUs for
 // 512 heads and measured ~2 us slower on short steps).
+template <int CH>
 __global__ __launch_bounds__(REDUCE_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void
 reduce_kernel(Shape s, State st, float *__restrict__ out)
 {
-    __shared__ ReduceLds lds;
+    __shared__ ReduceLds<CH> lds;
     const int b = blockIdx.y, h = blockIdx.x, kvh = h / s.G, hh = h % s.G;
     const int g = b * s.Hkv + kvh;
-    const int t = threadIdx.x, c = t % RCH;
+    const int t = threadIdx.x;
+    const int chunk = (int)blockIdx.z * CH + t % CH;   // this thread's float4 column chunk
     const long idx = (long)b * s.Hq + h;
-    // the stored summary to merge with (threads 0..RCH-1)
+    // the stored summary to merge with (threads 0..CH-1)
     Sum4 S;
     S.o = make_float4(0.f, 0.f, 0.f, 0.f);
     S.M = NEG_INF;
     S.L = 0.f;
-    if (t < RCH) {
+    if (t < CH) {
         const int slot = st.dec_slot[idx];
         if (slot >= 0) {
             const float *rs = st.ring_s + (idx * s.W + slot) * SUMM;
-            S.o = *reinterpret_cast<const float4 *>(rs + 4 * c);
+            S.o = *reinterpret_cast<const float4 *>(rs + 4 * chunk);
             S.M = rs[D];
             S.L = rs[D + 1];
         }
@@ -228,21 +249,24 @@ reduce_kernel(Shape s, State st, float *__restrict__ out)
         return;   // idle request: match wrote its zero output, nothing is stored
     const long pstride = (long)s.G * SUMM;   // one slot
     const float *p0 = st.partials + ((long)rg0.x + seg0) * pstride + hh * SUMM;
+    const int col0 = 4 * CH * (int)blockIdx.z;
     Sum4 part0, part1;
     if (s.nseg == 2)
-        combine_partials<2>(p0, rg0.y - rg0.x + 1,
-                            st.partials + ((long)rg1.x + seg0 + 1) * pstride + hh * SUMM,
-                            rg1.y - rg1.x + 1, pstride, lds, part0, part1);
+        combine_partials<2, CH>(p0, rg0.y - rg0.x + 1,
+                                st.partials + ((long)rg1.x + seg0 + 1) * pstride + hh * SUMM,
+                                rg1.y - rg1.x + 1, pstride, col0, lds, part0, part1);
     else
-        combine_partials<1>(p0, rg0.y - rg0.x + 1, nullptr, 0, pstride, lds, part0, part1);
-    if (t >= RCH)
+        combine_partials<1, CH>(p0, rg0.y - rg0.x + 1, nullptr, 0, pstride, col0, lds, part0,
+                                part1);
+    if (t >= CH)
         return;
+    const bool lead = blockIdx.z == 0 && t == 0;   // writes the scalars
     Sum4 O;
     if (s.nseg == 1) {
         O = merge(S, part0);
         float *asf = st.as_full + idx * SUMM;
-        *reinterpret_cast<float4 *>(asf + 4 * c) = O.o;
-        if (t == 0) {
+        *reinterpret_cast<float4 *>(asf + 4 * chunk) = O.o;
+        if (lead) {
             asf[D] = O.M;
             asf[D + 1] = O.L;
         }
@@ -251,23 +275,23 @@ reduce_kernel(Shape s, State st, float *__restrict__ out)
         O = merge(X, part1);
         const int slot_new = *st.step_slot;   // this call's ring slot (match)
         float *dst = st.ring_s + (idx * s.W + slot_new) * SUMM;
-        *reinterpret_cast<float4 *>(dst + 4 * c) = X.o;
-        const float4 qv = *reinterpret_cast<const float4 *>(st.q_copy + idx * D + 4 * c);
+        *reinterpret_cast<float4 *>(dst + 4 * chunk) = X.o;
+        const float4 qv = *reinterpret_cast<const float4 *>(st.q_copy + idx * D + 4 * chunk);
         const long row = (idx * s.W + slot_new) * D;
         if (s.ring_bf16)
-            reinterpret_cast<uint2 *>(static_cast<uint16_t *>(st.ring_q) + row)[c] =
+            reinterpret_cast<uint2 *>(static_cast<uint16_t *>(st.ring_q) + row)[chunk] =
                 make_uint2(bf16_rne_bits(qv.x) | bf16_rne_bits(qv.y) << 16,
                            bf16_rne_bits(qv.z) | bf16_rne_bits(qv.w) << 16);
         else
-            reinterpret_cast<float4 *>(static_cast<float *>(st.ring_q) + row)[c] = qv;
-        if (t == 0) {
+            reinterpret_cast<float4 *>(static_cast<float *>(st.ring_q) + row)[chunk] = qv;
+        if (lead) {
             dst[D] = X.M;
             dst[D + 1] = X.L;
             if (h == 0)
                 st.ring_pos[(long)b * s.W + slot_new] = m;
         }
     }
-    *reinterpret_cast<float4 *>(out + idx * D + 4 * c) = O.o;
+    *reinterpret_cast<float4 *>(out + idx * D + 4 * chunk) = O.o;
 }
 
 }  // namespace
@@ -276,8 +300,21 @@ hipError_t launch_reduce(const Shape &s, const State &st, float *out, hipStream_
 {
     if (!supported_group(s.G) || s.nseg < 1 || s.nseg > 2)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(reduce_kernel, dim3(s.Hq, s.B), dim3(REDUCE_THREADS), 0, stream, s, st,
-                       out);
+    // column slices per head while the blocks stay within one per CU: at
+    // 32 heads, four slices took the reduce from 10.1-11.6 to 8.7-9.3 us
+    // (32K x 1); at 512 heads (128K x 16) two and four slices cost 2.5 and
+    // 7 us (same box, HIP events)
+    const long heads = (long)s.B * s.Hq;
+    const long n_cu = st.n_workers / (st.slots * WAVES);
+    const int slices = 4 * heads <= n_cu ? 4 : 2 * heads <= n_cu ? 2 : 1;
+    switch (slices) {
+    case 4: hipLaunchKernelGGL(reduce_kernel<RCH / 4>, dim3(s.Hq, s.B, 4), dim3(REDUCE_THREADS), 0,
+                               stream, s, st, out); break;
+    case 2: hipLaunchKernelGGL(reduce_kernel<RCH / 2>, dim3(s.Hq, s.B, 2), dim3(REDUCE_THREADS), 0,
+                               stream, s, st, out); break;
+    default: hipLaunchKernelGGL(reduce_kernel<RCH>, dim3(s.Hq, s.B, 1), dim3(REDUCE_THREADS), 0,
+                                stream, s, st, out); break;
+    }
     return hipGetLastError();
 }
 
