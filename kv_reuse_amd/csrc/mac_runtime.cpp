@@ -500,11 +500,18 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
             return bail(MAC_EHIP, std::string("hipStreamCreate: ") + hipGetErrorString(e));
         h->own_amend = true;
     }
-    if (hipEventCreateWithFlags(&h->ev_attn, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_amend[0], hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_amend[1], hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_drain, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_done, hipEventDisableTiming) != hipSuccess)
+    // These events only order streams of this device, and the host only asks
+    // whether one has completed; HIP documents that an event without the
+    // system-scope fence (a cache write-back and invalidate when it is
+    // reached) leaves device memory possibly invisible to the host and to
+    // other devices only.  Measured: 1.5 to 3 us less per call on short
+    // steps, the same on long ones.
+    constexpr unsigned ORDER_EVENT = hipEventDisableTiming | hipEventDisableSystemFence;
+    if (hipEventCreateWithFlags(&h->ev_attn, ORDER_EVENT) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_amend[0], ORDER_EVENT) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_amend[1], ORDER_EVENT) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_drain, ORDER_EVENT) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_done, ORDER_EVENT) != hipSuccess)
         return bail(MAC_EHIP, "hipEventCreate failed");
     for (auto &ev : h->tm)
         if (hipEventCreate(&ev) != hipSuccess)
