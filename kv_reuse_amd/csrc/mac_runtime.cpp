@@ -513,8 +513,10 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
         hipEventCreateWithFlags(&h->ev_drain, ORDER_EVENT) != hipSuccess ||
         hipEventCreateWithFlags(&h->ev_done, ORDER_EVENT) != hipSuccess)
         return bail(MAC_EHIP, "hipEventCreate failed");
+    // the timing events (MAC_F_TIMING) skip the fence too: a write-back at
+    // each would land inside the kernel times they bracket
     for (auto &ev : h->tm)
-        if (hipEventCreate(&ev) != hipSuccess)
+        if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess)
             return bail(MAC_EHIP, "hipEventCreate failed");
 
     e = mac::launch_reset(h->shape, h->st, h->main_stream);
