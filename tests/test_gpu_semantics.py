@@ -82,6 +82,37 @@ def test_async_amend_bit_identical_to_sync(stale):
     assert ha == s.layer.stats()["hits"] and ha > 0
 
 
+@pytest.mark.parametrize("stale", [False, True])
+def test_async_amend_bit_identical_to_sync_no_host_waits(stale):
+    """The same with every step enqueued back to back: inputs staged on the
+    device beforehand, each output copied on the device, one synchronisation
+    at the end.  The second stream's amend and the next call's match then
+    overlap whatever the host does, so the hand-offs between the streams
+    alone keep the ring entries whole."""
+    w = _case(steps=96, W=8, r=64)
+    base = mac.MAC_F_STALE_RING if stale else 0
+    forms = [Plain(w, paged=True, flags=base)]
+    forms.append(Plain(w, paged=True, flags=base | mac.MAC_F_SYNC_AMEND, K=forms[0].K,
+                       V=forms[0].V))
+    q_dev = torch.as_tensor(queries(w), device="cuda")
+    seq_dev = torch.as_tensor(np.stack([np.full(w.B, w.C + t + 1, np.int32)
+                                        for t in range(w.steps)]), device="cuda")
+    outs = []
+    for f in forms:
+        torch.cuda.synchronize()
+        got = []
+        for t in range(w.steps):
+            f.seq.copy_(seq_dev[t])
+            f.layer.decode_step(f.view, q_dev[t], f.out)
+            got.append(f.out.clone())
+        outs.append(torch.stack(got))
+    torch.cuda.synchronize()
+    for t in range(w.steps):
+        assert torch.equal(outs[0][t], outs[1][t]), t
+    ha = forms[0].layer.stats()["hits"]
+    assert ha == forms[1].layer.stats()["hits"] and ha > 0
+
+
 def test_paged_bit_identical_to_contiguous():
     w = _case(steps=24)
     pg = Plain(w, paged=True)
