@@ -77,8 +77,9 @@ enum {
      * itself: no band re-read, no log-domain removal, no amend stream work.
      * Same results up to rounding.  Where a step is short (a small batch) it
      * is the fast form: the default hands each call's amend to the second
-     * stream through a cross-queue event, which costs tens of microseconds of
-     * host time per call on this runtime. */
+     * stream through a cross-queue event wait, which costs 11-16 us of host
+     * time per call on this runtime (spent by the handle's own thread when it
+     * created the amend stream) and runs amend after the reduce. */
     MAC_F_FUSED_AMEND = 16u,
     /* Keep the ring's pre-RoPE queries as bfloat16 (rounded to nearest, ties
      * to even) and match against those: half the match traffic, ~6x a token's
@@ -209,7 +210,15 @@ mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv /* host */, const v
  * the step before it); enqueues match, complete and the
  * reduce/merge on `stream`, then amend on the amend stream (or on `stream`
  * with MAC_F_SYNC_AMEND; with MAC_F_FUSED_AMEND the reduce does the ring
- * update and no amend is enqueued).  When the amend stream was supplied to
+ * update and no amend is enqueued).  On an amend stream the handle created
+ * (amend_stream NULL at mac_init), a thread of the handle enqueues that amend
+ * and its ordering after the reduce, so the call returns once the reduce is
+ * enqueued; the handle's next call (and mac_stats, mac_reset,
+ * mac_debug_last, mac_prefill, mac_destroy) first waits until that thread
+ * has done so, and reports a HIP error it met there.  When calls of one
+ * handle come back to back with nothing between them, the calls enqueue the
+ * amend themselves for a while, as the thread would only add its wake-up.
+ * When the amend stream was supplied to
  * mac_init (layers may share it), the complete kernel also waits for all work
  * queued on it before it: complete gives every wave of a full-occupancy grid
  * an equal share, and a kernel still resident when it starts would delay some
