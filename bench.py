@@ -470,6 +470,52 @@ def workload_record(name, warm, steps, bands=(None,), loop=True):
     return rec
 
 
+def multilayer_record(name="llama32k", layers=8, warm=16, steps=32):
+    """Several layers of one small-batch workload decoded back to back, each
+    layer its own handle, cache and (library-created) amend stream, all on one
+    decode stream with no host synchronisation: µs per layer and step for MAC
+    with async amend, with fused amend, and for full attention.  Between two
+    calls of a layer the other layers' calls run, as in a model's decode."""
+    import torch
+    import kv_reuse_amd as mac
+    from workloads import get_config
+    w = get_config(name)
+    total = warm + steps
+    caches = [workload_cache(w, total) for _ in range(layers)]
+    k_rows, v_rows, q_dev = caches[0][1], caches[0][2], caches[0][3]
+    res = {}
+    for label, flags in (("mac", 0), ("mac_fused_amend", mac.MAC_F_FUSED_AMEND),
+                         ("full_attention", mac.MAC_F_DISABLE_REUSE)):
+        bns = [Bench(w, flags, *c[0]) for c in caches]
+        for t in range(warm):
+            for bn in bns:
+                bn.enqueue(t, q_dev[t], k_rows[t], v_rows[t])
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(bns[0].stream)
+        for t in range(warm, total):
+            for bn in bns:
+                bn.enqueue(t, q_dev[t], k_rows[t], v_rows[t])
+        e1.record(bns[0].stream)
+        torch.cuda.synchronize()
+        hits = sum(bn.layer.stats()["hits"] for bn in bns)
+        for bn in bns:
+            bn.layer.close()
+        us = e0.elapsed_time(e1) * 1e3 / (steps * layers)
+        res[label] = {"us_per_layer_step": us, "tokens_per_s": w.B / (us * 1e-6 * layers),
+                      "head_hit_rate": hits / (total * layers * w.B * w.Hq)}
+    del caches, k_rows, v_rows, q_dev
+    torch.cuda.empty_cache()
+    return {"workload": name, "layers": layers, "batch": w.B, "context": w.C, "warmup": warm,
+            "steps": steps, **res,
+            "speedup_vs_full": res["full_attention"]["us_per_layer_step"] / res["mac"]["us_per_layer_step"],
+            "speedup_vs_full_fused_amend": (res["full_attention"]["us_per_layer_step"] /
+                                            res["mac_fused_amend"]["us_per_layer_step"]),
+            "note": "layers decoded back to back on one stream, no host synchronisation; "
+                    "attention path only (append, match, complete, reduce, amend)"}
+
+
 def contgen_run(warm, steps, decisions=True):
     """Continuous generation: 32 layers x batch 32, 16384-token prompt then
     generated tokens, K/V appended every step and amend overlapping the next
@@ -1188,6 +1234,8 @@ def main():
                                         bands=(64, 256, 1024)),
             # continuous generation at mid-run context, W + 8 warm-up steps
             "contgen": contgen_run(_gc("contgen").W + 8, 16),
+            # small-batch layers back to back, each with its own amend stream
+            "multilayer_32k": multilayer_record("llama32k", 8, 16, 32),
         }
 
     cpu = None
