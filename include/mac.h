@@ -211,13 +211,14 @@ mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv /* host */, const v
  * reduce/merge on `stream`, then amend on the amend stream (or on `stream`
  * with MAC_F_SYNC_AMEND; with MAC_F_FUSED_AMEND the reduce does the ring
  * update and no amend is enqueued).  On an amend stream the handle created
- * (amend_stream NULL at mac_init), a thread of the handle enqueues that amend
- * and its ordering after the reduce, so the call returns once the reduce is
- * enqueued; the handle's next call (and mac_stats, mac_reset,
- * mac_debug_last, mac_prefill, mac_destroy) first waits until that thread
- * has done so, and reports a HIP error it met there.  When calls of one
- * handle come back to back with nothing between them, the calls enqueue the
- * amend themselves for a while, as the thread would only add its wake-up.
+ * (amend_stream NULL at mac_init), a thread of the handle launches that amend
+ * once it sees (blocking on the host) that the call's reduce has run, so the
+ * call returns once the reduce is enqueued; the handle's next call (and
+ * mac_stats, mac_reset, mac_debug_last, mac_prefill, mac_destroy) first waits
+ * until that thread has launched it, and reports a HIP error it met there.
+ * When calls of one handle come back to back with nothing between them, the
+ * calls enqueue the amend themselves for a while (after a cross-stream wait),
+ * as the thread would only add its wake-up.
  * When the amend stream was supplied to
  * mac_init (layers may share it), the complete kernel also waits for all work
  * queued on it before it: complete gives every wave of a full-occupancy grid

@@ -41,16 +41,18 @@ struct mac_ctx {
     hipStream_t amend_on[2] = {};
     hipEvent_t tm[6] = {};
     // The default form on an amend stream the handle owns: a worker thread
-    // of the handle enqueues each call's amend hand-off (the cross-stream wait
-    // after the reduce, which costs 11-16 us of host time, the amend launch,
-    // its end event), so the call returns once its reduce is enqueued.  Every
-    // later call on the handle first waits until the worker has enqueued the
-    // posted hand-off (wk_posted false), and takes over any error it met.
-    // When a decode call finds the worker still busy (calls of this handle
-    // back to back, nothing else between them), the next WK_BACKOFF calls do
-    // the hand-off themselves: the worker only adds its wake-up there.
-    // Measured, 8 layers back to back: 62 -> 46 us per layer and step at
-    // 32K x 1, 56 -> 38 us at 4096 x 1.
+    // of the handle waits on the host until the call's reduce has run
+    // (ev_attn), then launches the amend and records its end event, so the
+    // call returns once its reduce is enqueued and no cross-stream wait is
+    // enqueued at all (one costs 11-16 us of host time, and the HIP runtime
+    // serialises it against the caller's launches).  Every later call on the
+    // handle first waits until the worker has enqueued the posted amend
+    // (wk_posted false), and takes over any error it met.  When a decode call
+    // finds the worker still busy (calls of this handle back to back, nothing
+    // else between them), the next WK_BACKOFF calls enqueue the hand-off
+    // themselves (a cross-stream wait): the worker would only add its
+    // wake-up there.  Measured, 8 layers back to back, us per layer and
+    // step: 62 -> 37-39 at 32K x 1, 56 -> 30-35 at 4096 x 1.
     struct Job {
         mac::State S;
         mac::KvView v;
@@ -332,9 +334,11 @@ hipError_t mark_done(mac_ctx *h, hipStream_t st, hipEvent_t recorded = nullptr)
 }
 
 // The amend of the call whose reduce ev_attn follows (recorded on the decode
-// stream), on the amend stream, then ev_amend[cur] after it.
+// stream), on the amend stream, then ev_amend[cur] after it.  host_wait: wait
+// on the host until ev_attn has been reached instead of enqueueing a
+// cross-stream wait (the worker thread's way).
 hipError_t enqueue_amend(mac_ctx *h, const mac::State &S, const mac::KvView &v, int cur,
-                         bool timing, const char **what)
+                         bool timing, bool host_wait, const char **what)
 {
 #define MAC_TRY(call)                                                                       \
     do {                                                                                    \
@@ -345,7 +349,10 @@ hipError_t enqueue_amend(mac_ctx *h, const mac::State &S, const mac::KvView &v, 
         }                                                                                   \
     } while (0)
     hipStream_t as = h->amend_stream;
-    MAC_TRY(hipStreamWaitEvent(as, h->ev_attn, 0));
+    if (host_wait)
+        MAC_TRY(hipEventSynchronize(h->ev_attn));
+    else
+        MAC_TRY(hipStreamWaitEvent(as, h->ev_attn, 0));
     if (timing)
         MAC_TRY(hipEventRecord(h->tm[4], as));
     MAC_TRY(mac::launch_amend(h->shape, S, v, h->kv_fp32, as));
@@ -367,7 +374,7 @@ void worker_main(mac_ctx *h)
         const mac_ctx::Job j = h->wk_job;
         lk.unlock();
         const char *what = "";
-        const hipError_t e = enqueue_amend(h, j.S, j.v, j.cur, j.timing, &what);
+        const hipError_t e = enqueue_amend(h, j.S, j.v, j.cur, j.timing, true, &what);
         lk.lock();
         if (e != hipSuccess && h->wk_err == hipSuccess) {
             h->wk_err = e;
@@ -638,7 +645,9 @@ mac_status mac_init(const mac_config *cfg, void *main_stream, void *amend_stream
     // other devices only.  Measured: 1.5 to 3 us less per call on short
     // steps, the same on long ones.
     constexpr unsigned ORDER_EVENT = hipEventDisableTiming | hipEventDisableSystemFence;
-    if (hipEventCreateWithFlags(&h->ev_attn, ORDER_EVENT) != hipSuccess ||
+    // ev_attn is also what the amend worker waits for on the host: blocking,
+    // so a handle's thread sleeps instead of spinning a core
+    if (hipEventCreateWithFlags(&h->ev_attn, ORDER_EVENT | hipEventBlockingSync) != hipSuccess ||
         hipEventCreateWithFlags(&h->ev_amend[0], ORDER_EVENT) != hipSuccess ||
         hipEventCreateWithFlags(&h->ev_amend[1], ORDER_EVENT) != hipSuccess ||
         hipEventCreateWithFlags(&h->ev_drain, ORDER_EVENT) != hipSuccess ||
