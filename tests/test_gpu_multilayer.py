@@ -14,16 +14,20 @@ from workloads import get_config, scaled
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_layers_share_amend_stream_and_match_oracle(gpu_lib, fused):
+@pytest.mark.parametrize("fused,shared", [(False, True), (True, True), (False, False)])
+def test_layers_share_amend_stream_and_match_oracle(gpu_lib, fused, shared):
     """Default: amend of every layer on one shared stream.  Fused amend: no
-    amend stream work at all, the layers' reduce kernels update their rings."""
+    amend stream work at all, the layers' reduce kernels update their rings.
+    Not shared: each layer creates its own amend stream, and its thread
+    launches each call's amend once the reduce has run while the other
+    layers' calls are enqueued."""
     import torch
     import kv_reuse_amd as mac
     from gpu_harness import Lockstep
     w = scaled(get_config("contgen"), B=4, C=1500, steps=40, layers=3, jump_every=16)
-    print("case contgen layers", w.layers, "B", w.B, "C", w.C, "fused", fused, flush=True)
-    amend = torch.cuda.Stream()
+    print("case contgen layers", w.layers, "B", w.B, "C", w.C, "fused", fused, "shared", shared,
+          flush=True)
+    amend = torch.cuda.Stream() if shared else None
     flags = mac.MAC_F_FUSED_AMEND if fused else 0
     runs = [Lockstep(w, layer=layer, amend_stream=amend, flags=flags)
             for layer in range(w.layers)]
