@@ -484,7 +484,8 @@ def multilayer_record(name="llama32k", layers=8, warm=16, steps=32):
     caches = [workload_cache(w, total) for _ in range(layers)]
     k_rows, v_rows, q_dev = caches[0][1], caches[0][2], caches[0][3]
     res = {}
-    for label, flags in (("mac", 0), ("mac_fused_amend", mac.MAC_F_FUSED_AMEND),
+    for label, flags in (("mac", 0), ("mac_sync_amend", mac.MAC_F_SYNC_AMEND),
+                         ("mac_fused_amend", mac.MAC_F_FUSED_AMEND),
                          ("full_attention", mac.MAC_F_DISABLE_REUSE)):
         bns = [Bench(w, flags, *c[0]) for c in caches]
         for t in range(warm):
@@ -510,6 +511,8 @@ def multilayer_record(name="llama32k", layers=8, warm=16, steps=32):
     return {"workload": name, "layers": layers, "batch": w.B, "context": w.C, "warmup": warm,
             "steps": steps, **res,
             "speedup_vs_full": res["full_attention"]["us_per_layer_step"] / res["mac"]["us_per_layer_step"],
+            "speedup_vs_full_sync_amend": (res["full_attention"]["us_per_layer_step"] /
+                                           res["mac_sync_amend"]["us_per_layer_step"]),
             "speedup_vs_full_fused_amend": (res["full_attention"]["us_per_layer_step"] /
                                             res["mac_fused_amend"]["us_per_layer_step"]),
             "note": "layers decoded back to back on one stream, no host synchronisation; "
@@ -554,7 +557,8 @@ def contgen_run(warm, steps, decisions=True):
     main = torch.cuda.current_stream()
     amend = torch.cuda.Stream()
     res = {}
-    passes = [("mac", 0), ("mac_fused_amend", mac.MAC_F_FUSED_AMEND),
+    passes = [("mac", 0), ("mac_sync_amend", mac.MAC_F_SYNC_AMEND),
+              ("mac_fused_amend", mac.MAC_F_FUSED_AMEND),
               ("mac_fused_amend_ring_bf16", mac.MAC_F_FUSED_AMEND | mac.MAC_F_RING_BF16),
               ("full", mac.MAC_F_DISABLE_REUSE)]
     if decisions:
@@ -606,10 +610,13 @@ def contgen_run(warm, steps, decisions=True):
     return {"workload": "contgen", "batch": w.B, "layers": L, "context_at_window": ctx0,
             "q_heads": w.Hq, "kv_heads": w.Hkv, "ring": w.W, "band": w.r, "tau": w.tau,
             "rho": list(base.rho), "jump_every": base.jump_every, "warmup": warm,
-            "steps": steps, "mac": res["mac"], "mac_fused_amend": res["mac_fused_amend"],
+            "steps": steps, "mac": res["mac"], "mac_sync_amend": res["mac_sync_amend"],
+            "mac_fused_amend": res["mac_fused_amend"],
             "mac_fused_amend_ring_bf16": res["mac_fused_amend_ring_bf16"],
             "full_attention": res["full"],
             "speedup_vs_full": res["mac"]["tokens_per_s"] / res["full"]["tokens_per_s"],
+            "speedup_vs_full_sync_amend": (res["mac_sync_amend"]["tokens_per_s"] /
+                                           res["full"]["tokens_per_s"]),
             "speedup_vs_full_fused_amend": (res["mac_fused_amend"]["tokens_per_s"] /
                                             res["full"]["tokens_per_s"]),
             "speedup_vs_full_fused_amend_ring_bf16": (
