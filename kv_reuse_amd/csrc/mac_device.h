@@ -528,16 +528,23 @@ __device__ __forceinline__ int page_owner(long x, int nW, int P)
 // round by round (block b in round b / CUs), and the CU's issue arbiter
 // favours older waves: with equal shares the first round's waves finish
 // first.  At three rounds (G <= 4) the last round also holds the slowest
-// waves and sets the end of the launch (wave ends at 128K x 16 per round,
-// median / max: 967 / 1004, 998 / 1025, 1025 / 1054 us), so with many pages
-// per wave the balanced plan gives round k the weight
-// 1000 + SLOT_TILT * (slots - 1 - 2k) per mille: 1120 / 1000 / 880 at three
-// rounds.  Complete at 128K x 16 (mean of 3-4 runs per setting, two boxes):
-// +-6 % 1081-1088 us, +-9 % 1079, +-12 % 1071-1072, +-16 % 1070; full
-// attention 1322-1328 us at +-6 %, 1318-1323 at +-12 %.
+// waves and sets the end of the launch, so with many pages per wave the
+// balanced plan weights the rounds' shares (per mille) by ROUND_W3.  A wave
+// timeline at 128K x 16 under 1120 / 1000 / 880 (an earlier, symmetric
+// choice) had round 0 ending last (median / max 998 / 1027 us against 960 /
+// 995 and 973 / 1018); 1090 / 1030 / 880 then measured, same box, six runs
+// each: the mixed step 1080.3 -> 1073.2 us, full attention 1340.5 -> 1333.9
+// us (complete 1325.4 -> 1320.0 us).  Other round counts take
+// 1000 + SLOT_TILT * (slots - 1 - 2k).
 // At two rounds (G = 8) the rounds' slowest waves end together (310 / 312 us
-// of 8 x 122880) and the weights only lengthened the first round (+2.8 %).
+// of 8 x 122880) and weights only lengthened the first round (+2.8 %).
+constexpr int ROUND_W3[3] = {1090, 1030, 880};
 constexpr int SLOT_TILT = 60;
+
+__device__ __forceinline__ int round_weight(int k, int S)
+{
+    return S == 3 ? ROUND_W3[k] : 1000 + SLOT_TILT * (S - 1 - 2 * k);
+}
 
 __device__ __forceinline__ bool tilted_plan(const State &st, int nW, int P)
 {
@@ -550,8 +557,8 @@ __device__ __forceinline__ long long cum_weight(int w, int Nk, int S)
     const int k = w / Nk, j = w % Nk;
     long long c = 0;
     for (int i = 0; i < k; ++i)
-        c += (long long)Nk * (1000 + SLOT_TILT * (S - 1 - 2 * i));
-    return c + (long long)j * (1000 + SLOT_TILT * (S - 1 - 2 * k));
+        c += (long long)Nk * round_weight(i, S);
+    return c + (long long)j * round_weight(k, S);
 }
 
 // First flattened page of worker w's share (w = nW gives P).
@@ -564,7 +571,7 @@ __device__ __forceinline__ long share_start(const State &st, int w, int nW, int 
 }
 
 // Owner of flattened page x under share_start: the last worker whose share
-// starts at or before x (every share holds at least 15 pages when tilted).
+// starts at or before x (every share holds at least 14 pages when tilted).
 __device__ inline int share_owner(const State &st, long x, int nW, int P)
 {
     if (!tilted_plan(st, nW, P))
