@@ -232,9 +232,13 @@ mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv /* host */, const v
  * caller may capture append + decode on one stream into a HIP graph and
  * replay it, updating the positions, seq_lens and query buffers in place
  * between replays (warm up and capture on the same stream).  The default
- * form orders the amend stream with events chosen per call on the host and
- * must not be captured; neither may the stale-by-one ring, whose buffers
- * alternate per call on the host. */
+ * form orders the amend stream with events chosen per call on the host, the
+ * stale-by-one ring alternates its buffers per call on the host, and
+ * MAC_F_TIMING records events per kernel: on a stream being captured these
+ * return MAC_EUNSUPPORTED before enqueuing anything, and the handle stays
+ * usable.  The handle's amend thread makes no call on a captured stream; it
+ * runs in the relaxed capture mode, so a capture elsewhere in the process
+ * does not stop it. */
 mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv /* host */,
                            const float *q_pre_rope, float *out, const int32_t *override_pos,
                            void *stream);

@@ -315,12 +315,18 @@ hipError_t follow(mac_ctx *h, hipStream_t st)
 // Mark the end of a call's work on st (skipped while st is being captured).
 // `recorded`: an event the call has just recorded on st after its last work
 // (the hand-off to the amend stream), which then serves as the end mark.
-hipError_t mark_done(mac_ctx *h, hipStream_t st, hipEvent_t recorded = nullptr)
+// `known`: st's capture status when the caller has already queried it.
+hipError_t mark_done(mac_ctx *h, hipStream_t st, hipEvent_t recorded = nullptr,
+                     const hipStreamCaptureStatus *known = nullptr)
 {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    hipError_t e = hipStreamIsCapturing(st, &cs);
-    if (e != hipSuccess)
-        return e;
+    if (known) {
+        cs = *known;
+    } else {
+        const hipError_t e = hipStreamIsCapturing(st, &cs);
+        if (e != hipSuccess)
+            return e;
+    }
     h->last_stream = st;
     h->done_valid = cs == hipStreamCaptureStatusNone;
     if (!h->done_valid)
@@ -366,6 +372,11 @@ hipError_t enqueue_amend(mac_ctx *h, const mac::State &S, const mac::KvView &v, 
 void worker_main(mac_ctx *h)
 {
     (void)hipSetDevice(h->device);
+    // a graph capture that another thread of the process runs in global mode
+    // must not turn this thread's host wait into an error: its calls touch
+    // only streams and events of the handle, none of them captured
+    hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+    (void)hipThreadExchangeStreamCaptureMode(&mode);
     std::unique_lock<std::mutex> lk(h->wk_mu);
     for (;;) {
         h->wk_cv.wait(lk, [h] { return h->wk_posted || h->wk_stop; });
@@ -723,10 +734,25 @@ mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv, const void *k_new,
 
 namespace {
 
+// Decode calls that enqueue the same work with the same arguments every call,
+// so that a graph captured from one replays the step: no amend on another
+// stream (its events are chosen per call on the host), no alternating
+// buffers (stale-by-one ring), no per-kernel timing events.
+bool capturable(const mac_ctx *h, hipStream_t st)
+{
+    const unsigned f = h->cfg.flags;
+    if (f & (MAC_F_STALE_RING | MAC_F_TIMING))
+        return false;
+    const bool amend_elsewhere = h->shape.reuse && h->shape.nseg == 1 &&
+                                 !(f & MAC_F_SYNC_AMEND) && h->amend_stream != st;
+    return !amend_elsewhere;
+}
+
 // The enqueue sequence of one decode call on stream st; `what` names the HIP
 // call that failed.
 hipError_t decode_enqueue(mac_ctx *h, const mac_kv_view *kv, const float *q_pre_rope, float *out,
-                          const int32_t *override_pos, hipStream_t st, const char **what)
+                          const int32_t *override_pos, hipStream_t st,
+                          hipStreamCaptureStatus capture, const char **what)
 {
 #define MAC_TRY(call)                                                                       \
     do {                                                                                    \
@@ -813,7 +839,7 @@ hipError_t decode_enqueue(mac_ctx *h, const mac_kv_view *kv, const float *q_pre_
         }
         h->amend_pending[cur] = true;
     }
-    MAC_TRY(mark_done(h, st, end_mark));
+    MAC_TRY(mark_done(h, st, end_mark, &capture));
     h->timed_step = timing;
     h->calls += 1;
     return hipSuccess;
@@ -837,8 +863,15 @@ mac_status mac_decode_step(mac_handle h, const mac_kv_view *kv, const float *q_p
     if (!aligned16(q_pre_rope) || !aligned16(out))
         return fail(h, MAC_EINVAL, "q_pre_rope and out must be 16-byte aligned");
     hipStream_t st = stream ? (hipStream_t)stream : h->main_stream;
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    MAC_HIP(h, hipStreamIsCapturing(st, &capture));
+    if (capture != hipStreamCaptureStatusNone && !capturable(h, st))
+        return fail(h, MAC_EUNSUPPORTED,
+                    "this form chooses its events or buffers per call on the host and cannot be "
+                    "captured into a graph (capturable: fused amend or amend on the decode "
+                    "stream, or reuse disabled; without the stale ring or per-kernel timing)");
     const char *what = "";
-    const hipError_t e = decode_enqueue(h, kv, q_pre_rope, out, override_pos, st, &what);
+    const hipError_t e = decode_enqueue(h, kv, q_pre_rope, out, override_pos, st, capture, &what);
     if (e != hipSuccess) {
         h->broken = true;
         return fail_hip(h, what, e);

@@ -95,3 +95,79 @@ def test_graph_replay_equals_eager(gpu_lib, form):
     finally:
         eager.close()
         graphed.close()
+
+
+@pytest.mark.parametrize("form", ["async", "stale", "timing"])
+def test_capture_of_per_call_forms_is_rejected(gpu_lib, form):
+    """The forms whose calls choose events or buffers on the host refuse a
+    stream being captured with MAC_EUNSUPPORTED, enqueue nothing and stay
+    usable: the steps after the refused call are bit-equal to a twin handle
+    that never saw it.  The async form's amend thread then waits while
+    another stream is being captured (global mode) and must not fail."""
+    import kv_reuse_amd as mac
+    flags = {"async": 0, "stale": mac.MAC_F_STALE_RING, "timing": mac.MAC_F_TIMING}[form]
+    w = scaled(get_config("b16_128k"), B=2, C=600, steps=12, r=64, rho=("const", 0.97))
+    total = 8
+    print("capture refusal case", form, "B", w.B, "C", w.C, "steps", total, flush=True)
+    K, V = kv_logical(w, "cuda")
+    idx = torch.arange(w.C, w.C + total, device="cuda")
+    k_rows = K[:, :, idx].permute(2, 0, 1, 3).contiguous()
+    v_rows = V[:, :, idx].permute(2, 0, 1, 3).contiguous()
+    q = torch.as_tensor(queries(w, steps=total), device="cuda")
+    tab = page_table(w)
+    table = torch.as_tensor(tab, device="cuda")
+
+    def make():
+        kc, vc = to_paged(K, tab), to_paged(V, tab)
+        seq = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+        pos = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+        cfg = mac.make_config(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, ring_size=w.W,
+                              band=w.r, tau=w.tau, rope_theta=w.theta, layout=mac.MAC_KV_PAGED,
+                              kv_dtype=mac.MAC_BF16, max_seq_len=w.n_cap, flags=flags)
+        layer = mac.MacLayer(cfg)
+        view = mac.make_kv_view(kc, vc, seq, table, num_pages=kc.shape[0])
+        out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+        return layer, view, seq, pos, out, (kc, vc)
+
+    a, b = make(), make()
+    s = torch.cuda.Stream()
+    other = torch.cuda.Stream()
+    x = torch.ones(1 << 20, device="cuda")
+
+    def step(h, t, stream=None):
+        layer, view, seq, pos, out, _ = h
+        with torch.cuda.stream(stream or torch.cuda.current_stream()):
+            pos.fill_(w.C + t)
+            seq.fill_(w.C + t + 1)
+            layer.append_kv(view, k_rows[t], v_rows[t], pos, stream)
+            layer.decode_step(view, q[t], out, None, stream)
+
+    try:
+        refused = 0
+        for t in range(total):
+            torch.cuda.synchronize()
+            step(b, t)
+            step(a, t, s)
+            if form == "async":
+                # a capture on another stream while a's amend thread waits
+                g2 = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g2, stream=other):
+                    x.mul_(1.0)
+            if t == 2:
+                g = torch.cuda.CUDAGraph()
+                layer, view, seq, pos, out, _ = a
+                with torch.cuda.graph(g, stream=s):
+                    with pytest.raises(mac.MacError) as err:
+                        layer.decode_step(view, q[t], out, None, s)
+                    refused += 1
+                assert err.value.status == mac.MAC_EUNSUPPORTED, err.value
+            torch.cuda.synchronize()
+            assert torch.equal(a[4], b[4]), ("step", t)
+        st_a, st_b = a[0].stats(), b[0].stats()
+        print("  steps", st_a["steps"], "hits", st_a["hits"], "refused", refused, flush=True)
+        assert refused == 1
+        assert st_a["steps"] == st_b["steps"] == total
+        assert st_a["hits"] == st_b["hits"] > 0
+    finally:
+        a[0].close()
+        b[0].close()
