@@ -216,9 +216,10 @@ mac_status mac_append_kv(mac_handle h, const mac_kv_view *kv /* host */, const v
  * call returns once the reduce is enqueued; the handle's next call (and
  * mac_stats, mac_reset, mac_debug_last, mac_prefill, mac_destroy) first waits
  * until that thread has launched it, and reports a HIP error it met there.
- * When calls of one handle come back to back with nothing between them, the
- * calls enqueue the amend themselves for a while (after a cross-stream wait),
- * as the thread would only add its wake-up.
+ * When a call finds that thread still waiting (the GPU is behind the host,
+ * calls of one handle back to back), the following calls enqueue their amend
+ * on `stream` after the reduce, until a call finds the GPU caught up with the
+ * previous one; the results are the same bits either way.
  * When the amend stream was supplied to
  * mac_init (layers may share it), the complete kernel also waits for all work
  * queued on it before it: complete gives every wave of a full-occupancy grid

@@ -48,11 +48,14 @@ struct mac_ctx {
     // serialises it against the caller's launches).  Every later call on the
     // handle first waits until the worker has enqueued the posted amend
     // (wk_posted false), and takes over any error it met.  When a decode call
-    // finds the worker still busy (calls of this handle back to back, nothing
-    // else between them), the next WK_BACKOFF calls enqueue the hand-off
-    // themselves (a cross-stream wait): the worker would only add its
-    // wake-up there.  Measured, 8 layers back to back, us per layer and
-    // step: 62 -> 37-39 at 32K x 1, 56 -> 30-35 at 4096 x 1.
+    // finds the worker still busy, the GPU is behind the host (calls of this
+    // handle back to back, nothing else between them): the next WK_BACKOFF
+    // calls run their amend on the decode stream, where it needs no hand-off
+    // between queues, and the period is renewed for as long as the previous
+    // call has not finished when it ends.  Measured, 8 layers back to back, us
+    // per layer and step: 62 -> 37-39 at 32K x 1, 56 -> 30-35 at 4096 x 1;
+    // one layer in a tight loop: 59-61 -> 43 at 32K x 1, 62-64 -> 48-49 at
+    // 128K x 16 (every head hitting), 54-56 -> 37 at 4096 x 1.
     struct Job {
         mac::State S;
         mac::KvView v;
@@ -810,9 +813,20 @@ hipError_t decode_enqueue(mac_ctx *h, const mac_kv_view *kv, const float *q_pre_
         MAC_TRY(hipEventRecord(h->tm[3], st));
 
     hipEvent_t end_mark = nullptr;   // an event recorded on st after this call's last work
-    const bool via_worker = h->wk_on && h->amend_stream != st && h->wk_backoff == 0;
-    if (h->wk_backoff > 0)
-        --h->wk_backoff;
+    const bool backing_off = h->wk_on && h->wk_backoff > 0;
+    if (backing_off && --h->wk_backoff == 0 && h->done_valid && h->last_stream == st) {
+        // the period ends only once the GPU has caught up with the previous
+        // call: handing off to the thread while it is behind would stall the
+        // next call until the GPU drains
+        const hipError_t q = hipEventQuery(h->done_ev);
+        if (q == hipErrorNotReady)
+            h->wk_backoff = WK_BACKOFF;
+        else if (q != hipSuccess) {
+            *what = "hipEventQuery";
+            return q;
+        }
+    }
+    const bool via_worker = h->wk_on && h->amend_stream != st && !backing_off;
     if (h->shape.reuse && !fused && via_worker) {
         MAC_TRY(hipEventRecord(h->ev_attn, st));
         end_mark = h->ev_attn;
@@ -820,7 +834,9 @@ hipError_t decode_enqueue(mac_ctx *h, const mac_kv_view *kv, const float *q_pre_
         h->amend_on[cur] = nullptr;
         h->amend_pending[cur] = true;
     } else if (h->shape.reuse && !fused) {
-        hipStream_t as = (h->cfg.flags & MAC_F_SYNC_AMEND) ? st : h->amend_stream;
+        // backing off, the GPU is behind the host: amend on the decode stream
+        // costs it no hand-off between queues, and the host no stream wait
+        hipStream_t as = ((h->cfg.flags & MAC_F_SYNC_AMEND) || backing_off) ? st : h->amend_stream;
         if (as != st) {
             MAC_TRY(hipEventRecord(h->ev_attn, st));
             MAC_TRY(hipStreamWaitEvent(as, h->ev_attn, 0));
