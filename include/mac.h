@@ -188,7 +188,9 @@ size_t mac_aux_bytes(const mac_config *cfg /* host */, int32_t num_cu);
 mac_status mac_init(const mac_config *cfg /* host */, void *main_stream, void *amend_stream,
                     mac_handle *out /* host */);
 
-/* Free everything mac_init allocated; synchronises the handle's streams. */
+/* Free everything mac_init allocated.  Synchronises the handle's streams and
+ * waits for the last call's work on the stream it ran on (unless that stream
+ * was being captured). */
 mac_status mac_destroy(mac_handle h);
 
 /* Empty every ring and zero the counters (asynchronous on the main stream,

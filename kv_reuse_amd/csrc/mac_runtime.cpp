@@ -458,6 +458,10 @@ void stop_worker(mac_ctx *h)
 void release(mac_ctx *h)
 {
     stop_worker(h);   // it finishes a posted hand-off first
+    // the last call may have run on a stream of the caller's: its end mark
+    // follows all its work there (an amend on that stream included)
+    if (h->done_valid && h->done_ev)
+        (void)hipEventSynchronize(h->done_ev);
     if (h->main_stream || h->amend_stream) {
         if (h->amend_stream)
             (void)hipStreamSynchronize(h->amend_stream);
