@@ -177,8 +177,10 @@ typedef struct {
 /* Check a configuration without touching the GPU (host only). */
 mac_status mac_config_validate(const mac_config *cfg /* host */);
 
-/* Device bytes mac_init would allocate for cfg on a device with num_cu
- * compute units (host only). */
+/* An upper bound of the device bytes mac_init allocates for cfg on a device
+ * with num_cu compute units: it counts 8 resident blocks of the complete
+ * kernel per CU, where mac_init sizes the per-wave partials for the blocks
+ * that actually fit (2 or 3).  Host only; 0 for an invalid cfg. */
 size_t mac_aux_bytes(const mac_config *cfg /* host */, int32_t num_cu);
 
 /* Create a handle: validate cfg, allocate the rings, summaries and work

@@ -278,6 +278,8 @@ def test_stats_match_oracle_counts(fused):
         amend_toks = 0 if fused else 20 * w.B * w.Hkv * w.r   # every step has m >= r here
         assert st["kv_tokens_amend"] == amend_toks
         assert st["bad_input"] == 0 and st["aux_bytes"] > 0
+        n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+        assert st["aux_bytes"] <= mac.mac_aux_bytes(ls.cfg, n_cu)   # the bound the header states
     finally:
         ls.close()
 
