@@ -541,9 +541,13 @@ __device__ __forceinline__ int page_owner(long x, int nW, int P)
 constexpr int ROUND_W3[3] = {1090, 1030, 880};
 constexpr int SLOT_TILT = 60;
 
+// (selects with constant indices: an indexed read of the table would be a
+// memory load, and the plan calls this in dependent chains)
 __device__ __forceinline__ int round_weight(int k, int S)
 {
-    return S == 3 ? ROUND_W3[k] : 1000 + SLOT_TILT * (S - 1 - 2 * k);
+    if (S == 3)
+        return k == 0 ? ROUND_W3[0] : k == 1 ? ROUND_W3[1] : ROUND_W3[2];
+    return 1000 + SLOT_TILT * (S - 1 - 2 * k);
 }
 
 __device__ __forceinline__ bool tilted_plan(const State &st, int nW, int P)
@@ -552,26 +556,31 @@ __device__ __forceinline__ bool tilted_plan(const State &st, int nW, int P)
 }
 
 // Weight of the workers before worker w (nW = slots * Nk workers, round w / Nk).
-__device__ __forceinline__ long long cum_weight(int w, int Nk, int S)
+__device__ __forceinline__ long cum_weight(int w, int Nk, int S)
 {
     const int k = w / Nk, j = w % Nk;
-    long long c = 0;
+    int c = 0;
     for (int i = 0; i < k; ++i)
-        c += (long long)Nk * round_weight(i, S);
-    return c + (long long)j * round_weight(k, S);
+        c += round_weight(i, S);
+    return (long)c * Nk + (long)j * round_weight(k, S);
 }
 
-// First flattened page of worker w's share (w = nW gives P).
+// First flattened page of worker w's share (w = nW gives P).  The weighted
+// form is floor(P * cum(w) / cum(nW)), with P * cum(w) < 2^53 (P < 2^31,
+// cum(nW) = waves x per-mille weights < 2^22).
 __device__ __forceinline__ long share_start(const State &st, int w, int nW, int P)
 {
     if (!tilted_plan(st, nW, P))
         return div_floor((long)w * P, nW);
     const int S = st.slots, Nk = nW / S;
-    return (long)((long long)P * cum_weight(w, Nk, S) / cum_weight(nW, Nk, S));
+    return div_floor((long)P * cum_weight(w, Nk, S), (int)cum_weight(nW, Nk, S));
 }
 
 // Owner of flattened page x under share_start: the last worker whose share
 // starts at or before x (every share holds at least 14 pages when tilted).
+// Tilting shares of under 16 pages measured slower (same box, three runs:
+// complete at 32K x 1, full attention, 32.9 -> 37.1 us with 4 pages as the
+// floor), although the last round's waves end ~4 us after the first's there.
 __device__ inline int share_owner(const State &st, long x, int nW, int P)
 {
     if (!tilted_plan(st, nW, P))
