@@ -22,7 +22,12 @@ from workloads import bf16_bits, kv_logical, page_table, queries, to_paged
 MAX_ABS = 2e-3
 ROW_REL = 1e-2
 FORCED_FRAC = 0.01      # forced decisions allowed, as a share of all decisions
-FORCED_MIN = 3          # ... but at least this many in a short run
+# ... but at least this many early in a run: near-tau decisions arrive as Poisson
+# counts, and where tau sits at the mode of the nearest-entry distances (a
+# random-sweep case: tau 0.208, distances 0.20 +- 0.01) 160 decisions hold ~2
+# of them on average and 4 in one step of that case.  A widened forcing rule
+# would force a large share, which the 1 % bound still catches.
+FORCED_MIN = 10
 
 
 def force_near(res, override=None):
