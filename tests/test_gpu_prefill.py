@@ -7,6 +7,8 @@ window.  Decisions (matched positions) bit-exact; outputs within max-abs 2e-3
 and per-row relative 1e-2.  Near-threshold and near-tie decisions are forced
 to the oracle's through the override input, as in the decode tests.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -228,7 +230,10 @@ def _prefill_draw(i, rng):
                 ring_bf16=bool(rng.random() < 0.35))
 
 
-_PF_SWEEP = [_prefill_draw(i, rng) for rng in [np.random.default_rng(4242)] for i in range(8)]
+# a longer or different draw on demand: MAC_PREFILL_SWEEP_CASES=60 MAC_PREFILL_SWEEP_SEED=7
+_PF_N = int(os.environ.get("MAC_PREFILL_SWEEP_CASES", "8"))
+_PF_SEED = int(os.environ.get("MAC_PREFILL_SWEEP_SEED", "4242"))
+_PF_SWEEP = [_prefill_draw(i, rng) for rng in [np.random.default_rng(_PF_SEED)] for i in range(_PF_N)]
 _PF_IDS = ["p%d-B%d-%dq%dkv-N%d" % (c["i"], c["B"], c["Hq"], c["Hkv"], c["N"]) for c in _PF_SWEEP]
 
 
