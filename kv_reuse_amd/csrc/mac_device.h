@@ -550,9 +550,12 @@ __device__ __forceinline__ int round_weight(int k, int S)
     return 1000 + SLOT_TILT * (S - 1 - 2 * k);
 }
 
+// Three or more dispatch rounds (G <= 4): the rounds' waves end in order.
+__device__ __forceinline__ bool tilt_rounds(const State &st) { return st.slots >= 3; }
+
 __device__ __forceinline__ bool tilted_plan(const State &st, int nW, int P)
 {
-    return st.slots >= 3 && nW == st.n_workers && P >= 16 * nW;
+    return tilt_rounds(st) && nW == st.n_workers && P >= 16 * nW;
 }
 
 // Weight of the workers before worker w (nW = slots * Nk workers, round w / Nk).
