@@ -154,9 +154,11 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
     // few pages per wave, 1.5 times the pages on the first two rounds costs
     // less.  Measured, same box, three runs: full attention at 32K x 1
     // (contiguous) 33.5 -> 30.6 us, at 16K x 1 23.0 -> 20.9 us, 2 x 16K 32.9 ->
-    // 30.4 us; paged 1 x 32K and 2 x 16K unchanged; from 10 pages per wave up
-    // (64K x 1) it lost 8 %.
-    if (!s.unbalanced && tilt_rounds(st) && nW == st.n_workers && P < 8 * nW)
+    // 30.4 us; 128K x 16 with every head hitting (2176 pages) 16.8 -> 15.7 us;
+    // paged 1 x 32K and 2 x 16K unchanged; from 10 pages per wave up (64K x 1)
+    // it lost 8 %.
+    if (!s.unbalanced && tilt_rounds(st) && nW > st.n_workers / st.slots * 2 &&
+        P < 8 * st.n_workers)
         nW = st.n_workers / st.slots * 2;
     // the plan is published by the last block when its waves have no pages
     // (a small step), else by block 0 (the first dispatch round, whose waves
