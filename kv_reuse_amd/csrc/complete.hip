@@ -152,11 +152,12 @@ __global__ __launch_bounds__(BLOCK, G > 4 ? 2 : 3) void complete_mfma_kernel(Sha
     // rounds take part.  The third round's waves start with the lowest issue
     // priority and end last (~4 us after the first round's at 32K x 1); with
     // few pages per wave, 1.5 times the pages on the first two rounds costs
-    // less.  Measured, same box, three runs: full attention at 32K x 1
-    // (contiguous) 33.5 -> 30.6 us, at 16K x 1 23.0 -> 20.9 us, 2 x 16K 32.9 ->
-    // 30.4 us; 128K x 16 with every head hitting (2176 pages) 16.8 -> 15.7 us;
-    // paged 1 x 32K and 2 x 16K unchanged; from 10 pages per wave up (64K x 1)
-    // it lost 8 %.
+    // less.  Measured, same box: full attention at batch 1 (contiguous) over
+    // 63 contexts from 32K to 48K tokens, complete 34.7 -> 33.7 us on average
+    // (45 points better by over 0.5 us, 2 worse), 16K x 1 23.0 -> 20.9 us;
+    // 128K x 16 with every head hitting (2176 pages) 16.8 -> 15.7 us; paged
+    // 1 x 32K and 2 x 16K unchanged; with 10 or more pages per wave on three
+    // rounds (64K x 1) it lost 8 %.
     if (!s.unbalanced && tilt_rounds(st) && nW > st.n_workers / st.slots * 2 &&
         P < 8 * st.n_workers)
         nW = st.n_workers / st.slots * 2;
