@@ -553,24 +553,54 @@ __device__ __forceinline__ int round_weight(int k, int S)
 // Three or more dispatch rounds (G <= 4): the rounds' waves end in order.
 __device__ __forceinline__ bool tilt_rounds(const State &st) { return st.slots >= 3; }
 
+// (P < 2^26 keeps P * cum(nW) below 2^53 for the fp64 quotient of share_start.)
 __device__ __forceinline__ bool tilted_plan(const State &st, int nW, int P)
 {
-    return tilt_rounds(st) && nW == st.n_workers && P >= 16 * nW;
+    return tilt_rounds(st) && nW == st.n_workers && P >= 16 * nW && P < (1 << 26);
 }
 
-// Weight of the workers before worker w (nW = slots * Nk workers, round w / Nk).
+// XCD weights.  The dispatcher hands a launch's blocks to the 8 XCDs in turn
+// (block b on XCD b % 8), and a wave timeline at 128K x 16 (mean block end
+// per XCD, three runs, each round alike) had the even XCDs' blocks end 30-50
+// us after the odd ones' (mixed step ~1030 against ~993 us, full attention
+// ~1264 against ~1216 us).  So the tilted plan also weights a wave's share by
+// its XCD's parity, 28 : 27 for the odd ones.  Measured, two boxes, four runs
+// each: the mixed step 1071.7 -> 1064.1 and 1075.0 -> 1065.6 us, full
+// attention 1317.0 -> 1305.0 and 1318.6 -> 1308.8 us; 21 : 20 and 16 : 15
+// landed alike, 13 : 12 lost the gain.  Without whole XCD cycles per round
+// (CUs not a multiple of 8) the XCD weights are left out.
+constexpr int NXCD = 8;
+constexpr int XCD_W_EVEN = 27, XCD_W_ODD = 28;
+
+__device__ __forceinline__ int xcd_weight(int x) { return (x & 1) ? XCD_W_ODD : XCD_W_EVEN; }
+
+// Sum of the weights of XCDs 0 .. n-1.
+__device__ __forceinline__ int xcd_prefix(int n)
+{
+    return (n >> 1) * (XCD_W_EVEN + XCD_W_ODD) + ((n & 1) ? XCD_W_EVEN : 0);
+}
+
+// Weight of the workers before worker w (nW = slots * Nk workers; worker w is
+// wave w % 4 of block w / 4, in round w / Nk, on XCD (w / 4) % 8): round
+// weight x XCD weight per worker, summed in closed form.
 __device__ __forceinline__ long cum_weight(int w, int Nk, int S)
 {
     const int k = w / Nk, j = w % Nk;
     int c = 0;
     for (int i = 0; i < k; ++i)
         c += round_weight(i, S);
-    return (long)c * Nk + (long)j * round_weight(k, S);
+    if (Nk % (WAVES * NXCD) != 0)
+        return (long)c * Nk + (long)j * round_weight(k, S);
+    const long round_x = (long)(Nk / (WAVES * NXCD)) * xcd_prefix(NXCD) * WAVES;
+    const int jb = j / WAVES, jw = j % WAVES;
+    const long part_x = (long)(jb / NXCD) * xcd_prefix(NXCD) * WAVES +
+                        (long)xcd_prefix(jb % NXCD) * WAVES + (long)jw * xcd_weight(jb % NXCD);
+    return (long)c * round_x + (long)round_weight(k, S) * part_x;
 }
 
 // First flattened page of worker w's share (w = nW gives P).  The weighted
-// form is floor(P * cum(w) / cum(nW)), with P * cum(w) < 2^53 (P < 2^31,
-// cum(nW) = waves x per-mille weights < 2^22).
+// form is floor(P * cum(w) / cum(nW)), with P * cum(w) < 2^53 (P < 2^26,
+// cum(nW) = waves x round x XCD weights < 2^27).
 __device__ __forceinline__ long share_start(const State &st, int w, int nW, int P)
 {
     if (!tilted_plan(st, nW, P))
@@ -580,7 +610,7 @@ __device__ __forceinline__ long share_start(const State &st, int w, int nW, int 
 }
 
 // Owner of flattened page x under share_start: the last worker whose share
-// starts at or before x (every share holds at least 14 pages when tilted).
+// starts at or before x (every share holds at least 13 pages when tilted).
 // Tilting shares of under 16 pages measured slower (same box, three runs:
 // complete at 32K x 1, full attention, 32.9 -> 37.1 us with 4 pages as the
 // floor), although the last round's waves end ~4 us after the first's there.
