@@ -161,6 +161,7 @@ struct RingTile {
 // The head's inputs other than the ring, loaded by the deciding wave.
 struct HeadIn {
     float qa, qb;      // pre-RoPE query, elements lane and lane + 64
+    float q2;          // |q|^2 (head_norm2), read by decide
     double inv;        // inverse frequency of the lane's rotation pair
     int ov, band, pos_l;
     unsigned long long old[HEAD_NSTAT];
@@ -187,6 +188,12 @@ __device__ __forceinline__ void load_head(const Shape &s, const State &st, const
         for (int k = 0; k < HEAD_NSTAT; ++k)
             in.old[k] = hstat[k];
     }
+}
+
+// |q|^2 of the pre-RoPE query, wave-uniform.
+__device__ __forceinline__ void head_norm2(HeadIn &in)
+{
+    in.q2 = wave_sum(in.qa * in.qa + in.qb * in.qb);
 }
 
 // This step's query copies: pre-RoPE (for amend) and rotated (for complete);
@@ -221,7 +228,7 @@ __device__ __forceinline__ void decide(const Shape &s, const State &st, int b, i
     int cnt[HEAD_NSTAT] = {0, 0, 0, 0};
     const bool act = m >= 0;
     if (act && s.reuse) {
-        const float q2 = wave_sum(in.qa * in.qa + in.qb * in.qb);
+        const float q2 = in.q2;
         if (kp >= 0) {
             rel = q2 > 0.f ? sqrtf(kd / q2) : (kd == 0.f ? 0.f : INFINITY);
             // relative-L2 test compared squared: D <= tau^2 |q~|^2
@@ -307,6 +314,7 @@ __global__ __launch_bounds__(64) void match_kernel(Shape s, State st, KvView kv,
     int kp = INT_MIN, kj = -1;
     if (m >= 0 && s.reuse)
         ring.scan(q_pre + idx * D, 0, s.W, in.pos_l, m, kd, kp, kj);
+    head_norm2(in);
     decide(s, st, b, h, m, bad, in, kd, kp, kj, hidden);
 }
 
@@ -393,6 +401,7 @@ __global__ __launch_bounds__(64) void match_tiled_kernel(Shape s, State st, KvVi
     argmin_step<32>(kd, kp, kj);
     if (m < 0)
         kp = INT_MIN;
+    head_norm2(in);
     decide(s, st, b, h, m, bad, in, kd, kp, kj, hidden);
 }
 
@@ -418,13 +427,37 @@ match_wide_kernel(
     __shared__ int s_p[MATCH_WAVES], s_j[MATCH_WAVES];
     const int h = blockIdx.x, b = blockIdx.y;
     const long idx = (long)b * s.Hq + h;
-    const int lane = lane_id(), wv = threadIdx.x >> 6, nwv = blockDim.x >> 6;
+    // (wave index read as wave-uniform, so values set by wave 0 alone stay scalar)
+    const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwv = blockDim.x >> 6;
     const int nsub = (s.W + SUB - 1) / SUB;
     const int seq = seq_lens[b];
     bool bad;
     const int m = query_position(kv, seq, bad);
     float kd = INFINITY;
     int kp = INT_MIN, kj = -1;
+    // wave 0 (the deciding wave) loads the head's other inputs and stores the
+    // query copies before its share of the scan, off the block's tail
+    HeadIn in;
+    float q2s = 0.f;
+    int ov_s = -2, band_s = 0;
+    unsigned old_s[2 * HEAD_NSTAT];
+    if (wv == 0) {
+        load_head(s, st, q_pre, ovr, b, h, hidden, in);
+        store_queries(st, idx, m, in, out);
+        head_norm2(in);
+        // across the scan decide needs |q|^2, the override, the band and the
+        // head's counters (wave-uniform: scalar registers) and the first 64
+        // stamps (one register); the ring tiles keep the vector registers
+        q2s = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(in.q2)));
+        ov_s = __builtin_amdgcn_readfirstlane(in.ov);
+        band_s = __builtin_amdgcn_readfirstlane(in.band);
+#pragma unroll
+        for (int k = 0; k < HEAD_NSTAT; ++k) {
+            old_s[2 * k] = __builtin_amdgcn_readfirstlane((unsigned)in.old[k]);
+            old_s[2 * k + 1] = __builtin_amdgcn_readfirstlane((unsigned)(in.old[k] >> 32));
+        }
+    }
     if (m >= 0 && s.reuse) {
         // two sub-tiles per wave in flight: the next one's loads are issued
         // before the current one is scanned
@@ -472,11 +505,12 @@ match_wide_kernel(
     __syncthreads();
     if (wv != 0)
         return;
-    // the head's other inputs: loaded after the scan, whose ring tiles take
-    // the registers (two blocks per CU: at most 128 per lane)
-    HeadIn in;
-    load_head(s, st, q_pre, ovr, b, h, hidden, in);
-    store_queries(st, idx, m, in, out);
+    in.q2 = q2s;
+    in.ov = ov_s;
+    in.band = band_s;
+#pragma unroll
+    for (int k = 0; k < HEAD_NSTAT; ++k)
+        in.old[k] = lane == 0 ? ((unsigned long long)old_s[2 * k + 1] << 32 | old_s[2 * k]) : 0ULL;
     // nearest over the waves (a strict total order: the result does not
     // depend on the order of the comparisons)
     for (int k = 1; k < nwv; ++k) {
