@@ -43,7 +43,12 @@ struct RingTile {
     using Vec = typename std::conditional<BF16, uint4, float4>::type;
     Vec v[NL];
 
-    // slots [base, base + nslot) of head idx
+    // slots [base, base + nslot) of head idx.  ALL: every load is issued, a
+    // slot past nslot re-reading the last valid slot's row (scan ignores it):
+    // for loads kept in flight across later work, since loads under a branch
+    // leave the compiler unable to count a wave's loads in flight, and every
+    // later wait is then for all of them.  Otherwise such slots are zero.
+    template <bool ALL = false>
     __device__ __forceinline__ void load(const Shape &s, const State &st, long idx, int base,
                                          int nslot)
     {
@@ -58,9 +63,9 @@ struct RingTile {
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
             const int sl = PER * u + sub;
-            if (sl < nslot) {
+            if (ALL || sl < nslot) {
                 // read once per step: streaming hint
-                const uint4 t = load_stream(rq + (long)sl * VPR + c);
+                const uint4 t = load_stream(rq + (long)(ALL ? min(sl, nslot - 1) : sl) * VPR + c);
                 v[u] = *reinterpret_cast<const Vec *>(&t);
             } else {
                 v[u] = Vec{};
@@ -71,12 +76,10 @@ struct RingTile {
     // Nearest valid entry of the loaded slots (wave-uniform result): squared
     // L2 distance to the pre-RoPE query qsrc, summed over each slot's lanes;
     // pos_l is the stamp of slot base + lane; valid stamps are 0 .. m.
-    __device__ __forceinline__ void scan(const float *qsrc, int base, int nslot, int pos_l, int m,
-                                         float &kd, int &kp, int &kj) const
+    // The query columns this lane compares (4 for fp32 slots, 8 for bf16).
+    __device__ __forceinline__ static void load_query(const float *qsrc, float (&q)[8])
     {
-        const int lane = lane_id();
-        const int sub = lane / (64 / PER), c = lane % (64 / PER);
-        float q[8];
+        const int c = lane_id() % (64 / PER);
         if constexpr (BF16) {
             const float4 a = reinterpret_cast<const float4 *>(qsrc)[2 * c];
             const float4 b = reinterpret_cast<const float4 *>(qsrc)[2 * c + 1];
@@ -85,7 +88,24 @@ struct RingTile {
         } else {
             const float4 a = reinterpret_cast<const float4 *>(qsrc)[c];
             q[0] = a.x, q[1] = a.y, q[2] = a.z, q[3] = a.w;
+            q[4] = q[5] = q[6] = q[7] = 0.f;
         }
+    }
+
+    __device__ __forceinline__ void scan(const float *qsrc, int base, int nslot, int pos_l, int m,
+                                         float &kd, int &kp, int &kj) const
+    {
+        float q[8];
+        load_query(qsrc, q);
+        scan(q, base, nslot, pos_l, m, kd, kp, kj);
+    }
+
+    // The same with the lane's query columns already in registers (q).
+    __device__ __forceinline__ void scan(const float (&q)[8], int base, int nslot, int pos_l,
+                                         int m, float &kd, int &kp, int &kj) const
+    {
+        const int lane = lane_id();
+        const int sub = lane / (64 / PER);
         kd = INFINITY;
         kp = INT_MIN;
         kj = -1;
@@ -463,38 +483,53 @@ match_wide_kernel(
         // before the current one is scanned
         RingTile<SUB, BF16> ring[2];
         int pos_l[2];
+        // the query is read once, ahead of the ring: a query load issued
+        // after the next sub-tile's would make each scan wait for that
+        // sub-tile too (loads complete in order)
+        float qv[8];
+        RingTile<SUB, BF16>::load_query(q_pre + idx * D, qv);
+        // (fetch issues the same loads whatever j is, so that a scan waits
+        // only for its own sub-tile; the stamps are masked when scanned)
         auto fetch = [&](int k, int j) {
             const int base = j * SUB, nslot = min(SUB, s.W - base);
-            ring[k].load(s, st, idx, base, nslot);
-            pos_l[k] = (lane < nslot && base + lane != hidden)
-                           ? st.ring_pos[(long)b * s.W + base + lane]
-                           : -1;
+            ring[k].template load<true>(s, st, idx, base, nslot);
+            pos_l[k] = st.ring_pos[(long)b * s.W + base + min(lane, nslot - 1)];
         };
         auto scan = [&](int k, int j) {
             const int base = j * SUB, nslot = min(SUB, s.W - base);
+            const int pl = (lane < nslot && base + lane != hidden) ? pos_l[k] : -1;
             float d;
             int p, jj;
-            ring[k].scan(q_pre + idx * D, base, nslot, pos_l[k], m, d, p, jj);
+            ring[k].scan(qv, base, nslot, pl, m, d, p, jj);
             if (nearer(d, p, jj, kd, kp, kj)) {
                 kd = d;
                 kp = p;
                 kj = jj;
             }
         };
+        // this wave's sub-tiles: wv, wv + nwv, ... below nsub; the loop body
+        // prefetches unconditionally, the last one or two are peeled
         int j = wv;
-        if (j < nsub)
+        const int cnt = j < nsub ? (nsub - 1 - j) / nwv + 1 : 0;
+        if (cnt > 0) {
             fetch(0, j);
-        while (j < nsub) {
-            if (j + nwv < nsub)
+            int left = cnt - 1;   // sub-tiles not yet fetched
+            while (left >= 2) {
                 fetch(1, j + nwv);
-            scan(0, j);
-            j += nwv;
-            if (j >= nsub)
-                break;
-            if (j + nwv < nsub)
+                scan(0, j);
+                j += nwv;
                 fetch(0, j + nwv);
-            scan(1, j);
-            j += nwv;
+                scan(1, j);
+                j += nwv;
+                left -= 2;
+            }
+            if (left == 1) {
+                fetch(1, j + nwv);
+                scan(0, j);
+                scan(1, j + nwv);
+            } else {
+                scan(0, j);
+            }
         }
     }
     if (lane == 0) {
