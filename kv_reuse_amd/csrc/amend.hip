@@ -197,9 +197,11 @@ __global__ __launch_bounds__(64 * AMEND_MFMA_WAVES) void amend_mfma_kernel(Shape
     const int p_last = m / PAGE;
     int page = lo / PAGE + wv;
     MPage cur, nxt;
-    if (has_prefix && page <= p_last)
-        load_mpage(cur, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad),
-                   kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page, bad));
+    // (K and V share a page's element offset: one page-table lookup per page)
+    if (has_prefix && page <= p_last) {
+        const long off = kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page, bad) - kb;
+        load_mpage(cur, kb + off, vb + off);
+    }
     if (has_prefix && wv == 0) {
         float4 qf[8];
         load_qa_rows<G>(s, st, b, kvh, qf);
@@ -233,18 +235,25 @@ __global__ __launch_bounds__(64 * AMEND_MFMA_WAVES) void amend_mfma_kernel(Shape
             acc.L[v] = 0.f;
             acc.Ml[v] = NEG_INF;
         }
-        while (page <= p_last) {
-            // the next page's loads go out before this page is computed
-            if (page + NW <= p_last)
-                load_mpage(nxt, kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page + NW, bad),
-                           kv_page<uint16_t>(kv, vb, b, kvh, s.Hkv, page + NW, bad));
+        // the next page's loads go out before this page is computed; the
+        // loop issues them unconditionally and the wave's last page is
+        // peeled, since loads under a branch leave the compiler unable to
+        // count them and the K store would then wait for the next page too
+        while (page + NW <= p_last) {
+            const long off = kv_page<uint16_t>(kv, kb, b, kvh, s.Hkv, page + NW, bad) - kb;
+            load_mpage(nxt, kb + off, vb + off);
             kstore_page(cur, klds[wv]);
             const int tok0 = page * PAGE;
             compute_mpage<G>(klds[wv], cur.v, &qlds[0][0], plds[wv], tok0, m, hsl,
                              tok0 < hmax || tok0 + PAGE - 1 > m, half_mask, acc);
             page += NW;
-            if (page <= p_last)
-                cur = nxt;
+            cur = nxt;
+        }
+        if (page <= p_last) {
+            kstore_page(cur, klds[wv]);
+            const int tok0 = page * PAGE;
+            compute_mpage<G>(klds[wv], cur.v, &qlds[0][0], plds[wv], tok0, m, hsl,
+                             tok0 < hmax || tok0 + PAGE - 1 > m, half_mask, acc);
         }
         store_msummary<G>(acc, &red[wv][0][0]);
     }
